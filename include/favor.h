@@ -1,0 +1,133 @@
+/*
+ * libfavor -- FAVOR+ (Performer) linear attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes plain device pointers, sizes and a HIP stream.
+ *
+ * The operation (Performer notes: sections Kernel Attention View, Normalization
+ * and FAVOR+; lesson "Linear Attention and the Performer": Code; Performer for
+ * vision: How It Works, Steps 1 and 2):
+ *
+ *   phi(x)  = exp(W x - |x|^2 / 2) / sqrt(m)          positive random features
+ *   S       = Phi(K)^T V,   z = Phi(K)^T 1             key/value summary
+ *   y_i     = phi(q_i)^T S / phi(q_i)^T z              non-causal output
+ *   y_i     = phi(q_i)^T S_i / phi(q_i)^T z_i,         causal output, with
+ *             S_i, z_i summing keys j <= i only        (prefix sums, inclusive)
+ *
+ * The library applies no 1/sqrt(d) temperature: the caller folds it into q and
+ * k.  The same W serves queries and keys.  d_v = d.
+ *
+ * Layouts (all row-major, innermost last, no padding):
+ *   q, k, v, x, out : [B, H, n, d]
+ *   W               : [H, m, d]   one feature matrix per head, shared by the batch
+ *   phi             : [B, H, n, m]
+ * bf16 entry points take q, k, v, x, W as bfloat16 bit patterns (uint16) and
+ * write float32 results; the _f32 twins take float32 inputs.
+ *
+ * Ownership: the caller allocates every input, output and workspace and keeps
+ * them alive until the work queued on `stream` has finished.  The library
+ * never frees caller memory.  The self-allocating entries take scratch from
+ * hipMallocAsync/hipFreeAsync on `stream`.  stream may be 0 (null stream).
+ *
+ * Errors: arguments are checked before anything is queued; on error nothing is
+ * launched and no output is written.  Launch failures return FAVOR_ERR_HIP.
+ * Kernels run asynchronously: device faults surface at the caller's next
+ * synchronisation.  NaN/Inf inputs are not checked and propagate.
+ * favor_last_error() returns a thread-local description of the last failure.
+ *
+ * Determinism: for a fixed shape, device and library build, results are
+ * bitwise reproducible (all cross-workgroup reductions run in a fixed order;
+ * no floating-point atomics).
+ */
+#ifndef FAVOR_H_
+#define FAVOR_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FAVOR_OK = 0,
+  FAVOR_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad flag */
+  FAVOR_ERR_UNSUPPORTED = 2,      /* valid but outside what this build implements */
+  FAVOR_ERR_HIP = 3,              /* a HIP call or kernel launch failed */
+  FAVOR_ERR_OUT_OF_MEMORY = 4     /* scratch allocation failed, or workspace too small */
+} favor_status_t;
+
+/* Version as major*10000 + minor*100 + patch. */
+int favor_version(void);
+const char* favor_status_string(favor_status_t s);
+/* Thread-local text for the last failing call on this thread ("" if none). */
+const char* favor_last_error(void);
+
+/*
+ * favor_feature_map -- the positive random-feature map itself (Performer
+ * notes, FAVOR+: phi in R^m whose inner products estimate exp(q.k)):
+ *   phi[b,h,i,:] = exp(W[h] x[b,h,i,:] - |x[b,h,i,:]|^2 / 2) / sqrt(m), fp32.
+ * Exact (no stabilising shift), so very large |x| can overflow or underflow
+ * fp32 exactly as the formula does.
+ *   x   : bf16 [B,H,n,d]         W : bf16 [H,m,d]        phi : fp32 [B,H,n,m]
+ * Supported: 1 <= d <= 256, 1 <= m <= 1024.  Pointers 4-byte aligned.
+ */
+favor_status_t favor_feature_map(const void* x, const void* W, float* phi,
+                                 int B, int H, int n, int d, int m, hipStream_t stream);
+favor_status_t favor_feature_map_f32(const float* x, const float* W, float* phi,
+                                     int B, int H, int n, int d, int m, hipStream_t stream);
+
+/*
+ * favor_attention -- FAVOR+ attention, y = Phi(Q) S / (Phi(Q) z) (Performer
+ * notes, Normalization).  causal = 0: every query sees every key.  causal = 1:
+ * query i sees keys j <= i (Performer for vision, Step 2); identical to
+ * favor_attention_causal with chunk = 0.
+ *   q, k, v : bf16 [B,H,n,d]     W : bf16 [H,m,d]        out : fp32 [B,H,n,d]
+ * bf16 path: d == 64; m in {64, 128, 192, 256, 320, 384, 448, 512}; pointers
+ * 16-byte aligned; otherwise FAVOR_ERR_UNSUPPORTED.  Scratch is allocated
+ * stream-ordered on `stream` (see favor_attention_ws to supply it).
+ */
+favor_status_t favor_attention(const void* q, const void* k, const void* v, const void* W,
+                               float* out, int B, int H, int n, int d, int m, int causal,
+                               hipStream_t stream);
+
+/*
+ * favor_attention_causal -- causal FAVOR+ by chunked prefix sums (Performer for
+ * vision, How It Works, Step 2): the sequence is cut into chunks of `chunk`
+ * tokens; each chunk combines the running key/value state of all earlier
+ * chunks with the masked pairwise weights inside the chunk.  chunk == 0 picks
+ * the default (64).  Supported chunk: 64.  Same shapes and limits as
+ * favor_attention.
+ */
+favor_status_t favor_attention_causal(const void* q, const void* k, const void* v,
+                                      const void* W, float* out, int B, int H, int n, int d,
+                                      int m, int chunk, hipStream_t stream);
+
+/*
+ * fp32 twins: identical semantics with float32 q, k, v, W.  Arithmetic in fp32
+ * throughout.  Limits: 1 <= d <= 128, 1 <= m <= 512, m*d <= 16384; pointers
+ * 4-byte aligned.  The causal fp32 entry walks tokens one by one per (b,h); it
+ * is meant for checking, not speed.
+ */
+favor_status_t favor_attention_f32(const float* q, const float* k, const float* v,
+                                   const float* W, float* out, int B, int H, int n, int d,
+                                   int m, int causal, hipStream_t stream);
+favor_status_t favor_attention_causal_f32(const float* q, const float* k, const float* v,
+                                          const float* W, float* out, int B, int H, int n,
+                                          int d, int m, int chunk, hipStream_t stream);
+
+/*
+ * Caller-owned scratch for the bf16 attention path.  favor_workspace_bytes
+ * returns the size favor_attention_ws needs for a shape (0 if the shape is not
+ * supported).  The workspace must be zero-filled once before its first use
+ * (hipMemset); every call leaves it ready for the next call.  Two calls that
+ * share one workspace must not overlap in time (same stream is fine).
+ */
+size_t favor_workspace_bytes(int B, int H, int n, int d, int m, int causal);
+favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, const void* W,
+                                  float* out, int B, int H, int n, int d, int m, int causal,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FAVOR_H_ */

@@ -1,0 +1,210 @@
+"""Plain fp64 reference for FAVOR+ attention (Performer).
+
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module.  It shares no code with the HIP path.
+
+Every function works on float64 NumPy arrays, follows one statement of the
+method written out directly, and does no blocking, fusion or reordering beyond
+what that statement says (except where a docstring says the token loop is cut
+into blocks only to bound memory).  Shapes: X/Q/K/V are [..., n, d] with any
+leading batch/head axes; W is [m, d] (one head) or [H, m, d] broadcast over a
+leading head axis that matches X's second-to-last-but-one axis.
+
+Sources (pages on the method):
+  * "Performer" paper notes (eightmm): sections Kernel Attention View,
+    Normalization, FAVOR+, Standard Attention Cost.
+  * "Linear Attention and the Performer" lesson (creativeworksofknowledge):
+    sections The kernelization trick and Code.
+  * "Performer for vision" (chipfoundryservices): How It Works (Step 1, Step 2),
+    Kernel Choices.
+
+Readings taken where the pages are silent (all stated again in the design notes):
+  * phi(x) = exp(W x - |x|^2/2) / sqrt(m) with the same W for queries and keys
+    (the FAVOR+ identity E[phi(q).phi(k)] = exp(q.k) uses one omega on both
+    sides).  No stabiliser: this oracle computes the unshifted definition.
+  * The library applies no 1/sqrt(d) temperature; inputs carry it.
+  * Causal attention is inclusive: token i aggregates keys j <= i.
+  * d_v = d; the denominator has no epsilon.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "feature_map", "kv_state", "attention", "attention_causal", "attention_quadratic",
+    "attention_quadratic_rows", "softmax_attention", "max_rel_err",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _heads_W(W: np.ndarray, X: np.ndarray) -> np.ndarray:
+    """Broadcast W ([m,d] or [H,m,d]) against X ([..., H, n, d] or [n, d])."""
+    W = _f64(W)
+    if W.ndim == 2:
+        return W
+    if W.ndim == 3:
+        if X.ndim < 3 or X.shape[-3] != W.shape[0]:
+            raise ValueError("W has a head axis that does not match X")
+        return W
+    raise ValueError("W must be [m,d] or [H,m,d]")
+
+
+def feature_map(X, W) -> np.ndarray:
+    """Positive random features phi(x) = exp(W x - |x|^2 / 2) / sqrt(m).
+
+    Performer notes, section FAVOR+ (positive features whose inner product
+    estimates exp(q.k)); Performer for vision, Kernel Choices (exp of Gaussian
+    projections keeps features positive).  Returns [..., n, m].
+    """
+    X = _f64(X)
+    W = _heads_W(W, X)
+    m = W.shape[-2]
+    if W.ndim == 2:
+        proj = X @ W.T                                   # [..., n, m]
+    else:
+        proj = X @ np.swapaxes(W, -1, -2)               # [..., H, n, d] @ [H, d, m]
+    half_sq = 0.5 * np.sum(X * X, axis=-1, keepdims=True)
+    return np.exp(proj - half_sq) / math.sqrt(m)
+
+
+def kv_state(K, V, W):
+    """S = Phi(K)^T V ([..., m, d]) and z = Phi(K)^T 1 ([..., m]).
+
+    Performer notes, Kernel Attention View (the key/value summary S computed
+    once) and Normalization (the summed key features in the denominator).
+    """
+    phiK = feature_map(K, W)
+    V = _f64(V)
+    S = np.swapaxes(phiK, -1, -2) @ V
+    z = np.sum(phiK, axis=-2)
+    return S, z
+
+
+def attention(Q, K, V, W) -> np.ndarray:
+    """Non-causal FAVOR+ attention y_i = phi(q_i)^T S / phi(q_i)^T z.
+
+    Performer notes, Normalization (associative form of the normalised
+    output); lesson "Linear Attention and the Performer", Code (numerator
+    phi(Q)(phi(K)^T V), denominator phi(Q)(phi(K)^T 1), output their ratio).
+    """
+    S, z = kv_state(K, V, W)
+    phiQ = feature_map(Q, W)
+    num = phiQ @ S
+    den = phiQ @ z[..., :, None]
+    return num / den
+
+
+def attention_causal(Q, K, V, W, block: int = 256) -> np.ndarray:
+    """Causal FAVOR+ attention by running prefix sums over tokens.
+
+    Performer for vision, How It Works, Step 2 (prefix sums so each token sees
+    only earlier ones) with the inclusive reading j <= i:
+        S_i = S_{i-1} + phi(k_i) v_i^T,   z_i = z_{i-1} + phi(k_i),
+        y_i = phi(q_i)^T S_i / phi(q_i)^T z_i.
+    The token loop is cut into blocks of `block` tokens only to bound memory:
+    inside a block the running sums are np.cumsum of the per-token terms, and
+    the last running value carries into the next block.
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    phiQ = feature_map(Q, W)
+    phiK = feature_map(K, W)
+    n = Q.shape[-2]
+    lead = Q.shape[:-2]
+    m = phiQ.shape[-1]
+    d = V.shape[-1]
+    S = np.zeros(lead + (m, d))
+    z = np.zeros(lead + (m,))
+    Y = np.empty(lead + (n, d))
+    for s in range(0, n, block):
+        e = min(n, s + block)
+        outer = phiK[..., s:e, :, None] * V[..., s:e, None, :]       # [..., b, m, d]
+        Srun = S[..., None, :, :] + np.cumsum(outer, axis=-3)         # S_i for i in block
+        zrun = z[..., None, :] + np.cumsum(phiK[..., s:e, :], axis=-2)
+        pq = phiQ[..., s:e, :]
+        num = np.einsum("...bm,...bmd->...bd", pq, Srun)
+        den = np.einsum("...bm,...bm->...b", pq, zrun)
+        Y[..., s:e, :] = num / den[..., None]
+        S = Srun[..., -1, :, :]
+        z = zrun[..., -1, :]
+    return Y
+
+
+def attention_quadratic(Q, K, V, W, causal: bool = False) -> np.ndarray:
+    """Explicit quadratic form y = (A V) / (A 1) with A = Phi(Q) Phi(K)^T.
+
+    Performer notes, Normalization (the ratio of sums over keys before
+    reassociation) and Kernel Attention View (the n x n order that FAVOR+
+    avoids).  causal=True keeps A_ij only for j <= i.  Small n only.
+    """
+    phiQ = feature_map(Q, W)
+    phiK = feature_map(K, W)
+    A = phiQ @ np.swapaxes(phiK, -1, -2)
+    if causal:
+        n = A.shape[-1]
+        A = A * np.tril(np.ones((n, n)))
+    V = _f64(V)
+    return (A @ V) / np.sum(A, axis=-1, keepdims=True)
+
+
+def attention_quadratic_rows(Q, K, V, W, rows, causal: bool) -> np.ndarray:
+    """Rows `rows` of the explicit quadratic form for one (batch, head) slice.
+
+    Q, K, V are [n, d] and W is [m, d].  For each requested row i the weights
+    a_j = phi(q_i)^T phi(k_j) (j <= i when causal) give y_i = sum a_j v_j / sum a_j.
+    Returns [len(rows), d].  Cost is O(n m) per row, so it serves as a sampled
+    check at any sequence length.
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    rows = np.asarray(rows, dtype=np.int64)
+    phiq = feature_map(Q[rows], W)                      # [r, m]
+    phiK = feature_map(K, W)                            # [n, m]
+    out = np.empty((len(rows), V.shape[-1]))
+    for t, i in enumerate(rows):
+        hi = i + 1 if causal else K.shape[0]
+        a = phiK[:hi] @ phiq[t]
+        out[t] = (a @ V[:hi]) / np.sum(a)
+    return out
+
+
+def softmax_attention(Q, K, V, causal: bool = False) -> np.ndarray:
+    """Exact attention softmax(Q K^T) V in fp64 (comparator, not a parity target).
+
+    Performer notes, Standard Attention Cost; the 1/sqrt(d) temperature is
+    already folded into Q and K by the inputs.  Row maxima are subtracted
+    before exponentiating.
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    L = Q @ np.swapaxes(K, -1, -2)
+    if causal:
+        n = L.shape[-1]
+        L = np.where(np.tril(np.ones((n, n), dtype=bool)), L, -np.inf)
+    L = L - np.max(L, axis=-1, keepdims=True)
+    P = np.exp(L)
+    return (P @ V) / np.sum(P, axis=-1, keepdims=True)
+
+
+def max_rel_err(y, y_ref) -> float:
+    """Error metric: max over (batch, head) slices of max|y - y_ref| / max|y_ref|.
+
+    Outputs are convex combinations of value rows and cross zero, so an
+    elementwise ratio is ill-posed; each slice is normalised by its own
+    largest reference magnitude.
+    """
+    y = _f64(y)
+    y_ref = _f64(y_ref)
+    if y.shape != y_ref.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {y_ref.shape}")
+    if y.ndim < 2:
+        y = y[None, :]
+        y_ref = y_ref[None, :]
+    lead = y.shape[:-2]
+    a = np.abs(y - y_ref).reshape(lead + (-1,)).max(axis=-1)
+    b = np.abs(y_ref).reshape(lead + (-1,)).max(axis=-1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r = a / b
+    return float(np.max(r)) if r.size else 0.0
