@@ -1,0 +1,135 @@
+"""FAVOR+ (Performer) linear attention for AMD MI355X, on libfavor's HIP kernels.
+
+PyTorch supplies device memory and the current stream; every step of the
+computation runs in libfavor.so.  Tensors must live on a ROCm GPU: there is no
+CPU path, and calls on CPU tensors raise.
+
+    y = attention(q, k, v, W)                  # non-causal, bf16 or fp32 inputs
+    y = attention(q, k, v, W, causal=True)     # causal (prefix-sum form)
+    phi = feature_map(x, W)                    # exp(W x - |x|^2/2) / sqrt(m)
+
+Layouts: q, k, v, x [B, H, n, d]; W [H, m, d]; outputs float32.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import FavorError, check  # noqa: F401
+
+__all__ = ["feature_map", "attention", "attention_causal", "Workspace", "FavorError",
+           "workspace_bytes", "version"]
+
+
+def version() -> int:
+    return _lib.favor_version()
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libfavor has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shapes(q: torch.Tensor, W: torch.Tensor):
+    if q.dim() != 4 or W.dim() != 3:
+        raise ValueError("expected q/k/v of shape [B, H, n, d] and W of shape [H, m, d]")
+    B, H, n, d = q.shape
+    H2, m, d2 = W.shape
+    if H2 != H or d2 != d:
+        raise ValueError(f"W shape {tuple(W.shape)} does not match q shape {tuple(q.shape)}")
+    return B, H, n, d, m
+
+
+def feature_map(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """phi = exp(W x - |x|^2/2)/sqrt(m) as float32 [B, H, n, m] (no stabilising shift)."""
+    B, H, n, d, m = _shapes(x, W)
+    dt = x.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be bfloat16 or float32")
+    _need(x, "x", dt, (B, H, n, d))
+    _need(W, "W", dt, (H, m, d))
+    if out is None:
+        out = torch.empty((B, H, n, m), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (B, H, n, m))
+    fn = _lib.favor_feature_map if dt == torch.bfloat16 else _lib.favor_feature_map_f32
+    check(fn(x.data_ptr(), W.data_ptr(), out.data_ptr(), B, H, n, d, m, _stream_handle(stream)))
+    return out
+
+
+def workspace_bytes(B: int, H: int, n: int, d: int, m: int, causal: bool = False) -> int:
+    return _lib.favor_workspace_bytes(B, H, n, d, m, int(bool(causal)))
+
+
+class Workspace:
+    """Caller-owned scratch for the bf16 attention path (zero-filled once)."""
+
+    def __init__(self, B: int, H: int, n: int, d: int, m: int, causal: bool = False,
+                 device="cuda"):
+        nbytes = workspace_bytes(B, H, n, d, m, causal)
+        if nbytes == 0:
+            raise FavorError(_lib.FAVOR_ERR_UNSUPPORTED, "shape not supported by the bf16 path")
+        self.nbytes = nbytes
+        self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor,
+              causal: bool = False, out: torch.Tensor | None = None,
+              workspace: Workspace | None = None, stream=None) -> torch.Tensor:
+    """FAVOR+ attention y = phi(Q) S / (phi(Q) z), float32 [B, H, n, d]."""
+    B, H, n, d, m = _shapes(q, W)
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, dt, (B, H, n, d))
+    _need(W, "W", dt, (H, m, d))
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, H, n, d))
+    s = _stream_handle(stream)
+    c = int(bool(causal))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), out.data_ptr())
+    if dt == torch.float32:
+        check(_lib.favor_attention_f32(*ptrs, B, H, n, d, m, c, s))
+    elif workspace is not None:
+        check(_lib.favor_attention_ws(*ptrs, B, H, n, d, m, c, workspace.buf.data_ptr(),
+                                      workspace.nbytes, s))
+    else:
+        check(_lib.favor_attention(*ptrs, B, H, n, d, m, c, s))
+    return out
+
+
+def attention_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor,
+                     chunk: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal FAVOR+ by chunked prefix sums (chunk 0 = default)."""
+    B, H, n, d, m = _shapes(q, W)
+    dt = q.dtype
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, dt, (B, H, n, d))
+    _need(W, "W", dt, (H, m, d))
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, H, n, d))
+    s = _stream_handle(stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), out.data_ptr())
+    if dt == torch.float32:
+        check(_lib.favor_attention_causal_f32(*ptrs, B, H, n, d, m, chunk, s))
+    elif dt == torch.bfloat16:
+        check(_lib.favor_attention_causal(*ptrs, B, H, n, d, m, chunk, s))
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    return out

@@ -1,0 +1,113 @@
+"""ctypes binding for libfavor (include/favor.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libfavor.so.  The library must have been built in-tree (see
+build.py); importing this module never falls back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfavor.so")
+
+FAVOR_OK = 0
+FAVOR_ERR_INVALID_ARGUMENT = 1
+FAVOR_ERR_UNSUPPORTED = 2
+FAVOR_ERR_HIP = 3
+FAVOR_ERR_OUT_OF_MEMORY = 4
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); the same list as include/favor.h
+SIGNATURES = {
+    "favor_version": (_i, []),
+    "favor_status_string": (ctypes.c_char_p, [_i]),
+    "favor_last_error": (ctypes.c_char_p, []),
+    "favor_feature_map": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "favor_feature_map_f32": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "favor_attention": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "favor_attention_causal": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "favor_attention_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "favor_attention_causal_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "favor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "favor_attention_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class FavorError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_string(status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfavor.so (built in-tree).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return lib().favor_status_string(st).decode()
+
+
+def last_error() -> str:
+    return lib().favor_last_error().decode()
+
+
+def check(st: int) -> None:
+    if st != FAVOR_OK:
+        raise FavorError(st, last_error())
+
+
+# Raw pointer-level calls with the C names (pointers and streams as ints).
+def favor_version() -> int:
+    return lib().favor_version()
+
+
+def favor_feature_map(x, W, phi, B, H, n, d, m, stream) -> int:
+    return lib().favor_feature_map(x, W, phi, B, H, n, d, m, stream)
+
+
+def favor_feature_map_f32(x, W, phi, B, H, n, d, m, stream) -> int:
+    return lib().favor_feature_map_f32(x, W, phi, B, H, n, d, m, stream)
+
+
+def favor_attention(q, k, v, W, out, B, H, n, d, m, causal, stream) -> int:
+    return lib().favor_attention(q, k, v, W, out, B, H, n, d, m, causal, stream)
+
+
+def favor_attention_causal(q, k, v, W, out, B, H, n, d, m, chunk, stream) -> int:
+    return lib().favor_attention_causal(q, k, v, W, out, B, H, n, d, m, chunk, stream)
+
+
+def favor_attention_f32(q, k, v, W, out, B, H, n, d, m, causal, stream) -> int:
+    return lib().favor_attention_f32(q, k, v, W, out, B, H, n, d, m, causal, stream)
+
+
+def favor_attention_causal_f32(q, k, v, W, out, B, H, n, d, m, chunk, stream) -> int:
+    return lib().favor_attention_causal_f32(q, k, v, W, out, B, H, n, d, m, chunk, stream)
+
+
+def favor_workspace_bytes(B, H, n, d, m, causal) -> int:
+    return lib().favor_workspace_bytes(B, H, n, d, m, causal)
+
+
+def favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream) -> int:
+    return lib().favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream)

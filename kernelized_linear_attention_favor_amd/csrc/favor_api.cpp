@@ -1,0 +1,234 @@
+// libfavor host layer: argument checks, dispatch, scratch, status codes.
+// Every check runs before anything is queued on the stream, so a failing call
+// launches nothing and writes nothing.
+#include "../../include/favor.h"
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "favor_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+favor_status_t fail(favor_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+favor_status_t ok() {
+  g_last_error[0] = '\0';
+  return FAVOR_OK;
+}
+
+favor_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(FAVOR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+favor_status_t check_sizes(int B, int H, int n, int d, int m) {
+  if (B < 1 || H < 1 || n < 1 || d < 1 || m < 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (B=%d H=%d n=%d d=%d m=%d)", B, H,
+                n, d, m);
+  const long long elems = static_cast<long long>(B) * H * n * (d > m ? d : m);
+  if (elems > (1LL << 40))
+    return fail(FAVOR_ERR_UNSUPPORTED, "problem too large (B*H*n*max(d,m) = %lld)", elems);
+  return FAVOR_OK;
+}
+
+favor_status_t check_ptrs(const void* a, const void* b, const void* c, const void* d,
+                          const void* e, size_t align) {
+  const void* ps[5] = {a, b, c, d, e};
+  const char* names[5] = {"q", "k", "v", "W", "out"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ps[i]) return fail(FAVOR_ERR_INVALID_ARGUMENT, "%s is null", names[i]);
+    if (!aligned(ps[i], align))
+      return fail(FAVOR_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], align);
+  }
+  return FAVOR_OK;
+}
+
+favor_status_t check_f32_limits(int d, int m) {
+  if (d > 128 || m > 512 || static_cast<long long>(m) * d > 16384)
+    return fail(FAVOR_ERR_UNSUPPORTED, "fp32 path needs d <= 128, m <= 512, m*d <= 16384 (d=%d m=%d)",
+                d, m);
+  return FAVOR_OK;
+}
+
+favor_status_t check_bf16(const void* q, const void* k, const void* v, const void* W, float* out,
+                          int B, int H, int n, int d, int m) {
+  favor_status_t st = check_sizes(B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  if ((st = check_ptrs(q, k, v, W, out, 16)) != FAVOR_OK) return st;
+  if (!favor::bf16_supported(d, m))
+    return fail(FAVOR_ERR_UNSUPPORTED,
+                "bf16 attention supports d = 64 and m in {64, 128, 192, 256} (d=%d m=%d)", d, m);
+  return FAVOR_OK;
+}
+
+// Stream-ordered scratch: allocated and freed on the caller's stream.
+struct StreamScratch {
+  void* p = nullptr;
+  hipStream_t s;
+  explicit StreamScratch(hipStream_t st) : s(st) {}
+  hipError_t alloc(size_t bytes) { return hipMallocAsync(&p, bytes, s); }
+  ~StreamScratch() {
+    if (p) (void)hipFreeAsync(p, s);
+  }
+};
+
+favor_status_t run_bf16(const void* q, const void* k, const void* v, const void* W, float* out,
+                        int B, int H, int n, int d, int m, int causal, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  favor::Bf16Plan plan = favor::bf16_plan(B, H, n, d, m, causal);
+  StreamScratch own(stream);
+  if (!ws) {
+    hipError_t e = own.alloc(plan.off_end);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(FAVOR_ERR_OUT_OF_MEMORY, "scratch allocation of %zu bytes failed: %s",
+                  plan.off_end, hipGetErrorString(e));
+    }
+    e = hipMemsetAsync(own.p, 0, plan.off_end, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(scratch)");
+    ws = own.p;
+  } else if (ws_bytes < plan.off_end) {
+    return fail(FAVOR_ERR_OUT_OF_MEMORY, "workspace has %zu bytes, needs %zu", ws_bytes,
+                plan.off_end);
+  } else if (!aligned(ws, 256)) {
+    return fail(FAVOR_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  }
+  hipError_t e = favor::launch_attention_bf16(
+      plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(W), out, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "bf16 attention launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int favor_version(void) { return 10000; }
+
+const char* favor_status_string(favor_status_t s) {
+  switch (s) {
+    case FAVOR_OK: return "FAVOR_OK";
+    case FAVOR_ERR_INVALID_ARGUMENT: return "FAVOR_ERR_INVALID_ARGUMENT";
+    case FAVOR_ERR_UNSUPPORTED: return "FAVOR_ERR_UNSUPPORTED";
+    case FAVOR_ERR_HIP: return "FAVOR_ERR_HIP";
+    case FAVOR_ERR_OUT_OF_MEMORY: return "FAVOR_ERR_OUT_OF_MEMORY";
+  }
+  return "FAVOR_ERR_UNKNOWN";
+}
+
+const char* favor_last_error(void) { return g_last_error; }
+
+favor_status_t favor_feature_map(const void* x, const void* W, float* phi, int B, int H, int n,
+                                 int d, int m, hipStream_t stream) {
+  favor_status_t st = check_sizes(B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  if (!x || !W || !phi) return fail(FAVOR_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(x, 4) || !aligned(W, 4) || !aligned(phi, 4))
+    return fail(FAVOR_ERR_UNSUPPORTED, "pointers must be 4-byte aligned");
+  if (d > 256 || m > 1024) return fail(FAVOR_ERR_UNSUPPORTED, "feature map needs d <= 256, m <= 1024");
+  hipError_t e = favor::launch_feature_map_bf16(static_cast<const uint16_t*>(x),
+                                                static_cast<const uint16_t*>(W), phi, B, H, n, d,
+                                                m, stream);
+  if (e != hipSuccess) return hip_fail(e, "feature map launch");
+  return ok();
+}
+
+favor_status_t favor_feature_map_f32(const float* x, const float* W, float* phi, int B, int H,
+                                     int n, int d, int m, hipStream_t stream) {
+  favor_status_t st = check_sizes(B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  if (!x || !W || !phi) return fail(FAVOR_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(x, 4) || !aligned(W, 4) || !aligned(phi, 4))
+    return fail(FAVOR_ERR_UNSUPPORTED, "pointers must be 4-byte aligned");
+  if (d > 256 || m > 1024) return fail(FAVOR_ERR_UNSUPPORTED, "feature map needs d <= 256, m <= 1024");
+  hipError_t e = favor::launch_feature_map_f32(x, W, phi, B, H, n, d, m, stream);
+  if (e != hipSuccess) return hip_fail(e, "feature map launch");
+  return ok();
+}
+
+favor_status_t favor_attention(const void* q, const void* k, const void* v, const void* W,
+                               float* out, int B, int H, int n, int d, int m, int causal,
+                               hipStream_t stream) {
+  if (causal != 0 && causal != 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  favor_status_t st = check_bf16(q, k, v, W, out, B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  return run_bf16(q, k, v, W, out, B, H, n, d, m, causal, nullptr, 0, stream);
+}
+
+favor_status_t favor_attention_causal(const void* q, const void* k, const void* v, const void* W,
+                                      float* out, int B, int H, int n, int d, int m, int chunk,
+                                      hipStream_t stream) {
+  if (chunk != 0 && chunk != 64)
+    return fail(chunk < 0 ? FAVOR_ERR_INVALID_ARGUMENT : FAVOR_ERR_UNSUPPORTED,
+                "chunk must be 0 (default) or 64 (got %d)", chunk);
+  favor_status_t st = check_bf16(q, k, v, W, out, B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  return run_bf16(q, k, v, W, out, B, H, n, d, m, 1, nullptr, 0, stream);
+}
+
+size_t favor_workspace_bytes(int B, int H, int n, int d, int m, int causal) {
+  if (B < 1 || H < 1 || n < 1 || !favor::bf16_supported(d, m) || (causal != 0 && causal != 1))
+    return 0;
+  return favor::bf16_plan(B, H, n, d, m, causal).off_end;
+}
+
+favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, const void* W,
+                                  float* out, int B, int H, int n, int d, int m, int causal,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (causal != 0 && causal != 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  favor_status_t st = check_bf16(q, k, v, W, out, B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  if (!ws) return fail(FAVOR_ERR_INVALID_ARGUMENT, "ws is null");
+  return run_bf16(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream);
+}
+
+favor_status_t favor_attention_f32(const float* q, const float* k, const float* v, const float* W,
+                                   float* out, int B, int H, int n, int d, int m, int causal,
+                                   hipStream_t stream) {
+  if (causal != 0 && causal != 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  favor_status_t st = check_sizes(B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  if ((st = check_ptrs(q, k, v, W, out, 4)) != FAVOR_OK) return st;
+  if ((st = check_f32_limits(d, m)) != FAVOR_OK) return st;
+  hipError_t e;
+  if (causal) {
+    e = favor::launch_attention_causal_f32(q, k, v, W, out, B, H, n, d, m, stream);
+    if (e != hipSuccess) return hip_fail(e, "fp32 causal launch");
+    return ok();
+  }
+  StreamScratch own(stream);
+  const size_t bytes = favor::f32_workspace_bytes(B, H, n, d, m);
+  e = own.alloc(bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FAVOR_ERR_OUT_OF_MEMORY, "scratch allocation of %zu bytes failed", bytes);
+  }
+  e = favor::launch_attention_f32(q, k, v, W, out, B, H, n, d, m, own.p, stream);
+  if (e != hipSuccess) return hip_fail(e, "fp32 attention launch");
+  return ok();
+}
+
+favor_status_t favor_attention_causal_f32(const float* q, const float* k, const float* v,
+                                          const float* W, float* out, int B, int H, int n, int d,
+                                          int m, int chunk, hipStream_t stream) {
+  if (chunk < 0) return fail(FAVOR_ERR_INVALID_ARGUMENT, "chunk must be >= 0 (got %d)", chunk);
+  return favor_attention_f32(q, k, v, W, out, B, H, n, d, m, 1, stream);
+}
+
+}  // extern "C"

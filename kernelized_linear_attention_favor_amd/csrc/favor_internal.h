@@ -1,0 +1,46 @@
+// Internal declarations shared by the libfavor host layer and its HIP kernels.
+// Nothing here is part of the public ABI (include/favor.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace favor {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- fp32 path
+// Launchers for the fp32 (SIMT) kernels.  All return hipGetLastError().
+hipError_t launch_feature_map_f32(const float* x, const float* W, float* phi, int B, int H, int n,
+                                  int d, int m, hipStream_t s);
+hipError_t launch_feature_map_bf16(const uint16_t* x, const uint16_t* W, float* phi, int B, int H,
+                                   int n, int d, int m, hipStream_t s);
+
+// Non-causal fp32 attention.  Workspace layout is private to the launcher;
+// f32_workspace_bytes gives its size.
+size_t f32_workspace_bytes(int B, int H, int n, int d, int m);
+hipError_t launch_attention_f32(const float* q, const float* k, const float* v, const float* W,
+                                float* out, int B, int H, int n, int d, int m, void* ws,
+                                hipStream_t s);
+hipError_t launch_attention_causal_f32(const float* q, const float* k, const float* v,
+                                       const float* W, float* out, int B, int H, int n, int d,
+                                       int m, hipStream_t s);
+
+// ---------------------------------------------------------------- bf16 path
+struct Bf16Plan {
+  int B, H, n, d, m;
+  int causal;
+  int splits;     // key-range splits per (b,h) for the state pass
+  int span;       // tokens per split (multiple of 32)
+  // workspace carve-up (byte offsets)
+  size_t off_part_S, off_part_zc, off_yhat, off_beta, off_sigma, off_carry, off_end;
+};
+bool bf16_supported(int d, int m);
+Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal);
+hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const uint16_t* W, float* out, void* ws,
+                                 hipStream_t s);
+
+}  // namespace favor

@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "favor.h")
+
+
+def _lib():
+    from kernelized_linear_attention_favor_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfavor.so not built")
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(favor_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("favor_feature_map", "favor_attention", "favor_attention_causal",
+              "favor_attention_ws", "favor_workspace_bytes", "favor_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(declared_functions()) == set(L.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    L = _lib()
+    assert L.favor_version() == 10000
+    assert L.status_string(0) == "FAVOR_OK"
+    assert L.status_string(2) == "FAVOR_ERR_UNSUPPORTED"
+    assert L.status_string(99) == "FAVOR_ERR_UNKNOWN"
+
+
+def test_workspace_bytes_host_only():
+    L = _lib()
+    assert L.favor_workspace_bytes(4, 8, 16384, 64, 256, 0) > 0
+    assert L.favor_workspace_bytes(4, 8, 16384, 64, 256, 1) > 0
+    assert L.favor_workspace_bytes(4, 8, 16384, 32, 256, 0) == 0   # d unsupported
+    assert L.favor_workspace_bytes(4, 8, 16384, 64, 100, 0) == 0   # m unsupported
+    assert L.favor_workspace_bytes(0, 8, 16384, 64, 256, 0) == 0
+    assert L.favor_workspace_bytes(1, 1, 16, 64, 64, 2) == 0
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 64, 0), 1),        # null q
+    ((FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 16, 64, 64, 0), 1),        # null out
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 16, 64, 64, 0), 1),     # B = 0
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, -3, 64, 64, 0), 1),     # n < 0
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 64, 2), 1),     # causal flag
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 48, 64, 0), 2),     # d unsupported
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 96, 0), 2),     # m unsupported
+    ((FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 64, 0), 2),  # misaligned
+])
+def test_attention_rejects_bad_arguments(args, status):
+    L = _lib()
+    st = L.favor_attention(*args, None)
+    assert st == status
+    assert L.last_error() != ""
+
+
+def test_causal_chunk_and_f32_limits():
+    L = _lib()
+    base = (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 64)
+    assert L.favor_attention_causal(*base, 32, None) == 2
+    assert L.favor_attention_causal(*base, -1, None) == 1
+    assert L.favor_attention_f32(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 256, 64, 0, None) == 2
+    assert L.favor_attention_f32(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 1024, 0, None) == 2
+    assert L.favor_feature_map(0, FAKE, FAKE, 1, 1, 16, 64, 64, None) == 1
+    assert L.favor_feature_map(FAKE, FAKE, FAKE, 1, 1, 16, 512, 64, None) == 2
+    assert L.favor_attention_ws(*base, 0, 0, 0, None) == 1
+    assert L.favor_attention_ws(*base, 0, FAKE, 16, None) == 4   # workspace too small
+
+
+def test_no_cpu_path():
+    import torch
+    import kernelized_linear_attention_favor_amd as favor
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    W = torch.zeros(1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        favor.attention(q, q, q, W)

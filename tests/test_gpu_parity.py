@@ -1,0 +1,170 @@
+"""GPU parity: libfavor's HIP path against the fp64 oracle on identical inputs.
+
+Tolerances (max over (b, h) of max|y - y_ref| / max|y_ref|):
+  bf16 inputs, fp32 accumulation : 2e-3
+  fp32 inputs                    : 1e-5
+  feature map (elementwise rel.) : 1e-5
+"""
+import numpy as np
+import pytest
+
+import favor_inputs as fi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import kernelized_linear_attention_favor_amd as favor  # noqa: E402
+
+TOL_BF16 = 2e-3
+TOL_F32 = 1e-5
+DEV = torch.device("cuda:0")
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=DEV, dtype=dtype)
+
+
+def run(x, dtype, causal=False, **kw):
+    t = {k: dev(v, dtype) for k, v in x.items()}
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"], causal=causal, **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def slice_err(y, x, causal=False):
+    """Per-(b,h) oracle evaluation, to bound host memory at large shapes."""
+    B, H = y.shape[:2]
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            f = oracle.attention_causal if causal else oracle.attention
+            ref = f(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["W"][h])
+            worst = max(worst, oracle.max_rel_err(y[b, h], ref))
+    return worst
+
+
+# ----------------------------------------------------------------- feature map
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,n,d,m", [(1, 1, 1, 64, 64), (2, 3, 37, 64, 256), (1, 2, 100, 32, 48),
+                                       (1, 1, 65, 16, 130)])
+def test_feature_map(dtype, B, H, n, d, m):
+    cfg = fi.Config("fm", B, H, n, d, m, dtype, False, 64, "iid", 7)
+    x = fi.make_inputs(cfg)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    phi = favor.feature_map(dev(x["q"], td), dev(x["W"], td))
+    torch.cuda.synchronize()
+    ref = oracle.feature_map(x["q"], x["W"])
+    rel = np.max(np.abs(phi.cpu().numpy() - ref) / ref)
+    assert rel < 1e-5
+
+
+# ---------------------------------------------------------------- fp32 path
+def test_f32_C1_noncausal_and_causal():
+    x = fi.make_inputs(fi.config("C1"))
+    y = run(x, torch.float32)
+    assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_F32
+    yc = run(x, torch.float32, causal=True)
+    assert oracle.max_rel_err(yc, oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])) < TOL_F32
+
+
+@pytest.mark.parametrize("B,H,n,d,m", [(1, 1, 1, 32, 64), (2, 2, 37, 16, 48), (1, 3, 300, 64, 256),
+                                       (1, 1, 129, 128, 128)])
+def test_f32_shapes(B, H, n, d, m):
+    cfg = fi.Config("f32", B, H, n, d, m, "f32", False, 64, "iid", 11)
+    x = fi.make_inputs(cfg)
+    y = run(x, torch.float32)
+    assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_F32
+    yc = run(x, torch.float32, causal=True)
+    assert oracle.max_rel_err(yc, oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])) < TOL_F32
+
+
+# ---------------------------------------------------------------- bf16 path
+def test_bf16_C2_against_oracle_and_softmax():
+    x = fi.make_inputs(fi.config("C2"))
+    y = run(x, torch.bfloat16)
+    ref = oracle.attention(x["q"], x["k"], x["v"], x["W"])
+    err = oracle.max_rel_err(y, ref)
+    sm = oracle.softmax_attention(x["q"], x["k"], x["v"])
+    div = np.linalg.norm(y - sm) / np.linalg.norm(sm)
+    print(f"C2 bf16: err vs oracle {err:.3e}; relative Frobenius divergence from softmax {div:.3f}")
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("n", [1, 7, 31, 32, 33, 64, 65, 100, 1000, 4097])
+@pytest.mark.parametrize("m", [64, 128, 192, 256])
+def test_bf16_ragged(n, m):
+    cfg = fi.Config("rag", 1, 2, n, 64, m, "bf16", False, 64, "iid", 100 + n)
+    x = fi.make_inputs(cfg)
+    y = run(x, torch.bfloat16)
+    assert np.all(np.isfinite(y))
+    assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
+
+
+def test_bf16_C3_full():
+    cfg = fi.config("C3")
+    x = fi.make_inputs(cfg)
+    y = run(x, torch.bfloat16)
+    err = slice_err(y, x)
+    print(f"C3 bf16 err {err:.3e}")
+    assert err < TOL_BF16
+
+
+def test_bf16_C5_full():
+    cfg = fi.config("C5")
+    x = fi.make_inputs(cfg)
+    y = run(x, torch.bfloat16)
+    err = slice_err(y, x)
+    print(f"C5 bf16 err {err:.3e}")
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("scale", [2.0, 4.0])
+def test_bf16_stress_large_norms(scale):
+    """Q, K scaled up: exponents far outside fp32 exp range without shifts."""
+    cfg = fi.config("C2", H=4)
+    x = fi.make_inputs(cfg, qk_scale=scale)
+    y = run(x, torch.bfloat16)
+    assert np.all(np.isfinite(y))
+    assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
+
+
+def test_bf16_overflow_fallback():
+    """First keys of the range tiny next to later ones: the first-tile shift
+    would overflow, so the kernel must take its recompute path."""
+    cfg = fi.config("C2", H=2, n=512)
+    x = fi.make_inputs(cfg)
+    k = x["k"].astype(np.float64)
+    k[:, :, :64, :] *= 12.0      # huge norms -> exponents around -700 for the first tile
+    x["k"] = fi.round_bf16(k)
+    y = run(x, torch.bfloat16)
+    assert np.all(np.isfinite(y))
+    assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
+
+
+def test_bf16_convexity_determinism_workspace():
+    cfg = fi.config("C2", H=4, n=2000)
+    x = fi.make_inputs(cfg)
+    t = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    y1 = favor.attention(t["q"], t["k"], t["v"], t["W"])
+    y2 = favor.attention(t["q"], t["k"], t["v"], t["W"])
+    ws = favor.Workspace(1, 4, 2000, 64, 256)
+    y3 = favor.attention(t["q"], t["k"], t["v"], t["W"], workspace=ws)
+    y4 = favor.attention(t["q"], t["k"], t["v"], t["W"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3) and torch.equal(y1, y4)
+    y = y1.cpu().numpy()
+    v = x["v"]
+    assert np.all(y <= v.max(axis=-2, keepdims=True) + 1e-6)
+    assert np.all(y >= v.min(axis=-2, keepdims=True) - 1e-6)
+
+
+def test_bf16_constant_values():
+    cfg = fi.config("C2", H=2, n=300)
+    x = fi.make_inputs(cfg)
+    x["v"] = np.broadcast_to(fi.round_bf16(np.linspace(-3, 3, 64)), x["v"].shape).copy()
+    y = run(x, torch.bfloat16)
+    assert np.max(np.abs(y - x["v"])) < 3 * 2 ** -11
