@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the FAVOR+ attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+non-causal FAVOR+ attention (feature map, key/value state, output) followed by
+causal FAVOR+ attention (chunked prefix sums) on the same batch.  Workload:
+B=4, H=8, n=16384, d=64, m=256, bf16 inputs, fp32 outputs.  Several
+independent input sets rotate between steps so that the 256 MB Infinity Cache
+cannot hold a step's working set.  Inputs are resident in HBM before timing.
+
+Prints one JSON line:
+  value          tokens/s for the step (B*n tokens per step)
+  roofline       dominant kernel: algorithmic bytes per launch / mean launch
+                 time (HIP events on the launch stream), against 8 TB/s HBM
+  cpu_baseline   the fp64 oracle timed on host cores on a sample of the same
+                 workload (whole (b, h) slices)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+CSRC = os.path.join(ROOT, "kernelized_linear_attention_favor_amd", "csrc")
+
+
+def kernel_bytes(name: str, B: int, H: int, n: int, d: int, m: int) -> float:
+    """Algorithmic HBM bytes one launch of `name` must move (inputs read once,
+    outputs written once; bf16 inputs, fp32 outputs)."""
+    BH = B * H
+    tok = BH * n * d
+    W = H * m * d * 2
+    table = {
+        "k_kv_state": 2 * tok * 2 + W,               # K, V
+        "k_output": tok * 2 + tok * 4 + W,           # Q in, y out
+        "k_causal_state": 2 * tok * 2 + W,           # K, V
+        "k_causal_output": 3 * tok * 2 + tok * 4 + W,  # Q, K, V in, y out
+    }
+    return float(table.get(name, 0.0))
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    for line in open(PMC_FILE):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
+        if kv.get("kernel") == kernel and kv.get("sources") == digest and "bytes_per_launch" in kv:
+            return float(kv["bytes_per_launch"])
+    return None
+
+
+# ----------------------------------------------------------- CPU baseline
+_ORACLE_INPUT = None
+
+
+def _oracle_slice(args):
+    b, h, causal = args
+    import oracle  # cpu_baseline leg only
+    q, k, v, W = (_ORACLE_INPUT[key] for key in ("q", "k", "v", "W"))
+    f = oracle.attention_causal if causal else oracle.attention
+    f(q[b, h], k[b, h], v[b, h], W[h])
+    return 1
+
+
+def cpu_baseline(x, cfg, with_causal: bool, budget_s: float = 10.0) -> dict:
+    """Time the fp64 oracle (as it stands) on whole (b, h) slices of the workload."""
+    global _ORACLE_INPUT
+    _ORACLE_INPUT = x
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    slices = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    done = 0
+    with ctx.Pool(cores) as pool:
+        # one round of `cores` slices, repeated until the time budget is used
+        i = 0
+        while True:
+            batch = [slices[(i + j) % len(slices)] for j in range(cores)]
+            i += cores
+            jobs = [(b, h, False) for b, h in batch]
+            if with_causal:
+                jobs += [(b, h, True) for b, h in batch]
+            sum(pool.map(_oracle_slice, jobs, chunksize=1))
+            done += len(batch)
+            if time.perf_counter() - t0 >= budget_s or done >= 4 * len(slices):
+                break
+    wall = time.perf_counter() - t0
+    tokens = done / cfg.H * cfg.n   # a token = one query position through all H heads
+    variants = "non-causal + causal" if with_causal else "non-causal"
+    return {
+        "value": tokens / wall,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{done} whole (b,h) slices of n={cfg.n} (d={cfg.d}, m={cfg.m}) through {variants} "
+                  f"fp64 NumPy oracle in {wall:.1f} s on {cores} worker processes",
+    }
+
+
+# ------------------------------------------------------------------- main
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--noncausal-only", action="store_true", help="time only the non-causal call")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (b, h) or over the sequence without running here)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import favor_inputs as fi
+    import kernelized_linear_attention_favor_amd as favor
+    from kernelized_linear_attention_favor_amd import _lib
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    cfg = fi.config("C3")
+    B, H, n, d, m = cfg.B, cfg.H, cfg.n, cfg.d, cfg.m
+    print(f"[bench] generating {args.sets} input sets B={B} H={H} n={n} d={d} m={m}", file=sys.stderr, flush=True)
+    sets = []
+    host0 = None
+    for si in range(args.sets):
+        x = fi.make_inputs(cfg, set_index=si)
+        if si == 0:
+            host0 = x
+        sets.append({k: torch.from_numpy(v).to(device=dev, dtype=torch.bfloat16) for k, v in x.items()})
+        if si:
+            del x
+    W = sets[0]["W"]
+    outs_nc = [torch.empty((B, H, n, d), dtype=torch.float32, device=dev) for _ in sets]
+    outs_c = [torch.empty((B, H, n, d), dtype=torch.float32, device=dev) for _ in sets]
+    ws_nc = favor.Workspace(B, H, n, d, m, causal=False)
+    causal_ok = not args.noncausal_only
+    ws_c = None
+    if causal_ok:
+        try:
+            ws_c = favor.Workspace(B, H, n, d, m, causal=True)
+            t = sets[0]
+            favor.attention(t["q"], t["k"], t["v"], W, causal=True, out=outs_c[0], workspace=ws_c)
+            torch.cuda.synchronize()
+        except favor.FavorError as e:
+            print(f"[bench] causal path unavailable: {e}", file=sys.stderr)
+            causal_ok = False
+
+    def step(i):
+        t = sets[i % len(sets)]
+        favor.attention(t["q"], t["k"], t["v"], W, causal=False, out=outs_nc[i % len(sets)], workspace=ws_nc)
+        if causal_ok:
+            favor.attention(t["q"], t["k"], t["v"], W, causal=True, out=outs_c[i % len(sets)], workspace=ws_c)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    _lib.check(_lib.favor_profile_enable())
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    prof = _lib.favor_profile_collect()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {ms:.4f} ms/step; kernels: " +
+          ", ".join(f"{k} {c}x {t / c * 1e3:.1f}us" for k, (c, t) in prof.items()),
+          file=sys.stderr, flush=True)
+
+    tokens = B * n
+    value = tokens / (ms * 1e-3)
+    # dominant kernel = largest total time in the timed region
+    dom = max(prof.items(), key=lambda kv: kv[1][1])
+    dname, (dcount, dtotal) = dom
+    avg_ms = dtotal / dcount
+    dbytes = kernel_bytes(dname, B, H, n, d, m)
+    achieved = dbytes / (avg_ms * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = read_traffic(dname, digest)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": dname,
+        "kernel_us": round(avg_ms * 1e3, 2),
+        "bytes_per_launch": dbytes,
+    }
+    # whole-call view: algorithmic bytes and flops of each attention call
+    call_bytes = 10.0 * B * H * n * d + 2.0 * H * m * d
+    call_flops = (8.0 * n * m * d + 4.0 * n * m) * B * H
+    kernels = {k: {"launches": c, "mean_us": round(t / c * 1e3, 2)} for k, (c, t) in prof.items()}
+    per_call = {}
+    groups = {"noncausal": ("k_kv_state", "k_merge", "k_output"),
+              "causal": ("k_causal_state", "k_causal_scan", "k_causal_output")}
+    for g, names in groups.items():
+        us = sum(kernels[k]["mean_us"] for k in names if k in kernels)
+        if us > 0:
+            per_call[g] = {
+                "kernel_us": round(us, 2),
+                "tokens_per_s": round(tokens / (us * 1e-6), 1),
+                "hbm_frac": round(call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "tflops": round(call_flops / (us * 1e-6) / 1e12, 2),
+            }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(host0, cfg, causal_ok)
+
+    out = {
+        "metric": "FAVOR+ attention tokens/sec and % MI355X roofline (n=16k, d=64, m=256)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, Q/K scaled by d^-1/4; orthogonal random W per head)",
+        "config": {
+            "workload": "FAVOR+ attention B=4 H=8 n=16384 d=64 m=256, bf16 in / fp32 out; step = "
+                        + ("non-causal + causal (chunk 64)" if causal_ok else "non-causal only"),
+            "B": B, "H": H, "n": n, "d": d, "m": m, "chunk": 64,
+            "global_batch": B, "seq_len": n, "input_sets": len(sets),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_call": per_call,
+        "kernels": kernels,
+        "sources": digest,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -14,7 +14,7 @@ library is measured on:
   C4  bf16,  B=2,  H=12, n=32768, d=64, m=256  (causal, chunk 64)
   C5  bf16,  B=32, H=12, n=4096,  d=64, m=128  (non-causal, vision-style low-rank Q/K)
 
-Q and K entries are N(0,1) scaled by d^(-1/4) (so q.k already carries the
+Q and K entries are N(0,1) (drawn in float32) scaled by d^(-1/4) (so q.k already carries the
 1/sqrt(d) softmax temperature); V entries are N(0,1). The vision workload draws
 Q and K as a rank-16 product plus 0.1 N(0,1) noise before the same scaling.
 """
@@ -71,21 +71,22 @@ def config(name: str, **overrides) -> Config:
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round to the nearest bfloat16 value (ties to even), returned as float32.
 
-    The value goes fp64 -> fp32 (round to nearest even) -> bf16 (round to
-    nearest even).  The result is exactly representable in bf16, so the same
-    numbers can be handed to the device (as bits) and to a CPU checker (as
-    floats).
+    Non-float32 input is first converted to float32 (round to nearest even).
+    The result is exactly representable in bf16, so the same numbers can be
+    handed to the device (as bits) and to a CPU checker (as floats).  NaN stays
+    NaN and infinities stay infinite.
     """
-    f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    # NaN stays NaN (keep a quiet-NaN pattern); infinities round to themselves.
+    f = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = f.view(np.uint32)
     nan = np.isnan(f)
-    r = r.astype(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    del lsb
+    u &= np.uint32(0xFFFF0000)
     if nan.any():
-        r[nan] = 0x7FC00000
-    return r.view(np.float32).reshape(f.shape)
+        u[nan] = np.uint32(0x7FC00000)
+    return f
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -131,27 +132,47 @@ def iid_W(rng: np.random.Generator, H: int, m: int, d: int) -> np.ndarray:
 
 
 def draw_qk(rng: np.random.Generator, B: int, H: int, n: int, d: int, kind: str) -> np.ndarray:
-    """Q or K in fp64, [B, H, n, d], already multiplied by d^(-1/4)."""
+    """Q or K as float32 [B, H, n, d], already multiplied by d^(-1/4).
+
+    kind "iid": entries N(0, 1).  kind "lowrank": A B^T / sqrt(16) + 0.1 E with
+    A [n, 16], B [d, 16], E [n, d] all N(0, 1), drawn per (b, h).
+    """
+    f32 = np.float32
     if kind == "iid":
-        X = rng.standard_normal((B, H, n, d))
+        X = rng.standard_normal((B, H, n, d), dtype=f32)
     elif kind == "lowrank":
         r = 16
-        A = rng.standard_normal((B, H, n, r))
-        Bf = rng.standard_normal((B, H, d, r))
-        X = np.matmul(A, np.swapaxes(Bf, -1, -2)) / math.sqrt(r)
-        X += 0.1 * rng.standard_normal((B, H, n, d))
+        A = rng.standard_normal((B, H, n, r), dtype=f32)
+        Bf = rng.standard_normal((B, H, d, r), dtype=f32)
+        X = np.matmul(A, np.swapaxes(Bf, -1, -2))
+        X *= f32(1.0 / math.sqrt(r))
+        E = rng.standard_normal((B, H, n, d), dtype=f32)
+        E *= f32(0.1)
+        X += E
+        del E
     else:
         raise ValueError(kind)
-    X *= d ** -0.25
+    X *= f32(d ** -0.25)
     return X
 
 
 def draw_v(rng: np.random.Generator, B: int, H: int, n: int, d: int) -> np.ndarray:
-    return rng.standard_normal((B, H, n, d))
+    return rng.standard_normal((B, H, n, d), dtype=np.float32)
 
 
 def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
+        if x.dtype == np.float32 and x.flags.c_contiguous:
+            f = x.view(np.uint32)  # round in place: x is a fresh draw owned by the caller
+            nan = np.isnan(x)
+            lsb = (f >> 16) & np.uint32(1)
+            f += np.uint32(0x7FFF)
+            f += lsb
+            del lsb
+            f &= np.uint32(0xFFFF0000)
+            if nan.any():
+                f[nan] = np.uint32(0x7FC00000)
+            return x
         return round_bf16(x)
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
@@ -177,7 +198,11 @@ def make_inputs(cfg: Config, *, qk_scale: float = 1.0, w_kind: str = "orthogonal
     else:
         raise ValueError(w_kind)
     out = {"W": _cast(W, cfg.dtype)}
-    out["q"] = _cast(draw_qk(rq, cfg.B, cfg.H, cfg.n, cfg.d, cfg.qk) * qk_scale, cfg.dtype)
-    out["k"] = _cast(draw_qk(rk, cfg.B, cfg.H, cfg.n, cfg.d, cfg.qk) * qk_scale, cfg.dtype)
+    for name, r in (("q", rq), ("k", rk)):
+        X = draw_qk(r, cfg.B, cfg.H, cfg.n, cfg.d, cfg.qk)
+        if qk_scale != 1.0:
+            X *= np.float32(qk_scale)
+        out[name] = _cast(X, cfg.dtype)
+        del X
     out["v"] = _cast(draw_v(rv, cfg.B, cfg.H, cfg.n, cfg.d), cfg.dtype)
     return out

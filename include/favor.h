@@ -82,7 +82,7 @@ favor_status_t favor_feature_map_f32(const float* x, const float* W, float* phi,
  * query i sees keys j <= i (Performer for vision, Step 2); identical to
  * favor_attention_causal with chunk = 0.
  *   q, k, v : bf16 [B,H,n,d]     W : bf16 [H,m,d]        out : fp32 [B,H,n,d]
- * bf16 path: d == 64; m in {64, 128, 192, 256, 320, 384, 448, 512}; pointers
+ * bf16 path: d == 64; m in {64, 128, 256}; pointers
  * 16-byte aligned; otherwise FAVOR_ERR_UNSUPPORTED.  Scratch is allocated
  * stream-ordered on `stream` (see favor_attention_ws to supply it).
  */
@@ -126,6 +126,19 @@ size_t favor_workspace_bytes(int B, int H, int n, int d, int m, int causal);
 favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, const void* W,
                                   float* out, int B, int H, int n, int d, int m, int causal,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Diagnostics: per-kernel timing with HIP events.  favor_profile_enable()
+ * starts recording on the calling thread: every kernel the library launches
+ * from that thread is bracketed by two HIP events recorded on the launch
+ * stream.  favor_profile_collect() waits for those events, writes up to
+ * `capacity` entries (kernel name, launch count, total milliseconds; names
+ * are static strings owned by the library), stops recording, clears the
+ * record and returns the number of distinct kernels (which may exceed
+ * capacity).  Returns -1 if a HIP event call failed.
+ */
+favor_status_t favor_profile_enable(void);
+int favor_profile_collect(const char** names, int* counts, double* total_ms, int capacity);
 
 #ifdef __cplusplus
 }

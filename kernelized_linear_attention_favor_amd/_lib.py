@@ -10,7 +10,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfavor.so")
+# LIBFAVOR_PATH selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("LIBFAVOR_PATH") or os.path.join(_HERE, "libfavor.so")
 
 FAVOR_OK = 0
 FAVOR_ERR_INVALID_ARGUMENT = 1
@@ -35,6 +36,9 @@ SIGNATURES = {
     "favor_attention_causal_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "favor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "favor_attention_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "favor_profile_enable": (_i, []),
+    "favor_profile_collect": (_i, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_i),
+                                   ctypes.POINTER(ctypes.c_double), _i]),
 }
 
 _lib = None
@@ -111,3 +115,18 @@ def favor_workspace_bytes(B, H, n, d, m, causal) -> int:
 
 def favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream) -> int:
     return lib().favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream)
+
+
+def favor_profile_enable() -> int:
+    return lib().favor_profile_enable()
+
+
+def favor_profile_collect(capacity: int = 32) -> dict:
+    """{kernel name: (launch count, total ms)} for launches since favor_profile_enable()."""
+    names = (ctypes.c_char_p * capacity)()
+    counts = (_i * capacity)()
+    tot = (ctypes.c_double * capacity)()
+    k = lib().favor_profile_collect(names, counts, tot, capacity)
+    if k < 0:
+        raise FavorError(FAVOR_ERR_HIP, "HIP event failure while collecting kernel timings")
+    return {names[i].decode(): (counts[i], tot[i]) for i in range(min(k, capacity))}

@@ -8,7 +8,48 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "favor_internal.h"
+
+namespace favor {
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct Profiler {
+  bool on = false;
+  bool failed = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) failed = true;
+    return e;
+  }
+};
+thread_local Profiler g_prof;
+}  // namespace
+
+void prof_begin(hipStream_t s, const char* name) {
+  if (!g_prof.on) return;
+  ProfRec r{name, g_prof.get(), g_prof.get()};
+  if (r.start && hipEventRecord(r.start, s) != hipSuccess) g_prof.failed = true;
+  g_prof.recs.push_back(r);
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_prof.on || g_prof.recs.empty()) return;
+  hipEvent_t e = g_prof.recs.back().stop;
+  if (e && hipEventRecord(e, s) != hipSuccess) g_prof.failed = true;
+}
+}  // namespace favor
 
 namespace {
 
@@ -69,7 +110,7 @@ favor_status_t check_bf16(const void* q, const void* k, const void* v, const voi
   if ((st = check_ptrs(q, k, v, W, out, 16)) != FAVOR_OK) return st;
   if (!favor::bf16_supported(d, m))
     return fail(FAVOR_ERR_UNSUPPORTED,
-                "bf16 attention supports d = 64 and m in {64, 128, 192, 256} (d=%d m=%d)", d, m);
+                "bf16 attention supports d = 64 and m in {64, 128, 256} (d=%d m=%d)", d, m);
   return FAVOR_OK;
 }
 
@@ -117,6 +158,47 @@ favor_status_t run_bf16(const void* q, const void* k, const void* v, const void*
 extern "C" {
 
 int favor_version(void) { return 10000; }
+
+favor_status_t favor_profile_enable(void) {
+  favor::g_prof.on = true;
+  return ok();
+}
+
+int favor_profile_collect(const char** names, int* counts, double* total_ms, int capacity) {
+  auto& P = favor::g_prof;
+  std::vector<const char*> uniq;
+  std::vector<int> cnt;
+  std::vector<double> tot;
+  bool failed = P.failed;
+  for (auto& r : P.recs) {
+    float ms = 0.f;
+    if (!r.start || !r.stop || hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      failed = true;
+    }
+    size_t i = 0;
+    while (i < uniq.size() && strcmp(uniq[i], r.name) != 0) ++i;
+    if (i == uniq.size()) {
+      uniq.push_back(r.name);
+      cnt.push_back(0);
+      tot.push_back(0.0);
+    }
+    cnt[i] += 1;
+    tot[i] += ms;
+    if (r.start) P.pool.push_back(r.start);
+    if (r.stop) P.pool.push_back(r.stop);
+  }
+  P.recs.clear();
+  P.on = false;
+  P.failed = false;
+  for (size_t i = 0; i < uniq.size() && static_cast<int>(i) < capacity; ++i) {
+    if (names) names[i] = uniq[i];
+    if (counts) counts[i] = cnt[i];
+    if (total_ms) total_ms[i] = tot[i];
+  }
+  if (failed) return -1;
+  return static_cast<int>(uniq.size());
+}
 
 const char* favor_status_string(favor_status_t s) {
   switch (s) {

@@ -29,31 +29,14 @@
 //     parts in an extra k-block) accumulate in fp32.
 #include <math.h>
 
+#include "favor_bf16_common.h"
 #include "favor_internal.h"
 #include "favor_mfma.h"
 
 namespace favor {
 namespace {
 
-constexpr int kD = 64;          // head dimension supported by the MFMA path
-constexpr int kKT = 64;         // key tokens staged per iteration (two 32-token MFMA tiles)
-constexpr int kKStride = 88;    // bf16 per staged key row: 64 d + 8 aug + 8 zero + 8 pad
-constexpr int kVStride = 72;    // bf16 per staged value column: 64 tokens + 8 pad
-constexpr uint32_t kBf16One = 0x3f80u;
-constexpr float kFInf = __builtin_huge_valf();
-
-__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-// Three bf16 parts whose sum carries x to about 24 bits.
-__device__ __forceinline__ void split3_bf16(float x, uint32_t& w01, uint32_t& w23) {
-  const uint32_t p0 = pack_bf16(x, 0.f);
-  const float r1 = x - bf16_lo_as_f32(p0);
-  const uint32_t p1 = pack_bf16(r1, 0.f);
-  const float r2 = r1 - bf16_lo_as_f32(p1);
-  const uint32_t p2 = pack_bf16(r2, 0.f);
-  w01 = (p0 & 0xffffu) | (p1 << 16);
-  w23 = p2 & 0xffffu;
-}
+using namespace bf16k;
 
 // ---------------------------------------------------------------------------
 // k_kv_state: one workgroup = NW waves = 64*NW features (all m features) of
@@ -71,29 +54,51 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& w01, uint32_t& w2
 // If any phi overflowed (a later key far above the first tile), the range is
 // recomputed with c_f set by a max-only pass.
 // ---------------------------------------------------------------------------
+constexpr int kKBuf = 2;   // staged key/value tiles (double buffering)
+
 template <int NW>
 struct KvSmem {
-  uint16_t ks[2][kKT * kKStride];
-  uint16_t vt[2][kD * kVStride];
+  uint16_t k[kKBuf][kKT * kD];
+  uint16_t v[kKBuf][kKT * kD];
+  uint32_t aug[kKBuf][kKT * 2];   // per key: bf16 parts of -|k|^2/2, packed (p0 | p1 << 16, p2)
   int flag;
 };
 
+// 16-byte chunks of one 64-key tile (64 keys x 8 chunks) held per thread.
 template <int NW>
-__device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const u32x4* kreg,
-                                         const u32x4* vreg, int tid) {
-  constexpr int NT = NW * 64;
-  constexpr int R = (kKT * 8 + NT - 1) / NT;  // 16-byte chunks per thread per tensor
+struct KvRegs {
+  static constexpr int R = (kKT * 8) / (NW * 64);
+  u32x4 k[R], v[R];
+};
+
+// Global -> registers for one tile.  Keys past the end of the range are
+// clamped to the last key (finite data; their weights are masked later).
+template <int NW>
+__device__ __forceinline__ void load_kv(KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
+                                        int tile0, int ntok, int tid) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int c = tid + NT * r;
-    if (c >= kKT * 8) break;  // whole waves drop out together (NT is a multiple of 64)
-    const int tok = c >> 3, ch = c & 7;
-    *reinterpret_cast<u32x4*>(&sm.ks[buf][tok * kKStride + ch * 8]) = kreg[r];
-    // -|k|^2/2 from the 8 threads holding this token's 64 values
+  for (int i = 0; i < KvRegs<NW>::R; ++i) {
+    const int c = tid + NW * 64 * i;
+    const int tok = min(tile0 + (c >> 3), ntok - 1), ch = c & 7;
+    r.k[i] = *reinterpret_cast<const u32x4*>(Kb + static_cast<size_t>(tok) * kD + ch * 8);
+    r.v[i] = *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(tok) * kD + ch * 8);
+  }
+}
+
+// Registers -> swizzled LDS tile, plus -|k|^2/2 of each key as three bf16
+// parts (the 8 threads holding a key's 8 chunks are adjacent lanes).
+template <int NW>
+__device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<NW>& r, int tid) {
+#pragma unroll
+  for (int i = 0; i < KvRegs<NW>::R; ++i) {
+    const int c = tid + NW * 64 * i;
+    const int key = c >> 3, ch = c & 7;
+    *reinterpret_cast<u32x4*>(&sm.k[buf][swz(key, ch)]) = r.k[i];
+    *reinterpret_cast<u32x4*>(&sm.v[buf][swz(key, ch)]) = r.v[i];
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float a = bf16_lo_as_f32(kreg[r][w]), b = bf16_hi_as_f32(kreg[r][w]);
+      const float a = bf16_lo_as_f32(r.k[i][w]), b = bf16_hi_as_f32(r.k[i][w]);
       s = fmaf(a, a, s);
       s = fmaf(b, b, s);
     }
@@ -103,150 +108,105 @@ __device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const u32x4* k
     if (ch == 0) {
       uint32_t w01, w23;
       split3_bf16(-0.5f * s, w01, w23);
-      *reinterpret_cast<u32x4*>(&sm.ks[buf][tok * kKStride + 64]) = u32x4{w01, w23, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.ks[buf][tok * kKStride + 72]) = u32x4{0u, 0u, 0u, 0u};
-    }
-    // V transposed: vt[dv][pos(tok)], pos applies the k-block slot permutation
-    const int pos = (tok & ~15) | kblock_pos(tok & 15);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      sm.vt[buf][(ch * 8 + 2 * w) * kVStride + pos] = static_cast<uint16_t>(vreg[r][w] & 0xffffu);
-      sm.vt[buf][(ch * 8 + 2 * w + 1) * kVStride + pos] = static_cast<uint16_t>(vreg[r][w] >> 16);
+      *reinterpret_cast<u32x2*>(&sm.aug[buf][2 * key]) = u32x2{w01, w23};
     }
   }
 }
 
-template <int NW>
-__device__ __forceinline__ void load_kv(const uint16_t* Kb, const uint16_t* Vb, int tile0, int ntok,
-                                        u32x4* kreg, u32x4* vreg, int tid) {
-  constexpr int NT = NW * 64;
-  constexpr int R = (kKT * 8 + NT - 1) / NT;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int c = tid + NT * r;
-    if (c >= kKT * 8) break;
-    const int tok = tile0 + (c >> 3), ch = c & 7;
-    if (tok < ntok) {
-      kreg[r] = *reinterpret_cast<const u32x4*>(Kb + static_cast<size_t>(tok) * kD + ch * 8);
-      vreg[r] = *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(tok) * kD + ch * 8);
-    } else {
-      kreg[r] = u32x4{0u, 0u, 0u, 0u};
-      vreg[r] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-// MODE 0: accumulate, first tile fixes c.  MODE 1: max only.  MODE 2: accumulate with fixed c.
-template <int NW, int MODE>
+// MODE 0: accumulate, first tile fixes c.  MODE 1: max only.  MODE 2: accumulate
+// with fixed c.  PARTIAL: the tile runs past the end of the key range, so the
+// tail keys are masked.  Each wave owns one 32-feature tile.
+template <int NW, int MODE, bool PARTIAL>
 __device__ __forceinline__ void kv_tile(KvSmem<NW>& sm, int buf, int tile0, int ntok,
-                                        const u32x4 (&wB)[2][4], const u32x4 augB, float (&c)[2],
-                                        float (&z)[2], f32x16 (&sacc)[2][2], bool& cinit, int col,
-                                        int half) {
+                                        const u32x4 (&wB)[4], const u32x4 augB, float& c,
+                                        float& z, f32x16 (&sacc)[2], bool& cinit, int col,
+                                        int half, int lane) {
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     const int tok_base = tile0 + 32 * st;
-    if (tok_base >= ntok) break;
-    const bool partial = tok_base + 32 > ntok;
-    bf16x8 ka[5];
+    if (PARTIAL && tok_base >= ntok) break;
+    const int row = 32 * st + col;
+    f32x16 pacc = {};
 #pragma unroll
-    for (int kb = 0; kb < 5; ++kb)
-      ka[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-          &sm.ks[buf][(32 * st + col) * kKStride + 16 * kb + 8 * half]));
-    f32x16 pacc[2];
-#pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16(ka[kb], as_bf16x8(wB[ft][kb]), acc);
-      acc = mfma_bf16(ka[4], as_bf16x8(augB), acc);
+    for (int kb = 0; kb < 4; ++kb)
+      pacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][swz(row, 2 * kb + half)])),
+                       as_bf16x8(wB[kb]), pacc);
+    {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.aug[buf][2 * row]);
+      const u32x4 ka4 = half == 0 ? u32x4{a[0], a[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+      pacc = mfma_bf16(as_bf16x8(ka4), as_bf16x8(augB), pacc);
+    }
+    if (PARTIAL) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float e = acc[i] * kLog2e;
-        if (partial) {
-          const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-          if (tok_base + row >= ntok) e = -kFInf;
-        }
-        acc[i] = e;
+        const int r = 8 * (i >> 2) + 4 * half + (i & 3);
+        if (tok_base + r >= ntok) pacc[i] = -kFInf;
       }
-      pacc[ft] = acc;
     }
     if (MODE == 1 || (MODE == 0 && !cinit)) {
+      float mx = pacc[0];
 #pragma unroll
-      for (int ft = 0; ft < 2; ++ft) {
-        float mx = pacc[ft][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pacc[ft][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        c[ft] = fmaxf(c[ft], mx);
-      }
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pacc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      c = fmaxf(c, mx * kLog2e);
       cinit = true;
     }
     if (MODE == 1) continue;
-    // value operand: B[k = token slot][n = dv], read from the transposed stage
-    u32x4 vb[2][2];
+    const float nc = -c;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      u32x4 hi, lo;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-        vb[dt][kb2] = *reinterpret_cast<const u32x4*>(
-            &sm.vt[buf][(32 * dt + col) * kVStride + 32 * st + 16 * kb2 + 8 * half]);
-#pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(pacc[ft][i] - c[ft]);
-        z[ft] += p[i];
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w], kLog2e, nc));
+        const float p1 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w + 1], kLog2e, nc));
+        z += p0 + p1;
+        uint32_t h_, l_;
+        split_bf16_trunc(p0, p1, h_, l_);
+        hi[w] = h_;
+        lo[w] = l_;
       }
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        u32x4 hi, lo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t h_, l_;
-          split_bf16(p[8 * kb2 + 2 * w], p[8 * kb2 + 2 * w + 1], h_, l_);
-          hi[w] = h_;
-          lo[w] = l_;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          sacc[ft][dt] = mfma_bf16(as_bf16x8(hi), as_bf16x8(vb[dt][kb2]), sacc[ft][dt]);
-          sacc[ft][dt] = mfma_bf16(as_bf16x8(lo), as_bf16x8(vb[dt][kb2]), sacc[ft][dt]);
-        }
+      for (int dt = 0; dt < 2; ++dt) {
+        const u32x4 vb = v_operand(sm.v[buf], 32 * st + 16 * kb2, dt, lane);
+        sacc[dt] = mfma_bf16(as_bf16x8(hi), as_bf16x8(vb), sacc[dt]);
+        sacc[dt] = mfma_bf16(as_bf16x8(lo), as_bf16x8(vb), sacc[dt]);
       }
     }
   }
 }
 
+// One pass over the key range.  The next tile is loaded into registers while
+// the current one is computed from LDS, then staged into the other buffer.
 template <int NW, int MODE>
-__device__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb, int ntok,
-                         const u32x4 (&wB)[2][4], const u32x4 augB, float (&c)[2], float (&z)[2],
-                         f32x16 (&sacc)[2][2], bool& cinit, int tid, int col, int half) {
-  constexpr int R = (kKT * 8 + NW * 64 - 1) / (NW * 64);
+__device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb,
+                                         int ntok, const u32x4 (&wB)[4], const u32x4 augB,
+                                         float& c, float& z, f32x16 (&sacc)[2], bool& cinit,
+                                         int tid, int lane, int col, int half) {
   const int ntiles = (ntok + kKT - 1) / kKT;
-  u32x4 kreg[R], vreg[R];
+  KvRegs<NW> r;
   if (ntiles > 0) {
-    load_kv<NW>(Kb, Vb, 0, ntok, kreg, vreg, tid);
-    stage_kv<NW>(sm, 0, kreg, vreg, tid);
+    load_kv<NW>(r, Kb, Vb, 0, ntok, tid);
+    stage_kv<NW>(sm, 0, r, tid);
   }
-  __syncthreads();
+  lds_barrier();
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
-    if (more) load_kv<NW>(Kb, Vb, (t + 1) * kKT, ntok, kreg, vreg, tid);
-    kv_tile<NW, MODE>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, col, half);
-    if (more) stage_kv<NW>(sm, (t + 1) & 1, kreg, vreg, tid);
-    __syncthreads();
+    if (more) load_kv<NW>(r, Kb, Vb, (t + 1) * kKT, ntok, tid);
+    if ((t + 1) * kKT <= ntok)
+      kv_tile<NW, MODE, false>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, col, half, lane);
+    else
+      kv_tile<NW, MODE, true>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, col, half, lane);
+    if (more) stage_kv<NW>(sm, (t + 1) & 1, r, tid);
+    lds_barrier();
   }
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void k_kv_state(const uint16_t* __restrict__ K,
-                                                         const uint16_t* __restrict__ V,
-                                                         const uint16_t* __restrict__ W,
-                                                         float* __restrict__ part_S,
-                                                         float* __restrict__ part_zc, int H,
-                                                         int n, int splits, int span) {
-  constexpr int M = NW * 64;
+__global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
+    float* __restrict__ part_S, float* __restrict__ part_zc, int H, int n, int splits, int span) {
+  constexpr int M = NW * 32;
   __shared__ __attribute__((aligned(16))) KvSmem<NW> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -258,70 +218,62 @@ __global__ __launch_bounds__(NW * 64, 2) void k_kv_state(const uint16_t* __restr
   const int ntok = max(0, min(n, j0 + span) - j0);
   const uint16_t* Kb = K + (static_cast<size_t>(bh) * n + j0) * kD;
   const uint16_t* Vb = V + (static_cast<size_t>(bh) * n + j0) * kD;
+  const int f = 32 * wave + col;   // this lane's feature (B operand column of the projection)
 
-  u32x4 wB[2][4];
+  u32x4 wB[4];
 #pragma unroll
-  for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int f = 64 * wave + 32 * ft + col;
-      wB[ft][kb] = *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD +
-                                                   16 * kb + 8 * half);
-    }
+  for (int kb = 0; kb < 4; ++kb) {
+    wB[kb] = *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD + 16 * kb +
+                                             8 * half);
+    // Keep W resident: an opaque definition stops the compiler from re-loading
+    // it inside the key loop (whose vmcnt waits would also stall on the prefetch).
+    asm volatile("" : "+v"(wB[kb]));
+  }
   const u32x4 augB = half == 0 ? u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u}
                                : u32x4{0u, 0u, 0u, 0u};
 
-  float c[2] = {-kFInf, -kFInf}, z[2] = {0.f, 0.f};
-  f32x16 sacc[2][2] = {};
+  float c = -kFInf, z = 0.f;
+  f32x16 sacc[2] = {};
   bool cinit = false;
-  kv_range<NW, 0>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, col, half);
-
-  // Overflow guard: a key far above the first tile's maximum makes phi, z or S
-  // non-finite; recompute the range with c from a max-only pass.
-  bool bad = !(fabsf(z[0]) <= 3.0e38f) || !(fabsf(z[1]) <= 3.0e38f);
+  // Pass 0 accumulates with c fixed from the first tile.  If a later key sat
+  // far above that tile's maximum, phi, z or S overflowed: then a max-only
+  // pass finds the exact maximum over the range and the range is accumulated
+  // again with it.
+  kv_range<NW, 0>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane, col, half);
+  bool bad = !(fabsf(z) <= 3.0e38f);
 #pragma unroll
-  for (int ft = 0; ft < 2; ++ft)
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bad |= !(fabsf(sacc[ft][dt][i]) <= 3.0e38f);
+    for (int i = 0; i < 16; ++i) bad |= !(fabsf(sacc[dt][i]) <= 3.0e38f);
   if (tid == 0) sm.flag = 0;
   __syncthreads();
   if (bad) sm.flag = 1;
   __syncthreads();
   if (sm.flag) {
-    c[0] = c[1] = -kFInf;
-    z[0] = z[1] = 0.f;
-#pragma unroll
-    for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) sacc[ft][dt] = f32x16{};
-    kv_range<NW, 1>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, col, half);
-    kv_range<NW, 2>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, col, half);
+    c = -kFInf;
+    z = 0.f;
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+    kv_range<NW, 1>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane, col, half);
+    kv_range<NW, 2>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane, col, half);
   }
 
   // write this range's partial state
   const size_t base = static_cast<size_t>(bh) * splits + split;
   float* zc = part_zc + base * 2 * M;
-#pragma unroll
-  for (int ft = 0; ft < 2; ++ft) {
-    const float zt = z[ft] + __shfl_xor(z[ft], 32);
-    const int f = 64 * wave + 32 * ft + col;
-    if (half == 0) {
-      zc[f] = zt;
-      zc[M + f] = c[ft];
-    }
+  const float zt = z + __shfl_xor(z, 32);
+  if (half == 0) {
+    zc[f] = zt;
+    zc[M + f] = c;
   }
   float* Sb = part_S + base * M * kD;
 #pragma unroll
-  for (int ft = 0; ft < 2; ++ft)
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int f = 64 * wave + 32 * ft + 8 * (i >> 2) + 4 * half + (i & 3);
-        Sb[static_cast<size_t>(f) * kD + 32 * dt + col] = sacc[ft][dt][i];
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int fr = 32 * wave + 8 * (i >> 2) + 4 * half + (i & 3);
+      Sb[static_cast<size_t>(fr) * kD + 32 * dt + col] = sacc[dt][i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -345,19 +297,22 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
   float y[8];
   float amax[8];
   if (f < m) {
+    const float* zc0 = part_zc + static_cast<size_t>(bh) * splits * 2 * m;
     float cm = -kFInf;
-    for (int s = 0; s < splits; ++s)
-      cm = fmaxf(cm, part_zc[(static_cast<size_t>(bh) * splits + s) * 2 * m + m + f]);
+#pragma unroll 4
+    for (int s = 0; s < splits; ++s) cm = fmaxf(cm, zc0[static_cast<size_t>(s) * 2 * m + m + f]);
     float zt = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 8 * g;
+#pragma unroll 4
     for (int s = 0; s < splits; ++s) {
-      const size_t base = static_cast<size_t>(bh) * splits + s;
-      const float cs = part_zc[base * 2 * m + m + f];
-      if (cs == -kFInf) continue;
-      const float a = exp2f(cs - cm);
-      zt = fmaf(a, part_zc[base * 2 * m + f], zt);
-      const f32x4* row = reinterpret_cast<const f32x4*>(part_S + (base * m + f) * kD + 8 * g);
+      const float cs = zc0[static_cast<size_t>(s) * 2 * m + m + f];
+      const float zs = zc0[static_cast<size_t>(s) * 2 * m + f];
+      const f32x4* row = reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
       const f32x4 r0 = row[0], r1 = row[1];
+      // an empty range has c = -inf and contributes nothing
+      const float a = (cs == -kFInf) ? 0.f : exp2f(cs - cm);
+      zt = fmaf(a, zs, zt);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         acc[cc] = fmaf(a, r0[cc], acc[cc]);
@@ -418,45 +373,6 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
 //   [num | den] = u [yhat' | 1]                        (fp16 MFMA, fp32 acc)
 //   y = sigma * num / den
 // ---------------------------------------------------------------------------
-constexpr int kWStride = 80;   // bf16 per staged W' row: 64 d + 8 beta parts + 8 zero
-
-// Projection of one 32-feature tile: D[feature, query] = w_f.q + beta_f.
-__device__ __forceinline__ f32x16 out_proj(const uint16_t* wsh, int ft, int col, int half,
-                                           const u32x4 (&qB)[4], const u32x4 augB) {
-  f32x16 acc = {};
-  const uint16_t* wr = &wsh[(32 * ft + col) * kWStride + 8 * half];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(wr + 16 * kb)), as_bf16x8(qB[kb]),
-                    acc);
-  return mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(wr + 64)), as_bf16x8(augB), acc);
-}
-
-// Softmax weights of one feature tile -> fp16 A operand -> numerator and
-// denominator MFMAs.  tmax tracks the largest exponent used (log2 units).
-__device__ __forceinline__ void out_accumulate(const f32x16& pa, float off, int ft,
-                                               const uint16_t* ysh, int YS, int col, int half,
-                                               const u32x4 onesB, f32x16& yacc0, f32x16& yacc1,
-                                               f32x16& dacc, float& tmax) {
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    u32x4 a;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float e0 = fmaf(pa[8 * kb2 + 2 * w], kLog2e, off);
-      const float e1 = fmaf(pa[8 * kb2 + 2 * w + 1], kLog2e, off);
-      tmax = fmaxf(tmax, fmaxf(e0, e1));
-      a[w] = pack_f16(fast_exp2(e0), fast_exp2(e1));
-    }
-    const int kpos = 32 * ft + 16 * kb2 + 8 * half;
-    const u32x4 b0 = *reinterpret_cast<const u32x4*>(&ysh[col * YS + kpos]);
-    const u32x4 b1 = *reinterpret_cast<const u32x4*>(&ysh[(32 + col) * YS + kpos]);
-    yacc0 = mfma_f16(as_f16x8(a), as_f16x8(b0), yacc0);
-    yacc1 = mfma_f16(as_f16x8(a), as_f16x8(b1), yacc1);
-    dacc = mfma_f16(as_f16x8(a), as_f16x8(onesB), dacc);
-  }
-}
-
 template <int MT>
 __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ Q,
                                                    const uint16_t* __restrict__ W,
@@ -507,23 +423,29 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * kD;
   float* Ob = out + static_cast<size_t>(bh) * n * kD;
 
-  for (int tb = t0 + 32 * wave; tb < t1; tb += 128) {
+  auto load_q = [&](int tb, u32x4 (&qB)[4]) {
     const int qt = tb + col;  // this lane's query (B operand column)
-    u32x4 qB[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
       qB[kb] = (qt < t1) ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * kD +
                                                             16 * kb + 8 * half)
                          : u32x4{0u, 0u, 0u, 0u};
-    // Shift: the first feature tile's row maximum plus 8 (log2 units).  Any
-    // later feature more than 23 above it would overflow fp16; that case is
+  };
+  u32x4 qB[4], qN[4];
+  int tb = t0 + 32 * wave;
+  if (tb < t1) load_q(tb, qB);
+  for (; tb < t1; tb += 128) {
+    // Shift: the first feature tile's row maximum (log2 units), so the largest
+    // weights sit near 1 with the whole fp16 normal range below them.  A later
+    // feature more than 2^15 above it would overflow fp16; that case is
     // detected and the tile is redone with the exact row maximum.
     f32x16 p0 = out_proj(wsh, 0, col, half, qB, augB);
+    if (tb + 128 < t1) load_q(tb + 128, qN);  // next tile's queries, in flight during this one
     float mx = p0[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, p0[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float off = -fmaf(mx, kLog2e, 8.0f);
+    float off = -mx * kLog2e;
     f32x16 yacc0 = {}, yacc1 = {}, dacc = {};
     float tmax = -kFInf;
     out_accumulate(p0, off, 0, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
@@ -552,24 +474,37 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
         out_accumulate(pa, off, ft, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
       }
     }
+    float* orow = Ob + static_cast<size_t>(tb) * kD;
+    if (tb + 32 <= t1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-      const int t = tb + row;
-      if (t < t1) {
-        const float inv = 1.0f / dacc[i];
-        Ob[static_cast<size_t>(t) * kD + col] = yacc0[i] * sg0 * inv;
-        Ob[static_cast<size_t>(t) * kD + 32 + col] = yacc1[i] * sg1 * inv;
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+        const float inv = fast_rcp(dacc[i]);
+        __builtin_nontemporal_store(yacc0[i] * sg0 * inv, orow + row * kD + col);
+        __builtin_nontemporal_store(yacc1[i] * sg1 * inv, orow + row * kD + 32 + col);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+        if (tb + row < t1) {
+          const float inv = fast_rcp(dacc[i]);
+          orow[row * kD + col] = yacc0[i] * sg0 * inv;
+          orow[row * kD + 32 + col] = yacc1[i] * sg1 * inv;
+        }
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qB[kb] = qN[kb];
   }
 }
 
 template <int NW>
 hipError_t launch_kv(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W,
                      float* pS, float* pzc, hipStream_t s) {
-  hipLaunchKernelGGL(k_kv_state<NW>, dim3(p.B * p.H * p.splits), dim3(NW * 64), 0, s, k, v, W, pS,
-                     pzc, p.H, p.n, p.splits, p.span);
+  // the causal path runs the same kernel over its segments; it is timed under its own name
+  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", k_kv_state<NW>, dim3(p.B * p.H * p.splits),
+               dim3(NW * 64), 0, s, k, v, W, pS, pzc, p.H, p.n, p.splits, p.span);
   return hipGetLastError();
 }
 
@@ -578,16 +513,14 @@ hipError_t launch_out(const Bf16Plan& p, const uint16_t* q, const uint16_t* W, c
                       const float* beta, const float* sigma, float* out, int span,
                       hipStream_t s) {
   const int nblk = (p.n + span - 1) / span;
-  hipLaunchKernelGGL(k_output<MT>, dim3(p.B * p.H * nblk), dim3(256), 0, s, q, W, yh, beta, sigma,
+  FAVOR_LAUNCH("k_output", k_output<MT>, dim3(p.B * p.H * nblk), dim3(256), 0, s, q, W, yh, beta, sigma,
                      out, p.H, p.n, span);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool bf16_supported(int d, int m) {
-  return d == kD && (m == 64 || m == 128 || m == 192 || m == 256);
-}
+bool bf16_supported(int d, int m) { return d == kD && (m == 64 || m == 128 || m == 256); }
 
 Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
   Bf16Plan p{};
@@ -598,13 +531,21 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
   p.m = m;
   p.causal = causal;
   const long long BH = static_cast<long long>(B) * H;
-  // aim for >= 512 state workgroups (two per CU), each with >= 64 keys
-  long long splits = (512 + BH - 1) / BH;
   const long long max_splits = (n + kKT - 1) / kKT;
+  long long splits;
+  if (causal) {
+    // one chunk-walking workgroup per CU: segments per (b, h)
+    splits = (256 + BH - 1) / BH;
+  } else {
+    // about 2048 state waves (8 per CU); a workgroup has m/32 waves
+    const long long wgs = 2048 / (m / 32);
+    splits = (wgs + BH - 1) / BH;
+  }
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
-  p.splits = static_cast<int>(splits);
-  p.span = static_cast<int>(align_up((n + splits - 1) / splits, kKT));
+  const long long span = align_up((n + splits - 1) / splits, kKT);
+  p.span = static_cast<int>(span);
+  p.splits = static_cast<int>((n + span - 1) / span);
   size_t o = 0;
   p.off_part_S = o;
   o = align_up(o + sizeof(float) * BH * p.splits * m * kD, 256);
@@ -616,7 +557,10 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
   o = align_up(o + sizeof(float) * BH * m, 256);
   p.off_sigma = o;
   o = align_up(o + sizeof(float) * BH * kD, 256);
-  p.off_carry = o;
+  p.off_carry_S = o;
+  if (causal) o = align_up(o + sizeof(float) * BH * p.splits * m * kD, 256);
+  p.off_carry_zc = o;
+  if (causal) o = align_up(o + sizeof(float) * BH * p.splits * 2 * m, 256);
   p.off_end = o;
   return p;
 }
@@ -624,34 +568,42 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
 hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                                  const uint16_t* v, const uint16_t* W, float* out, void* ws,
                                  hipStream_t s) {
-  if (p.causal) return hipErrorNotSupported;
   char* base = static_cast<char*>(ws);
   float* pS = reinterpret_cast<float*>(base + p.off_part_S);
   float* pzc = reinterpret_cast<float*>(base + p.off_part_zc);
   uint16_t* yh = reinterpret_cast<uint16_t*>(base + p.off_yhat);
   float* beta = reinterpret_cast<float*>(base + p.off_beta);
   float* sigma = reinterpret_cast<float*>(base + p.off_sigma);
-  hipError_t e;
-  switch (p.m) {
-    case 64: e = launch_kv<1>(p, k, v, W, pS, pzc, s); break;
-    case 128: e = launch_kv<2>(p, k, v, W, pS, pzc, s); break;
-    case 192: e = launch_kv<3>(p, k, v, W, pS, pzc, s); break;
-    case 256: e = launch_kv<4>(p, k, v, W, pS, pzc, s); break;
-    default: return hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
+  if (!p.causal || p.splits > 1) {
+    switch (p.m) {
+      case 64: e = launch_kv<2>(p, k, v, W, pS, pzc, s); break;
+      case 128: e = launch_kv<4>(p, k, v, W, pS, pzc, s); break;
+      case 256: e = launch_kv<8>(p, k, v, W, pS, pzc, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_merge, dim3(p.B * p.H * 8), dim3(256), 0, s, pS, pzc, yh, beta, sigma, p.m,
-                     p.splits);
+  if (p.causal) {
+    float* cS = reinterpret_cast<float*>(base + p.off_carry_S);
+    float* czc = reinterpret_cast<float*>(base + p.off_carry_zc);
+    if (p.splits > 1) {
+      e = launch_causal_scan(p, pS, pzc, cS, czc, s);
+      if (e != hipSuccess) return e;
+    }
+    return launch_causal_chunks(p, q, k, v, W, cS, czc, out, s);
+  }
+  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * 8), dim3(256), 0, s, pS, pzc, yh, beta, sigma,
+               p.m, p.splits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // output: about 512+ workgroups, each a contiguous run of query tiles
+  // output: about 512 workgroups, each a contiguous run of query tiles
   const long long BH = static_cast<long long>(p.B) * p.H;
-  long long per = (1024 + BH - 1) / BH;
+  long long per = (512 + BH - 1) / BH;
   long long span = (p.n + per - 1) / per;
   span = align_up(span < 128 ? 128 : span, 128);
   switch (p.m) {
     case 64: return launch_out<2>(p, q, W, yh, beta, sigma, out, static_cast<int>(span), s);
     case 128: return launch_out<4>(p, q, W, yh, beta, sigma, out, static_cast<int>(span), s);
-    case 192: return launch_out<6>(p, q, W, yh, beta, sigma, out, static_cast<int>(span), s);
     case 256: return launch_out<8>(p, q, W, yh, beta, sigma, out, static_cast<int>(span), s);
   }
   return hipErrorInvalidValue;

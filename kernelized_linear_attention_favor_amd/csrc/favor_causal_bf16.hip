@@ -1,0 +1,667 @@
+// bf16-input causal FAVOR+ attention on gfx950 (prefix-sum form, chunk 64).
+//
+// The method (Performer for vision, How It Works, Step 2; Performer notes,
+// Normalization): query i aggregates keys j <= i,
+//     y_i = phi(q_i)^T S_i / phi(q_i)^T z_i,  S_i = sum_{j<=i} phi(k_j) v_j^T,
+//     z_i = sum_{j<=i} phi(k_j).
+// Each (b, h) sequence is cut into segments (one workgroup each) and each
+// segment into chunks of 64 tokens:
+//   phase 1 (k_kv_state, shared with the non-causal path): per-segment state
+//            (S, z, per-feature shift c) of the segment's own keys;
+//   phase 2 (k_causal_scan): exclusive prefix over segments in index order,
+//            giving every segment the state of all keys before it;
+//   phase 3 (k_causal_chunks): walk the segment's chunks in order.  Query i of
+//            chunk t sums two terms,
+//     carry  phi(q_i)^T S and phi(q_i)^T z over the keys before the chunk, as a
+//            softmax over features with weights phi(q_i)_f z_f and values
+//            yhat_f = S_f / z_f (the state the non-causal output uses), and
+//     chunk  sum_{j in t, j <= i} (phi(q_i)^T phi(k_j)) v_j, from the chunk's own
+//            kernel matrix with one exponent shift per query and per key,
+//   each with its own log2 scale; the two are brought to the larger scale of
+//   the row before they are added, then S += Phi(K_t)^T V_t and z += Phi(K_t)^T 1.
+//   Normalising the chunk term per key (not per feature) keeps it exact for the
+//   first rows of a chunk, whose visible keys may be far smaller than the ones
+//   after them.  Factors common to a row (exp(-|q|^2/2), 1/sqrt(m)) cancel.
+#include <math.h>
+
+#include "favor_bf16_common.h"
+#include "favor_internal.h"
+#include "favor_mfma.h"
+
+namespace favor {
+namespace {
+
+using namespace bf16k;
+
+// ---------------------------------------------------------------------------
+// phase 2: carry_in[s] = merge of segment partials 0..s-1, in index order.
+// One workgroup per (b, h, 8 value columns); thread f owns feature f.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_causal_scan(const float* __restrict__ part_S,
+                                                     const float* __restrict__ part_zc,
+                                                     float* __restrict__ carry_S,
+                                                     float* __restrict__ carry_zc, int m,
+                                                     int nseg) {
+  const int bh = blockIdx.x >> 3;
+  const int g = blockIdx.x & 7;
+  const int f = threadIdx.x;
+  if (f >= m) return;
+  float c = -kFInf, z = 0.f;
+  float S[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nseg; ++s) {
+    const size_t base = static_cast<size_t>(bh) * nseg + s;
+    f32x4* dst = reinterpret_cast<f32x4*>(carry_S + (base * m + f) * kD + 8 * g);
+    dst[0] = f32x4{S[0], S[1], S[2], S[3]};
+    dst[1] = f32x4{S[4], S[5], S[6], S[7]};
+    if (g == 0) {
+      carry_zc[base * 2 * m + f] = z;
+      carry_zc[base * 2 * m + m + f] = c;
+    }
+    // Segment partials may be far from 1 (the state kernel only bounds them
+    // below overflow), so each one is first renormalised to z = 1 by folding
+    // log2 z into its shift; the running state is renormalised the same way.
+    float cp = part_zc[base * 2 * m + m + f];
+    const float zp = part_zc[base * 2 * m + f];
+    const f32x4* src = reinterpret_cast<const f32x4*>(part_S + (base * m + f) * kD + 8 * g);
+    const f32x4 r0 = src[0], r1 = src[1];
+    float bscale = 0.f;
+    if (cp != -kFInf && zp > 0.f) {
+      bscale = 1.0f / zp;
+      cp += log2f(zp);
+    } else {
+      cp = -kFInf;
+    }
+    const float cn = fmaxf(c, cp);
+    const float a = (c == -kFInf) ? 0.f : exp2f(c - cn);
+    const float b = (cp == -kFInf) ? 0.f : exp2f(cp - cn) * bscale;
+    z = fmaf(a, z, b * zp);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      S[k] = fmaf(a, S[k], b * r0[k]);
+      S[4 + k] = fmaf(a, S[4 + k], b * r1[k]);
+    }
+    c = cn;
+    if (z > 0.f) {
+      const float iz = 1.0f / z;
+      c += log2f(z);
+      z = 1.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) S[k] *= iz;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// phase 3
+// ---------------------------------------------------------------------------
+template <int NW>
+struct CsSmem {
+  static constexpr int M = NW * 32;
+  static constexpr int YS = M + 8;   // fp16 per row of the transposed yhat' table (padded)
+  uint16_t w[M * kD];                // W rows (swizzled like the token tiles)
+  uint16_t ysh[kD * YS];             // yhat_f / sigma_d, [value column][feature slot], fp16
+  uint16_t k[kKT * kD];              // chunk tiles, bf16, swizzled
+  uint16_t v[kKT * kD];
+  uint16_t q[kKT * kD];
+  float knorm[kKT];                  // -|k|^2/2 in log2 units; -inf past the segment end
+  float gam[M];                      // log2 of the running feature sums z_f (with shift)
+  float colmax[NW][kD];              // per wave: max_f |yhat_fd|
+  float np[NW][32 * kD];             // per wave: partial numerators [query][value]
+  float dp[NW][32];                  // per wave: partial denominators
+  float lp[NW][32];                  // per wave: log2 scale of the partials
+  float xs[NW][32];                  // per wave: per-feature scalars, lane -> register layout
+};
+
+template <int NW>
+struct CsRegs {
+  static constexpr int R = (kKT * 8) / (NW * 64);
+  u32x4 k[R], v[R], q[R];
+};
+
+template <int NW>
+__device__ __forceinline__ void cs_load(CsRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
+                                        const uint16_t* Qb, int t0, int ntok, int tid) {
+#pragma unroll
+  for (int i = 0; i < CsRegs<NW>::R; ++i) {
+    const int c = tid + NW * 64 * i;
+    const size_t off = static_cast<size_t>(min(t0 + (c >> 3), ntok - 1)) * kD + (c & 7) * 8;
+    r.k[i] = *reinterpret_cast<const u32x4*>(Kb + off);
+    r.v[i] = *reinterpret_cast<const u32x4*>(Vb + off);
+    r.q[i] = *reinterpret_cast<const u32x4*>(Qb + off);
+  }
+}
+
+// Tiles to LDS; per key -|k|^2/2 (log2 units), or -inf for keys past the end.
+template <int NW>
+__device__ __forceinline__ void cs_stage(CsSmem<NW>& sm, const CsRegs<NW>& r, int tid, int nvalid) {
+#pragma unroll
+  for (int i = 0; i < CsRegs<NW>::R; ++i) {
+    const int c = tid + NW * 64 * i;
+    const int key = c >> 3, ch = c & 7;
+    *reinterpret_cast<u32x4*>(&sm.k[swz(key, ch)]) = r.k[i];
+    *reinterpret_cast<u32x4*>(&sm.v[swz(key, ch)]) = r.v[i];
+    *reinterpret_cast<u32x4*>(&sm.q[swz(key, ch)]) = r.q[i];
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = bf16_lo_as_f32(r.k[i][w]), b = bf16_hi_as_f32(r.k[i][w]);
+      s = fmaf(a, a, s);
+      s = fmaf(b, b, s);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (ch == 0) sm.knorm[key] = key < nvalid ? -0.5f * kLog2e * s : -kFInf;
+  }
+}
+
+// D[row, token] = w_row . x_token for one 32-row tile of W (A operand, rows
+// from LDS) against 32 tokens (B operand xB).
+__device__ __forceinline__ f32x16 w_proj(const uint16_t* w, int row, int half, const u32x4 (&xB)[4]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&w[swz(row, 2 * kb + half)])),
+                    as_bf16x8(xB[kb]), acc);
+  return acc;
+}
+
+__device__ __forceinline__ void tile_rows(const uint16_t* t, int row, int half, u32x4 (&xB)[4]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) xB[kb] = *reinterpret_cast<const u32x4*>(&t[swz(row, 2 * kb + half)]);
+}
+
+// Row of D-layout register i inside a 32 x 32 tile, for lane half `half`.
+__device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+// Query side of one chunk for the wave's 32 queries (tile qt) and 64 features
+// (group fg): partial numerator, denominator and their log2 scale L_i.
+//   carry:  u_if = 2^(a_if + gam_f - mc_i) (fp16), mc_i = max_f (a_if + gam_f);
+//           sum_f u_if yhat'_f sigma and sum_f u_if, both times 2^(mc_i - L_i)
+//   chunk:  P_ij = sum_f 2^(a_if - alpha_i) 2^(b_jf - bmax_j)   (bf16 hi/lo, three MFMAs;
+//           bmax_j is the key's largest b_jf over the first 32 of the features)
+//           times 2^(beta_j - B_i), B_i = max of beta over the keys row i sees, and
+//           times 2^(alpha_i + B_i - L_i);  sum_j P_ij v_j and sum_j P_ij
+// with a_if = log2e w_f.q_i, b_jf = log2e w_f.k_j, beta_j = bmax_j - log2e |k_j|^2/2,
+// L_i = max(mc_i, alpha_i + B_i + log2 max_j P_ij).  The factor
+// exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
+template <int NW>
+__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float sg0,
+                                               float sg1) {
+  constexpr int YS = CsSmem<NW>::YS;
+  const int col = lane & 31, half = lane >> 5;
+  const int qt = wave / (NW / 2);
+  const int f0 = 64 * (wave % (NW / 2));
+
+  u32x4 xB[4];
+  tile_rows(sm.q, 32 * qt + col, half, xB);
+  f32x16 pa[2];
+  pa[0] = w_proj(sm.w, f0 + col, half, xB);
+  pa[1] = w_proj(sm.w, f0 + 32 + col, half, xB);
+  float amax = -kFInf, mc = -kFInf;
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.gam[f0 + 32 * ft + 8 * g4 + 4 * half]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g4 + j;
+        pa[ft][i] *= kLog2e;
+        amax = fmaxf(amax, pa[ft][i]);
+        mc = fmaxf(mc, pa[ft][i] + g[j]);
+      }
+    }
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  mc = fmaxf(mc, __shfl_xor(mc, 32));
+  const float mcs = mc == -kFInf ? 0.f : mc;
+
+  // carry weights (fp16, A operand: lane = query, k = feature) and their sum
+  u32x4 ua[2][2];
+  float dsc = 0.f;
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.gam[f0 + 32 * ft + 8 * g4 + 4 * half]);
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const int i = 4 * g4 + j;
+        const f16x2 hv = {static_cast<_Float16>(fast_exp2(pa[ft][i] + g[j] - mcs)),
+                          static_cast<_Float16>(fast_exp2(pa[ft][i + 1] + g[j + 1] - mcs))};
+        dsc += static_cast<float>(hv[0]) + static_cast<float>(hv[1]);
+        ua[ft][g4 >> 1][2 * (g4 & 1) + (j >> 1)] = __builtin_bit_cast(uint32_t, hv);
+      }
+    }
+  // query features of the chunk term, bf16 hi + lo (B operand: k = feature, n = query)
+  u32x4 ahi[2][2], alo[2][2];
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t h_, l_;
+        split_bf16_trunc(fast_exp2(pa[ft][8 * kb2 + 2 * w] - amax),
+                         fast_exp2(pa[ft][8 * kb2 + 2 * w + 1] - amax), h_, l_);
+        ahi[ft][kb2][w] = h_;
+        alo[ft][kb2][w] = l_;
+      }
+
+  // P^T[key, query] for key tiles kt <= qt; beta_j per key (lane = key)
+  f32x16 pt[2] = {};
+  float bj[2] = {-kFInf, -kFInf};
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    if (kt > qt) break;
+    tile_rows(sm.k, 32 * kt + col, half, xB);
+    // per-key shift: the key's largest projection on the first 32 features
+    // (the second tile may exceed it; bf16 and fp32 keep that range)
+    float bm = -kFInf;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+      f32x16 pk = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pk[i] *= kLog2e;
+      if (ft == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, pk[i]);
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+      }
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        u32x4 bhi, blo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t h_, l_;
+          split_bf16_trunc(fast_exp2(pk[8 * kb2 + 2 * w] - bm), fast_exp2(pk[8 * kb2 + 2 * w + 1] - bm),
+                           h_, l_);
+          bhi[w] = h_;
+          blo[w] = l_;
+        }
+        pt[kt] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(ahi[ft][kb2]), pt[kt]);
+        pt[kt] = mfma_bf16(as_bf16x8(blo), as_bf16x8(ahi[ft][kb2]), pt[kt]);
+        pt[kt] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(alo[ft][kb2]), pt[kt]);
+      }
+    }
+    bj[kt] = bm + sm.knorm[32 * kt + col];
+  }
+
+  // B_i: largest beta among the keys query i sees (all of tile 0 when qt = 1,
+  // keys <= i of the diagonal tile): inclusive prefix max over key lanes.
+  float pm = bj[qt];
+#pragma unroll
+  for (int sft = 1; sft < 32; sft <<= 1) pm = fmaxf(pm, __shfl_up(pm, sft, 32));
+  float bvis = pm;
+  if (qt == 1) {
+    float t = bj[0];
+#pragma unroll
+    for (int sft = 1; sft < 32; sft <<= 1) t = fmaxf(t, __shfl_xor(t, sft));
+    bvis = fmaxf(bvis, t);
+  }
+  // beta of the key in each register (lane -> register layout through the
+  // wave's own partial slot, which is written only at the end)
+  float* scr = sm.np[wave];
+  if (half == 0) {
+    scr[col] = bj[0];
+    scr[32 + col] = bj[1];
+  }
+  float rmax = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    if (kt > qt) break;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&scr[32 * kt + 8 * g4 + 4 * half]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g4 + j;
+        const bool vis = kt < qt || drow(i, half) <= col;
+        const float p = vis ? pt[kt][i] * fast_exp2(b4[j] - bvis) : 0.f;
+        pt[kt][i] = p;
+        rmax = fmaxf(rmax, p);
+      }
+    }
+  }
+  rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+  const float ic = rmax > 0.f ? amax + bvis + __log2f(rmax) : -kFInf;
+  const float L = fmaxf(mc, ic);
+  const float Ls = L == -kFInf ? 0.f : L;
+  const float fac = rmax > 0.f ? fast_exp2(amax + bvis - Ls) : 0.f;
+  const float cfac = mc == -kFInf ? 0.f : fast_exp2(mc - Ls);
+
+  // carry term
+  f32x16 nc0 = {}, nc1 = {};
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int kpos = f0 + 32 * ft + 16 * kb2 + 8 * half;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(&sm.ysh[col * YS + kpos]);
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(&sm.ysh[(32 + col) * YS + kpos]);
+      nc0 = mfma_f16(as_f16x8(ua[ft][kb2]), as_f16x8(b0), nc0);
+      nc1 = mfma_f16(as_f16x8(ua[ft][kb2]), as_f16x8(b1), nc1);
+    }
+
+  // chunk term: P (bf16 hi + lo, A operand with lane = query) times V
+  f32x16 np0 = {}, np1 = {};
+  float dsp = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    if (kt > qt) break;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t h_, l_;
+        split_bf16_trunc(pt[kt][8 * kb2 + 2 * w] * fac, pt[kt][8 * kb2 + 2 * w + 1] * fac, h_, l_);
+        hi[w] = h_;
+        lo[w] = l_;
+        dsp += (bf16_lo_as_f32(h_) + bf16_lo_as_f32(l_)) + (bf16_hi_as_f32(h_) + bf16_hi_as_f32(l_));
+      }
+      const u32x4 v0 = v_operand(sm.v, 32 * kt + 16 * kb2, 0, lane);
+      const u32x4 v1 = v_operand(sm.v, 32 * kt + 16 * kb2, 1, lane);
+      np0 = mfma_bf16(as_bf16x8(hi), as_bf16x8(v0), np0);
+      np0 = mfma_bf16(as_bf16x8(lo), as_bf16x8(v0), np0);
+      np1 = mfma_bf16(as_bf16x8(hi), as_bf16x8(v1), np1);
+      np1 = mfma_bf16(as_bf16x8(lo), as_bf16x8(v1), np1);
+    }
+  }
+  float dsum = fmaf(cfac, dsc, dsp);
+  dsum += __shfl_xor(dsum, 32);
+
+  if (half == 0) scr[64 + col] = cfac;
+  f32x4 cf4[4];
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) cf4[g4] = *reinterpret_cast<const f32x4*>(&scr[64 + 8 * g4 + 4 * half]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = drow(i, half);
+    const float cf = cf4[i >> 2][i & 3];
+    scr[r * kD + col] = fmaf(nc0[i], sg0 * cf, np0[i]);
+    scr[r * kD + 32 + col] = fmaf(nc1[i], sg1 * cf, np1[i]);
+  }
+  if (half == 0) {
+    sm.dp[wave][col] = dsum;
+    sm.lp[wave][col] = L;
+  }
+}
+
+// Power of two >= x (x >= 0); 1 for x = 0.
+__device__ __forceinline__ float pow2_above(float x) {
+  int ex = 0;
+  if (x > 0.f && x <= 3.0e38f) frexpf(x, &ex);
+  return ldexpf(1.0f, ex);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ W, const float* __restrict__ carry_S,
+    const float* __restrict__ carry_zc, float* __restrict__ out, int H, int n, int nseg,
+    int seglen, int has_carry) {
+  constexpr int M = NW * 32;
+  constexpr int YS = CsSmem<NW>::YS;
+  constexpr int NQ = NW / 2;  // feature groups per query tile
+  __shared__ __attribute__((aligned(16))) CsSmem<NW> sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int bh = blockIdx.x / nseg;
+  const int seg = blockIdx.x - bh * nseg;
+  const int hh = bh % H;
+  const int s0 = seg * seglen;
+  const int ntok = min(n, s0 + seglen) - s0;
+  if (ntok <= 0) return;  // whole workgroup exits together
+  const size_t tok0 = static_cast<size_t>(bh) * n + s0;
+  const uint16_t* Kb = K + tok0 * kD;
+  const uint16_t* Vb = V + tok0 * kD;
+  const uint16_t* Qb = Q + tok0 * kD;
+  float* Ob = out + tok0 * kD;
+
+  for (int c = tid; c < M * 8; c += NW * 64) {
+    const int f = c >> 3, ch = c & 7;
+    *reinterpret_cast<u32x4*>(&sm.w[swz(f, ch)]) =
+        *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD + ch * 8);
+  }
+
+  // Running state of the keys before the current chunk for the wave's 32
+  // features: S (D layout, rows = features, lanes = value columns), z and the
+  // shift c (lane = feature).  sum_j exp(w_f.k_j - |k_j|^2/2) = z_f 2^c_f.
+  const int fk = 32 * wave + col;
+  float c = -kFInf, z = 0.f;
+  f32x16 sacc[2] = {};
+  if (has_carry) {
+    const size_t base = static_cast<size_t>(bh) * nseg + seg;
+    z = carry_zc[base * 2 * M + fk];
+    c = carry_zc[base * 2 * M + M + fk];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        sacc[dt][i] = carry_S[(base * M + 32 * wave + drow(i, half)) * kD + 32 * dt + col];
+  }
+
+  const int nchunks = (ntok + kKT - 1) / kKT;
+  CsRegs<NW> regs;
+  cs_load<NW>(regs, Kb, Vb, Qb, 0, ntok, tid);
+
+  float izr[16];   // 1/z of the feature held in D-layout register i
+  float gam = -kFInf;
+  // state summary: yhat = S / z, its column maxima, gam = c + log2 z
+  auto summarize = [&](int col, int half) {
+    const float iz = z > 0.f ? 1.0f / z : 0.f;
+    gam = z > 0.f ? c + __log2f(z) : -kFInf;
+    if (half == 0) sm.xs[wave][col] = iz;
+    float cm0 = 0.f, cm1 = 0.f;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 z4 = *reinterpret_cast<const f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g4 + j;
+        izr[i] = z4[j];
+        cm0 = fmaxf(cm0, fabsf(sacc[0][i] * izr[i]));
+        cm1 = fmaxf(cm1, fabsf(sacc[1][i] * izr[i]));
+      }
+    }
+    cm0 = fmaxf(cm0, __shfl_xor(cm0, 32));
+    cm1 = fmaxf(cm1, __shfl_xor(cm1, 32));
+    if (half == 0) {
+      sm.colmax[wave][col] = cm0;
+      sm.colmax[wave][32 + col] = cm1;
+    }
+  };
+  // after a barrier: per-column fp16 scale sigma, then yhat' = yhat / sigma and gam to LDS
+  float sg0 = 1.f, sg1 = 1.f;
+  auto publish = [&](int col, int half) {
+    float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      m0 = fmaxf(m0, sm.colmax[w][col]);
+      m1 = fmaxf(m1, sm.colmax[w][32 + col]);
+    }
+    sg0 = pow2_above(m0);
+    sg1 = pow2_above(m1);
+    const float is0 = 1.0f / sg0, is1 = 1.0f / sg1;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int fr = 32 * wave + 8 * g4 + 4 * half;
+      const int pos = (fr & ~15) | kblock_pos(fr & 15);
+      const int i = 4 * g4;
+      const float y0 = izr[i] * is0, y1 = izr[i + 1] * is0, y2 = izr[i + 2] * is0, y3 = izr[i + 3] * is0;
+      *reinterpret_cast<u32x2*>(&sm.ysh[col * YS + pos]) =
+          u32x2{pack_f16(sacc[0][i] * y0, sacc[0][i + 1] * y1), pack_f16(sacc[0][i + 2] * y2, sacc[0][i + 3] * y3)};
+      const float x0 = izr[i] * is1, x1 = izr[i + 1] * is1, x2 = izr[i + 2] * is1, x3 = izr[i + 3] * is1;
+      *reinterpret_cast<u32x2*>(&sm.ysh[(32 + col) * YS + pos]) =
+          u32x2{pack_f16(sacc[1][i] * x0, sacc[1][i + 1] * x1), pack_f16(sacc[1][i + 2] * x2, sacc[1][i + 3] * x3)};
+    }
+    if (half == 0) sm.gam[32 * wave + col] = gam;
+  };
+
+  summarize(col, half);
+  lds_barrier();
+  publish(col, half);
+  cs_stage<NW>(sm, regs, tid, ntok);
+  if (nchunks > 1) cs_load<NW>(regs, Kb, Vb, Qb, kKT, ntok, tid);
+  lds_barrier();
+
+  for (int t = 0; t < nchunks; ++t) {
+    const int t0 = t * kKT;
+    // Lane-dependent LDS addresses are cheap to recompute; keeping them out of
+    // loop-invariant registers leaves room for the accumulators.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int col = ln & 31, half = ln >> 5;
+    const int fk = 32 * wave + col;
+    cs_query_phase<NW>(sm, wave, ln, sg0, sg1);
+
+    // ---- key side: this chunk's keys into the wave's features
+    f32x16 pk[2];
+    {
+      u32x4 wB[4];
+      tile_rows(sm.w, fk, half, wB);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[swz(32 * st + col, 2 * kb + half)])),
+                          as_bf16x8(wB[kb]), acc);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 kn = *reinterpret_cast<const f32x4*>(&sm.knorm[32 * st + 8 * g4 + 4 * half]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[4 * g4 + j] = fmaf(acc[4 * g4 + j], kLog2e, kn[j]);
+        }
+        pk[st] = acc;
+      }
+    }
+    float mx = -kFInf;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, pk[st][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // raise the shift when this chunk's keys exceed it by more than 2^8
+    const bool need = mx > c + 8.0f;
+    if (__ballot(need) != 0) {
+      const float cn = need ? mx : c;
+      const float sc = need ? ((c == -kFInf) ? 0.f : exp2f(c - cn)) : 1.0f;
+      z *= sc;
+      c = cn;
+      if (half == 0) sm.xs[wave][col] = sc;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sacc[0][4 * g4 + j] *= s4[j];
+          sacc[1][4 * g4 + j] *= s4[j];
+        }
+      }
+    }
+    const float cs = c == -kFInf ? 0.f : c;
+    float zc = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pk[st][i] = fast_exp2(pk[st][i] - cs);
+        zc += pk[st][i];
+      }
+    zc += __shfl_xor(zc, 32);
+    z += zc;
+    // S += Phi(K_t)^T V_t (bf16 hi + lo key features)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        u32x4 hi, lo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t h_, l_;
+          split_bf16_trunc(pk[st][8 * kb2 + 2 * w], pk[st][8 * kb2 + 2 * w + 1], h_, l_);
+          hi[w] = h_;
+          lo[w] = l_;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const u32x4 vb = v_operand(sm.v, 32 * st + 16 * kb2, dt, ln);
+          sacc[dt] = mfma_bf16(as_bf16x8(hi), as_bf16x8(vb), sacc[dt]);
+          sacc[dt] = mfma_bf16(as_bf16x8(lo), as_bf16x8(vb), sacc[dt]);
+        }
+      }
+    const bool more = t + 1 < nchunks;
+    if (more) summarize(col, half);
+    lds_barrier();
+
+    if (more) publish(col, half);
+    // ---- combine the partials of the chunk's rows and store
+    for (int it = tid; it < kKT * 8; it += NW * 64) {
+      const int qrow = it >> 3, d0 = (it & 7) * 8;
+      if (t0 + qrow >= ntok) continue;
+      const int qt = qrow >> 5, r = qrow & 31;
+      float lmax = -kFInf;
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) lmax = fmaxf(lmax, sm.lp[qt * NQ + g][r]);
+      float den = 0.f;
+      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) {
+        const int w = qt * NQ + g;
+        const float l = sm.lp[w][r];
+        const float wt = l == -kFInf ? 0.f : exp2f(l - lmax);
+        den = fmaf(wt, sm.dp[w][r], den);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + d0]);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + d0 + 4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          n0[j] = fmaf(wt, a[j], n0[j]);
+          n1[j] = fmaf(wt, b[j], n1[j]);
+        }
+      }
+      const float inv = 1.0f / den;
+      f32x4* dst = reinterpret_cast<f32x4*>(Ob + static_cast<size_t>(t0 + qrow) * kD + d0);
+      __builtin_nontemporal_store(n0 * inv, dst);
+      __builtin_nontemporal_store(n1 * inv, dst + 1);
+    }
+    if (more) {
+      cs_stage<NW>(sm, regs, tid, ntok - t0 - kKT);
+      if (t + 2 < nchunks) cs_load<NW>(regs, Kb, Vb, Qb, t0 + 2 * kKT, ntok, tid);
+    }
+    lds_barrier();
+  }
+}
+
+template <int NW>
+hipError_t launch_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const uint16_t* W, const float* cS, const float* czc,
+                         float* out, hipStream_t s) {
+  FAVOR_LAUNCH("k_causal_output", k_causal_chunks<NW>, dim3(p.B * p.H * p.splits), dim3(NW * 64), 0,
+               s, q, k, v, W, cS, czc, out, p.H, p.n, p.splits, p.span, p.splits > 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_causal_scan(const Bf16Plan& p, const float* part_S, const float* part_zc,
+                              float* carry_S, float* carry_zc, hipStream_t s) {
+  FAVOR_LAUNCH("k_causal_scan", k_causal_scan, dim3(p.B * p.H * 8), dim3(256), 0, s, part_S,
+               part_zc, carry_S, carry_zc, p.m, p.splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const uint16_t* W, const float* carry_S,
+                                const float* carry_zc, float* out, hipStream_t s) {
+  switch (p.m) {
+    case 64: return launch_chunks<2>(p, q, k, v, W, carry_S, carry_zc, out, s);
+    case 128: return launch_chunks<4>(p, q, k, v, W, carry_S, carry_zc, out, s);
+    case 256: return launch_chunks<8>(p, q, k, v, W, carry_S, carry_zc, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace favor

@@ -8,6 +8,19 @@
 
 namespace favor {
 
+// Kernel timing hooks (no-ops unless favor_profile_enable() is active on the
+// calling thread).  name must be a string literal.
+void prof_begin(hipStream_t s, const char* name);
+void prof_end(hipStream_t s);
+
+// Kernel launch bracketed by the timing hooks.
+#define FAVOR_LAUNCH(name, kernel, grid, block, lds, stream, ...)                 \
+  do {                                                                        \
+    ::favor::prof_begin(stream, name);                                        \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);        \
+    ::favor::prof_end(stream);                                                \
+  } while (0)
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -32,13 +45,18 @@ hipError_t launch_attention_causal_f32(const float* q, const float* k, const flo
 struct Bf16Plan {
   int B, H, n, d, m;
   int causal;
-  int splits;     // key-range splits per (b,h) for the state pass
-  int span;       // tokens per split (multiple of 32)
+  int splits;     // key ranges per (b,h): state splits (non-causal) or segments (causal)
+  int span;       // tokens per split / segment (multiple of 64)
   // workspace carve-up (byte offsets)
-  size_t off_part_S, off_part_zc, off_yhat, off_beta, off_sigma, off_carry, off_end;
+  size_t off_part_S, off_part_zc, off_yhat, off_beta, off_sigma, off_carry_S, off_carry_zc, off_end;
 };
 bool bf16_supported(int d, int m);
 Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal);
+hipError_t launch_causal_scan(const Bf16Plan& p, const float* part_S, const float* part_zc,
+                              float* carry_S, float* carry_zc, hipStream_t s);
+hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const uint16_t* W, const float* carry_S,
+                                const float* carry_zc, float* out, hipStream_t s);
 hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                                  const uint16_t* v, const uint16_t* W, float* out, void* ws,
                                  hipStream_t s);

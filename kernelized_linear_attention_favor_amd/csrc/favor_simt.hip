@@ -99,7 +99,7 @@ hipError_t launch_fm(const T* x, const T* W, float* phi, int B, int H, int n, in
     if (e != hipSuccess) return e;
   }
   dim3 grid((n + 31) / 32, (m + 63) / 64, B * H);
-  hipLaunchKernelGGL(k_feature_map<T>, grid, dim3(256), lds, s, x, W, phi, H, n, d, m,
+  FAVOR_LAUNCH("k_feature_map", k_feature_map<T>, grid, dim3(256), lds, s, x, W, phi, H, n, d, m,
                      1.0f / sqrtf(static_cast<float>(m)));
   return hipGetLastError();
 }
@@ -440,15 +440,15 @@ hipError_t launch_attention_f32(const float* q, const float* k, const float* v, 
   const size_t ldsA = sizeof(float) * (static_cast<size_t>(m) * (d + 1) + 2 * kF32Tile * d + kF32Tile);
   hipError_t e = set_lds(reinterpret_cast<const void*>(&k_state_f32), ldsA);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_state_f32, dim3(kF32Splits, BH), dim3(256), ldsA, s, k, v, W, ws, H, n, d,
+  FAVOR_LAUNCH("k_state_f32", k_state_f32, dim3(kF32Splits, BH), dim3(256), ldsA, s, k, v, W, ws, H, n, d,
                      m, span);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_merge_f32, dim3(BH), dim3(256), 0, s, ws, d, m);
+  FAVOR_LAUNCH("k_merge_f32", k_merge_f32, dim3(BH), dim3(256), 0, s, ws, d, m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t ldsC = sizeof(float) * (64 * (d + 1) + 64 * 65 + 64 * d);
   e = set_lds(reinterpret_cast<const void*>(&k_output_f32), ldsC);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_output_f32, dim3((n + 63) / 64, BH), dim3(256), ldsC, s, q, W, ws, out, H,
+  FAVOR_LAUNCH("k_output_f32", k_output_f32, dim3((n + 63) / 64, BH), dim3(256), ldsC, s, q, W, ws, out, H,
                      n, d, m);
   return hipGetLastError();
 }
@@ -459,7 +459,7 @@ hipError_t launch_attention_causal_f32(const float* q, const float* k, const flo
   const size_t lds = sizeof(float) * (static_cast<size_t>(m) * (d + 1) + 2 * m + 4 * d + 1 + 4);
   hipError_t e = set_lds(reinterpret_cast<const void*>(&k_causal_f32), lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_causal_f32, dim3(B * H), dim3(256), lds, s, q, k, v, W, out, H, n, d, m);
+  FAVOR_LAUNCH("k_causal_f32", k_causal_f32, dim3(B * H), dim3(256), lds, s, q, k, v, W, out, H, n, d, m);
   return hipGetLastError();
 }
 
