@@ -132,6 +132,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--noncausal-only", action="store_true", help="time only the non-causal call")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="before timing, run a plain elementwise copy (negation) of MB MiB fp32 three "
+                         "times; its HBM counters calibrate the per-kernel traffic figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -176,6 +179,17 @@ def main() -> int:
         except favor.FavorError as e:
             print(f"[bench] causal path unavailable: {e}", file=sys.stderr)
             causal_ok = False
+
+    if args.copy_probe > 0:
+        nel = args.copy_probe * (1 << 20) // 4
+        src = torch.randn(nel, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {4 * nel} bytes read and {4 * nel} bytes written per launch",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     def step(i):
         t = sets[i % len(sets)]
