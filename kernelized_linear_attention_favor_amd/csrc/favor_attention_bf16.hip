@@ -39,9 +39,9 @@ namespace {
 using namespace bf16k;
 
 // ---------------------------------------------------------------------------
-// k_kv_state: one workgroup = NW waves = 64*NW features (all m features) of
-// one (b, h) over one contiguous key range.  Wave w owns features
-// [64w, 64w+64) as two 32-feature MFMA tiles.
+// k_kv_state: one workgroup = NW = m/32 waves (all m features) of one (b, h)
+// over one contiguous key range.  Wave w owns features [32w, 32w+32), one
+// 32-feature MFMA tile.
 //
 // Per 32-key tile and feature tile:
 //   proj (32x32 MFMA, k = 64 d + 1 aug block) -> D[key, feature] =

@@ -1,0 +1,74 @@
+"""Stored fixture: a tiny exact-binary-fraction FAVOR+ case written by
+tests/golden/make_golden.py from the fp64 oracle.
+
+CPU: the oracle as it stands reproduces the stored values (guards the oracle
+against unnoticed changes).  GPU: the fp32 entry points reproduce them to the
+fp32 bar (1e-5, metric max|y - y_ref| / max|y_ref| per (b, h)); the bf16
+entry points reproduce the bf16-exact inputs' outputs to the bf16 bar for
+the feature map (inputs here are exact in bf16 too; d = 8 is outside the
+bf16 attention path).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "favor_small_f32.json")
+
+
+def load():
+    with open(PATH) as fh:
+        g = json.load(fh)
+    return {k: (np.array(v, dtype=np.float64) if isinstance(v, list) else v) for k, v in g.items()}
+
+
+def test_oracle_reproduces_fixture():
+    g = load()
+    np.testing.assert_allclose(oracle.feature_map(g["q"], g["W"]), g["phi_q"], rtol=1e-13, atol=0)
+    np.testing.assert_allclose(oracle.attention(g["q"], g["k"], g["v"], g["W"]), g["y"],
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.attention_causal(g["q"], g["k"], g["v"], g["W"]),
+                               g["y_causal"], rtol=1e-12, atol=1e-14)
+
+
+def test_fixture_inputs_exact_in_bf16():
+    g = load()
+    for key in ("q", "k", "v", "W"):
+        u = g[key].astype(np.float32).view(np.uint32)
+        assert np.all((u & 0xFFFF) == 0), key
+        assert np.array_equal(g[key].astype(np.float32).astype(np.float64), g[key])
+
+
+def test_fixture_causal_first_row_is_v0():
+    # inclusive causal reading: the first query sees only the first key
+    g = load()
+    np.testing.assert_allclose(g["y_causal"][..., 0, :], g["v"][..., 0, :], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.gpu
+def test_gpu_fp32_matches_fixture():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kernelized_linear_attention_favor_amd as favor
+    g = load()
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(g[k]).to(device=dev, dtype=torch.float32) for k in ("q", "k", "v", "W")}
+    phi = favor.feature_map(t["q"], t["W"])
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"], causal=False)
+    yc = favor.attention(t["q"], t["k"], t["v"], t["W"], causal=True)
+    tb = {k: v.to(torch.bfloat16) for k, v in t.items()}
+    phib = favor.feature_map(tb["q"], tb["W"])
+    torch.cuda.synchronize()
+    ref_phi = g["phi_q"]
+    assert np.max(np.abs(phi.cpu().numpy() - ref_phi) / ref_phi) <= 1e-5
+    assert np.max(np.abs(phib.cpu().numpy() - ref_phi) / ref_phi) <= 1e-5
+    B, H = g["y"].shape[:2]
+    for out, ref in ((y, g["y"]), (yc, g["y_causal"])):
+        o = out.cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                assert oracle.max_rel_err(o[b, h], ref[b, h]) <= 1e-5
