@@ -176,29 +176,48 @@ __device__ __forceinline__ void kv_tile(KvSmem<NW>& sm, int buf, int tile0, int 
   }
 }
 
-// One pass over the key range.  The next tile is loaded into registers while
-// the current one is computed from LDS, then staged into the other buffer.
+// One pass over the key range.  Tiles are loaded into registers two tiles
+// ahead of use (one tile of compute does not cover the load latency), staged
+// into the LDS buffer the next tile reads, and computed from LDS.
+template <int NW, int MODE>
+__device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int ntok,
+                                        KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
+                                        const u32x4 (&wB)[4], const u32x4 augB, float& c,
+                                        float& z, f32x16 (&sacc)[2], bool& cinit, int tid,
+                                        int lane) {
+  // Lane-dependent LDS addresses are recomputed per tile rather than held in
+  // loop-invariant registers.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int lcol = ln & 31, lhalf = ln >> 5;
+  if ((t + 1) * kKT <= ntok)
+    kv_tile<NW, MODE, false>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, lcol, lhalf, ln);
+  else if (t < ntiles)
+    kv_tile<NW, MODE, true>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, lcol, lhalf, ln);
+  // r holds tile t + 1: stage it, then reuse r for tile t + 3.  The load is
+  // issued on every path (past the end it re-reads the clamped last key), so
+  // the wait before the next stage can leave the other tile's load in flight.
+  if (t + 1 < ntiles) stage_kv<NW>(sm, (t + 1) & 1, r, tid);
+  load_kv<NW>(r, Kb, Vb, (t + 3) * kKT, ntok, tid);
+  lds_barrier();
+}
+
 template <int NW, int MODE>
 __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb,
                                          int ntok, const u32x4 (&wB)[4], const u32x4 augB,
                                          float& c, float& z, f32x16 (&sacc)[2], bool& cinit,
-                                         int tid, int lane, int col, int half) {
+                                         int tid, int lane) {
   const int ntiles = (ntok + kKT - 1) / kKT;
-  KvRegs<NW> r;
-  if (ntiles > 0) {
-    load_kv<NW>(r, Kb, Vb, 0, ntok, tid);
-    stage_kv<NW>(sm, 0, r, tid);
-  }
+  if (ntiles == 0) return;
+  KvRegs<NW> ra, rb;   // ra: odd tiles, rb: even tiles (after tile 0)
+  load_kv<NW>(ra, Kb, Vb, 0, ntok, tid);
+  stage_kv<NW>(sm, 0, ra, tid);
+  load_kv<NW>(ra, Kb, Vb, kKT, ntok, tid);
+  load_kv<NW>(rb, Kb, Vb, 2 * kKT, ntok, tid);
   lds_barrier();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_kv<NW>(r, Kb, Vb, (t + 1) * kKT, ntok, tid);
-    if ((t + 1) * kKT <= ntok)
-      kv_tile<NW, MODE, false>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, col, half, lane);
-    else
-      kv_tile<NW, MODE, true>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, col, half, lane);
-    if (more) stage_kv<NW>(sm, (t + 1) & 1, r, tid);
-    lds_barrier();
+  for (int t = 0; t < ntiles; t += 2) {
+    kv_step<NW, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, wB, augB, c, z, sacc, cinit, tid, lane);
+    kv_step<NW, MODE>(sm, t + 1, ntiles, ntok, rb, Kb, Vb, wB, augB, c, z, sacc, cinit, tid, lane);
   }
 }
 
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
   // far above that tile's maximum, phi, z or S overflowed: then a max-only
   // pass finds the exact maximum over the range and the range is accumulated
   // again with it.
-  kv_range<NW, 0>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane, col, half);
+  kv_range<NW, 0>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane);
   bool bad = !(fabsf(z) <= 3.0e38f);
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -254,8 +273,8 @@ __global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
     z = 0.f;
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
-    kv_range<NW, 1>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane, col, half);
-    kv_range<NW, 2>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane, col, half);
+    kv_range<NW, 1>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane);
+    kv_range<NW, 2>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane);
   }
 
   // write this range's partial state
@@ -277,8 +296,9 @@ __global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
 }
 
 // ---------------------------------------------------------------------------
-// k_merge: one workgroup per (b, h, group of 8 value columns); thread f owns
-// feature f.  Splits are combined in index order (deterministic):
+// k_merge: one workgroup per (b, h, group of 16 value columns); thread f owns
+// feature f and reads 64 contiguous bytes of each partial row.  Splits are
+// combined in index order (deterministic):
 //   c_f = max_s c_fs;  z_f = sum_s 2^{c_fs - c_f} z_fs;  S_f likewise;
 //   yhat_f = S_f / z_f;  beta_f = (c_f + log2 z_f) ln 2  (natural-log units).
 // yhat is stored as fp16 after dividing each column by sigma_c, a power of two
@@ -290,78 +310,76 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
                                                uint16_t* __restrict__ yhat,
                                                float* __restrict__ beta,
                                                float* __restrict__ sigma, int m, int splits) {
-  __shared__ float red[8][8];
-  const int bh = blockIdx.x >> 3;
-  const int g = blockIdx.x & 7;
+  __shared__ float red[4][16];
+  const int bh = blockIdx.x >> 2;
+  const int g = blockIdx.x & 3;
   const int f = threadIdx.x;
-  float y[8];
-  float amax[8];
+  float y[16], am[16];
   if (f < m) {
     const float* zc0 = part_zc + static_cast<size_t>(bh) * splits * 2 * m;
     float cm = -kFInf;
-#pragma unroll 4
     for (int s = 0; s < splits; ++s) cm = fmaxf(cm, zc0[static_cast<size_t>(s) * 2 * m + m + f]);
     float zt = 0.f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 8 * g;
+    float acc[16];
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) acc[cc] = 0.f;
+    const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 16 * g;
 #pragma unroll 4
     for (int s = 0; s < splits; ++s) {
       const float cs = zc0[static_cast<size_t>(s) * 2 * m + m + f];
       const float zs = zc0[static_cast<size_t>(s) * 2 * m + f];
       const f32x4* row = reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
-      const f32x4 r0 = row[0], r1 = row[1];
+      f32x4 r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = row[j];
       // an empty range has c = -inf and contributes nothing
       const float a = (cs == -kFInf) ? 0.f : exp2f(cs - cm);
       zt = fmaf(a, zs, zt);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        acc[cc] = fmaf(a, r0[cc], acc[cc]);
-        acc[4 + cc] = fmaf(a, r1[cc], acc[4 + cc]);
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) acc[4 * j + cc] = fmaf(a, r[j][cc], acc[4 * j + cc]);
     }
     const float inv = 1.0f / zt;
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
+    for (int cc = 0; cc < 16; ++cc) {
       y[cc] = acc[cc] * inv;
-      amax[cc] = fabsf(y[cc]);
+      am[cc] = fabsf(y[cc]);
     }
     if (g == 0) beta[static_cast<size_t>(bh) * m + f] = (cm + log2f(zt)) * kLn2;
   } else {
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
+    for (int cc = 0; cc < 16; ++cc) {
       y[cc] = 0.f;
-      amax[cc] = 0.f;
+      am[cc] = 0.f;
     }
   }
   // column maxima over the m features
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc)
-    for (int o = 32; o > 0; o >>= 1) amax[cc] = fmaxf(amax[cc], __shfl_xor(amax[cc], o));
+  for (int cc = 0; cc < 16; ++cc)
+    for (int o = 32; o > 0; o >>= 1) am[cc] = fmaxf(am[cc], __shfl_xor(am[cc], o));
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0)
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) red[wave][cc] = amax[cc];
+    for (int cc = 0; cc < 16; ++cc) red[wave][cc] = am[cc];
   __syncthreads();
-  float sc[8];
+  float sc[16];
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    float mx = fmaxf(fmaxf(red[0][cc], red[1][cc]), fmaxf(red[2][cc], red[3][cc]));
-    // smallest power of two strictly above mx (1 for an all-zero column)
-    int ex = 0;
-    if (mx > 0.f && mx <= 3.0e38f) {
-      frexpf(mx, &ex);  // mx = frac * 2^ex, frac in [0.5, 1)
-    }
+  for (int cc = 0; cc < 16; ++cc) {
+    const float mx = fmaxf(fmaxf(red[0][cc], red[1][cc]), fmaxf(red[2][cc], red[3][cc]));
+    int ex = 0;  // smallest power of two strictly above mx (1 for an all-zero column)
+    if (mx > 0.f && mx <= 3.0e38f) frexpf(mx, &ex);
     sc[cc] = ldexpf(1.0f, ex);
   }
   if (f < m) {
     const int pos = (f & ~15) | kblock_pos(f & 15);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
+    for (int cc = 0; cc < 16; ++cc) {
       const _Float16 hv = static_cast<_Float16>(y[cc] / sc[cc]);
-      yhat[(static_cast<size_t>(bh) * kD + 8 * g + cc) * m + pos] = __builtin_bit_cast(uint16_t, hv);
+      yhat[(static_cast<size_t>(bh) * kD + 16 * g + cc) * m + pos] = __builtin_bit_cast(uint16_t, hv);
     }
   }
-  if (threadIdx.x < 8) sigma[static_cast<size_t>(bh) * kD + 8 * g + threadIdx.x] = sc[threadIdx.x];
+  if (threadIdx.x < 16) sigma[static_cast<size_t>(bh) * kD + 16 * g + threadIdx.x] = sc[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
@@ -593,7 +611,7 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
     }
     return launch_causal_chunks(p, q, k, v, W, cS, czc, out, s);
   }
-  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * 8), dim3(256), 0, s, pS, pzc, yh, beta, sigma,
+  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * 4), dim3(256), 0, s, pS, pzc, yh, beta, sigma,
                p.m, p.splits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // output: about 512 workgroups, each a contiguous run of query tiles

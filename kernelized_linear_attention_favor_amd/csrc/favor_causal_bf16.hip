@@ -35,25 +35,30 @@ using namespace bf16k;
 
 // ---------------------------------------------------------------------------
 // phase 2: carry_in[s] = merge of segment partials 0..s-1, in index order.
-// One workgroup per (b, h, 8 value columns); thread f owns feature f.
+// One workgroup per (b, h, 64 features); thread t owns feature 64 blk + t/4
+// and value columns [16 (t%4), 16 (t%4) + 16), so four adjacent threads read
+// and write one 256-byte state row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_causal_scan(const float* __restrict__ part_S,
                                                      const float* __restrict__ part_zc,
                                                      float* __restrict__ carry_S,
                                                      float* __restrict__ carry_zc, int m,
                                                      int nseg) {
-  const int bh = blockIdx.x >> 3;
-  const int g = blockIdx.x & 7;
-  const int f = threadIdx.x;
-  if (f >= m) return;
+  const int nblk = m >> 6;
+  const int bh = blockIdx.x / nblk;
+  const int f = 64 * (blockIdx.x - bh * nblk) + (threadIdx.x >> 2);
+  const int q = threadIdx.x & 3;
   float c = -kFInf, z = 0.f;
-  float S[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float S[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) S[k] = 0.f;
   for (int s = 0; s < nseg; ++s) {
     const size_t base = static_cast<size_t>(bh) * nseg + s;
-    f32x4* dst = reinterpret_cast<f32x4*>(carry_S + (base * m + f) * kD + 8 * g);
-    dst[0] = f32x4{S[0], S[1], S[2], S[3]};
-    dst[1] = f32x4{S[4], S[5], S[6], S[7]};
-    if (g == 0) {
+    const size_t row = (base * m + f) * kD + 16 * q;
+    f32x4* dst = reinterpret_cast<f32x4*>(carry_S + row);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = f32x4{S[4 * j], S[4 * j + 1], S[4 * j + 2], S[4 * j + 3]};
+    if (q == 0) {
       carry_zc[base * 2 * m + f] = z;
       carry_zc[base * 2 * m + m + f] = c;
     }
@@ -62,8 +67,10 @@ __global__ __launch_bounds__(256) void k_causal_scan(const float* __restrict__ p
     // log2 z into its shift; the running state is renormalised the same way.
     float cp = part_zc[base * 2 * m + m + f];
     const float zp = part_zc[base * 2 * m + f];
-    const f32x4* src = reinterpret_cast<const f32x4*>(part_S + (base * m + f) * kD + 8 * g);
-    const f32x4 r0 = src[0], r1 = src[1];
+    const f32x4* src = reinterpret_cast<const f32x4*>(part_S + row);
+    f32x4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = src[j];
     float bscale = 0.f;
     if (cp != -kFInf && zp > 0.f) {
       bscale = 1.0f / zp;
@@ -76,17 +83,16 @@ __global__ __launch_bounds__(256) void k_causal_scan(const float* __restrict__ p
     const float b = (cp == -kFInf) ? 0.f : exp2f(cp - cn) * bscale;
     z = fmaf(a, z, b * zp);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      S[k] = fmaf(a, S[k], b * r0[k]);
-      S[4 + k] = fmaf(a, S[4 + k], b * r1[k]);
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) S[4 * j + k] = fmaf(a, S[4 * j + k], b * r[j][k]);
     c = cn;
     if (z > 0.f) {
       const float iz = 1.0f / z;
       c += log2f(z);
       z = 1.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) S[k] *= iz;
+      for (int k = 0; k < 16; ++k) S[k] *= iz;
     }
   }
 }
@@ -648,7 +654,7 @@ hipError_t launch_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k
 
 hipError_t launch_causal_scan(const Bf16Plan& p, const float* part_S, const float* part_zc,
                               float* carry_S, float* carry_zc, hipStream_t s) {
-  FAVOR_LAUNCH("k_causal_scan", k_causal_scan, dim3(p.B * p.H * 8), dim3(256), 0, s, part_S,
+  FAVOR_LAUNCH("k_causal_scan", k_causal_scan, dim3(p.B * p.H * (p.m / 64)), dim3(256), 0, s, part_S,
                part_zc, carry_S, carry_zc, p.m, p.splits);
   return hipGetLastError();
 }
