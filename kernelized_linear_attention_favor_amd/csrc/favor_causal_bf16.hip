@@ -112,7 +112,7 @@ struct CsSmem {
   float knorm[kKT];                  // -|k|^2/2 in log2 units; -inf past the segment end
   float gam[M];                      // log2 of the running feature sums z_f (with shift)
   float colmax[NW][kD];              // per wave: max_f |yhat_fd|
-  float np[NW][32 * kD];             // per wave: partial numerators [query][value]
+  float np[NW][32 * kD];             // per wave: partial numerators [query][value, swizzled]
   float dp[NW][32];                  // per wave: partial denominators
   float lp[NW][32];                  // per wave: log2 scale of the partials
   float xs[NW][32];                  // per wave: per-feature scalars, lane -> register layout
@@ -154,9 +154,7 @@ __device__ __forceinline__ void cs_stage(CsSmem<NW>& sm, const CsRegs<NW>& r, in
       s = fmaf(a, a, s);
       s = fmaf(b, b, s);
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
+    s = sum8(s);
     if (ch == 0) sm.knorm[key] = key < nvalid ? -0.5f * kLog2e * s : -kFInf;
   }
 }
@@ -191,12 +189,12 @@ __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 *
 // with a_if = log2e w_f.q_i, b_jf = log2e w_f.k_j, beta_j = bmax_j - log2e |k_j|^2/2,
 // L_i = max(mc_i, alpha_i + B_i + log2 max_j P_ij).  The factor
 // exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
-template <int NW>
+template <int NW, int QT>
 __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float sg0,
                                                float sg1) {
   constexpr int YS = CsSmem<NW>::YS;
+  constexpr int qt = QT;
   const int col = lane & 31, half = lane >> 5;
-  const int qt = wave / (NW / 2);
   const int f0 = 64 * (wave % (NW / 2));
 
   u32x4 xB[4];
@@ -218,8 +216,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         mc = fmaxf(mc, pa[ft][i] + g[j]);
       }
     }
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  mc = fmaxf(mc, __shfl_xor(mc, 32));
+  amax = pair_max(amax);
+  mc = pair_max(mc);
   const float mcs = mc == -kFInf ? 0.f : mc;
 
   // carry weights (fp16, A operand: lane = query, k = feature) and their sum
@@ -272,7 +270,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       if (ft == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) bm = fmaxf(bm, pk[i]);
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = pair_max(bm);
       }
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -295,15 +293,10 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 
   // B_i: largest beta among the keys query i sees (all of tile 0 when qt = 1,
   // keys <= i of the diagonal tile): inclusive prefix max over key lanes.
-  float pm = bj[qt];
-#pragma unroll
-  for (int sft = 1; sft < 32; sft <<= 1) pm = fmaxf(pm, __shfl_up(pm, sft, 32));
-  float bvis = pm;
-  if (qt == 1) {
-    float t = bj[0];
-#pragma unroll
-    for (int sft = 1; sft < 32; sft <<= 1) t = fmaxf(t, __shfl_xor(t, sft));
-    bvis = fmaxf(bvis, t);
+  float bvis = prefix_max32(bj[QT], lane);
+  if (QT == 1) {
+    const float t = prefix_max32(bj[0], lane);
+    bvis = fmaxf(bvis, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 31)));
   }
   // beta of the key in each register (lane -> register layout through the
   // wave's own partial slot, which is written only at the end)
@@ -329,7 +322,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       }
     }
   }
-  rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+  rmax = pair_max(rmax);
   const float ic = rmax > 0.f ? amax + bvis + __log2f(rmax) : -kFInf;
   const float L = fmaxf(mc, ic);
   const float Ls = L == -kFInf ? 0.f : L;
@@ -375,7 +368,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
     }
   }
   float dsum = fmaf(cfac, dsc, dsp);
-  dsum += __shfl_xor(dsum, 32);
+  dsum = pair_sum(dsum);
 
   if (half == 0) scr[64 + col] = cfac;
   f32x4 cf4[4];
@@ -385,8 +378,11 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   for (int i = 0; i < 16; ++i) {
     const int r = drow(i, half);
     const float cf = cf4[i >> 2][i & 3];
-    scr[r * kD + col] = fmaf(nc0[i], sg0 * cf, np0[i]);
-    scr[r * kD + 32 + col] = fmaf(nc1[i], sg1 * cf, np1[i]);
+    // row r's 64 values with their 8-float blocks XOR-swizzled by r & 7, so
+    // that the combine step's reads of 8 rows hit different banks
+    const int sw = (r & 7) << 3;
+    scr[r * kD + (col ^ sw)] = fmaf(nc0[i], sg0 * cf, np0[i]);
+    scr[r * kD + ((32 + col) ^ sw)] = fmaf(nc1[i], sg1 * cf, np1[i]);
   }
   if (half == 0) {
     sm.dp[wave][col] = dsum;
@@ -472,8 +468,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
         cm1 = fmaxf(cm1, fabsf(sacc[1][i] * izr[i]));
       }
     }
-    cm0 = fmaxf(cm0, __shfl_xor(cm0, 32));
-    cm1 = fmaxf(cm1, __shfl_xor(cm1, 32));
+    cm0 = pair_max(cm0);
+    cm1 = pair_max(cm1);
     if (half == 0) {
       sm.colmax[wave][col] = cm0;
       sm.colmax[wave][32 + col] = cm1;
@@ -510,7 +506,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   lds_barrier();
   publish(col, half);
   cs_stage<NW>(sm, regs, tid, ntok);
-  if (nchunks > 1) cs_load<NW>(regs, Kb, Vb, Qb, kKT, ntok, tid);
+  // Prefetch loads are issued on every path (past the end they re-read the
+  // clamped last token), which keeps the compiler's wait before each stage
+  // from also waiting on the output stores issued after the loads.
+  cs_load<NW>(regs, Kb, Vb, Qb, kKT, ntok, tid);
   lds_barrier();
 
   for (int t = 0; t < nchunks; ++t) {
@@ -521,7 +520,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     asm volatile("" : "+v"(ln));
     const int col = ln & 31, half = ln >> 5;
     const int fk = 32 * wave + col;
-    cs_query_phase<NW>(sm, wave, ln, sg0, sg1);
+    if (wave < NW / 2)
+      cs_query_phase<NW, 0>(sm, wave, ln, sg0, sg1);
+    else
+      cs_query_phase<NW, 1>(sm, wave, ln, sg0, sg1);
 
     // ---- key side: this chunk's keys into the wave's features
     f32x16 pk[2];
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, pk[st][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     // raise the shift when this chunk's keys exceed it by more than 2^8
     const bool need = mx > c + 8.0f;
     if (__ballot(need) != 0) {
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
         pk[st][i] = fast_exp2(pk[st][i] - cs);
         zc += pk[st][i];
       }
-    zc += __shfl_xor(zc, 32);
+    zc = pair_sum(zc);
     z += zc;
     // S += Phi(K_t)^T V_t (bf16 hi + lo key features)
 #pragma unroll
@@ -618,10 +620,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
       for (int g = 0; g < NQ; ++g) {
         const int w = qt * NQ + g;
         const float l = sm.lp[w][r];
-        const float wt = l == -kFInf ? 0.f : exp2f(l - lmax);
+        const float wt = l == -kFInf ? 0.f : fast_exp2(l - lmax);
         den = fmaf(wt, sm.dp[w][r], den);
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + d0]);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + d0 + 4]);
+        const int ds = d0 ^ ((r & 7) << 3);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + ds]);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + ds + 4]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           n0[j] = fmaf(wt, a[j], n0[j]);
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     }
     if (more) {
       cs_stage<NW>(sm, regs, tid, ntok - t0 - kKT);
-      if (t + 2 < nchunks) cs_load<NW>(regs, Kb, Vb, Qb, t0 + 2 * kKT, ntok, tid);
+      cs_load<NW>(regs, Kb, Vb, Qb, t0 + 2 * kKT, ntok, tid);
     }
     lds_barrier();
   }

@@ -66,6 +66,43 @@ __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Cross-lane helpers without LDS traffic (VALU permutes).
+// Combine x of lane l with x of lane l ^ 32 (v_permlane32_swap): every lane
+// gets the same result for the pair, computed in the same operand order.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// DPP row shift right by n within each 16-lane row; lanes shifted in get `fill`.
+template <int N>
+__device__ __forceinline__ float dpp_shr(float x, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x110 + N,
+                                                    0xf, 0xf, false));
+}
+// Inclusive prefix maximum over lanes 0..31 and, separately, 32..63.
+__device__ __forceinline__ float prefix_max32(float x, int lane) {
+  const float ninf = -__builtin_huge_valf();
+  x = fmaxf(x, dpp_shr<1>(x, ninf));
+  x = fmaxf(x, dpp_shr<2>(x, ninf));
+  x = fmaxf(x, dpp_shr<4>(x, ninf));
+  x = fmaxf(x, dpp_shr<8>(x, ninf));
+  const float r15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float r47 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  if (lane & 16) x = fmaxf(x, (lane & 32) ? r47 : r15);
+  return x;
+}
+// Sum over each aligned group of 8 lanes (quad swaps, then the half-row mirror).
+__device__ __forceinline__ float sum8(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));  // lane ^ 1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));  // lane ^ 2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)); // 7 - lane
+  return x;
+}
+
 // Position of feature offset f (0..15) inside a 16-wide MFMA k-block when the
 // A operand comes from a 32x32 MFMA output: slots 0-3 of lane half 0 hold
 // features 0-3, slots 4-7 hold 8-11; lane half 1 holds 4-7 and 12-15.
