@@ -113,65 +113,97 @@ __device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<N
   }
 }
 
-// MODE 0: accumulate, first tile fixes c.  MODE 1: max only.  MODE 2: accumulate
-// with fixed c.  PARTIAL: the tile runs past the end of the key range, so the
-// tail keys are masked.  Each wave owns one 32-feature tile.
-template <int NW, int MODE, bool PARTIAL>
+// Per-wave state of one 32-feature tile: W operand (B, lane = feature), the
+// shift c_f, the running z_f and S_f (D layout, rows = features).
+struct KvFeat {
+  u32x4 wB[4];
+  float c, z;
+  f32x16 sacc[2];
+};
+
+// Projection of 32 keys (rows row0 .. row0+31 of a staged tile) on one
+// 32-feature tile: D[key, feature] = w_f.k_j - |k_j|^2/2 (lane = feature column).
+template <int NW>
+__device__ __forceinline__ f32x16 kv_proj(const KvSmem<NW>& sm, int buf, int row0, int col, int half,
+                                          const u32x4 (&wB)[4], const u32x4 augB) {
+  const int row = row0 + col;
+  f32x16 acc = {};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][swz(row, 2 * kb + half)])),
+                    as_bf16x8(wB[kb]), acc);
+  const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.aug[buf][2 * row]);
+  const u32x4 ka4 = half == 0 ? u32x4{a[0], a[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+  return mfma_bf16(as_bf16x8(ka4), as_bf16x8(augB), acc);
+}
+
+// phi = 2^(D log2e - c) for 32 keys, z += phi, S += (phi_hi + phi_lo)^T V.
+template <int NW>
+__device__ __forceinline__ void kv_accumulate(const KvSmem<NW>& sm, int buf, int row0,
+                                              const f32x16& pacc, KvFeat& fs, int lane) {
+  const float nc = -fs.c;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    u32x4 hi, lo;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w], kLog2e, nc));
+      const float p1 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w + 1], kLog2e, nc));
+      fs.z += p0 + p1;
+      uint32_t h_, l_;
+      split_bf16_trunc(p0, p1, h_, l_);
+      hi[w] = h_;
+      lo[w] = l_;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const u32x4 vb = v_operand(sm.v[buf], row0 + 16 * kb2, dt, lane);
+      fs.sacc[dt] = mfma_bf16(as_bf16x8(hi), as_bf16x8(vb), fs.sacc[dt]);
+      fs.sacc[dt] = mfma_bf16(as_bf16x8(lo), as_bf16x8(vb), fs.sacc[dt]);
+    }
+  }
+}
+
+// Largest D log2e over 32 keys (keys at or past ntok excluded) into c.
+__device__ __forceinline__ void kv_max(const f32x16& pacc, int tok_base, int ntok, int half,
+                                       bool partial, float& c) {
+  float mx = -kFInf;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + 4 * half + (i & 3);
+    if (!partial || tok_base + r < ntok) mx = fmaxf(mx, pacc[i]);
+  }
+  mx = pair_max(mx);
+  c = fmaxf(c, mx * kLog2e);
+}
+
+// One 64-key tile for the wave's FT feature tiles.  MAX: only raise c.  ACC:
+// accumulate with c fixed.  PARTIAL: the tile runs past the end of the key
+// range; tail keys are masked.
+enum { kModeMax = 1, kModeAcc = 2 };
+template <int NW, int FT, int MODE, bool PARTIAL>
 __device__ __forceinline__ void kv_tile(KvSmem<NW>& sm, int buf, int tile0, int ntok,
-                                        const u32x4 (&wB)[4], const u32x4 augB, float& c,
-                                        float& z, f32x16 (&sacc)[2], bool& cinit, int col,
-                                        int half, int lane) {
+                                        const u32x4 augB, KvFeat (&fs)[FT], int col, int half,
+                                        int lane) {
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     const int tok_base = tile0 + 32 * st;
     if (PARTIAL && tok_base >= ntok) break;
-    const int row = 32 * st + col;
-    f32x16 pacc = {};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      pacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][swz(row, 2 * kb + half)])),
-                       as_bf16x8(wB[kb]), pacc);
-    {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.aug[buf][2 * row]);
-      const u32x4 ka4 = half == 0 ? u32x4{a[0], a[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
-      pacc = mfma_bf16(as_bf16x8(ka4), as_bf16x8(augB), pacc);
-    }
-    if (PARTIAL) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * half + (i & 3);
-        if (tok_base + r >= ntok) pacc[i] = -kFInf;
+    for (int ft = 0; ft < FT; ++ft) {
+      f32x16 pacc = kv_proj(sm, buf, 32 * st, col, half, fs[ft].wB, augB);
+      if (MODE == kModeMax) {
+        kv_max(pacc, tok_base, ntok, half, PARTIAL, fs[ft].c);
+        continue;
       }
-    }
-    if (MODE == 1 || (MODE == 0 && !cinit)) {
-      float mx = pacc[0];
+      if (PARTIAL) {
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pacc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      c = fmaxf(c, mx * kLog2e);
-      cinit = true;
-    }
-    if (MODE == 1) continue;
-    const float nc = -c;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      u32x4 hi, lo;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float p0 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w], kLog2e, nc));
-        const float p1 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w + 1], kLog2e, nc));
-        z += p0 + p1;
-        uint32_t h_, l_;
-        split_bf16_trunc(p0, p1, h_, l_);
-        hi[w] = h_;
-        lo[w] = l_;
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * half + (i & 3);
+          if (tok_base + r >= ntok) pacc[i] = -kFInf;
+        }
       }
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const u32x4 vb = v_operand(sm.v[buf], 32 * st + 16 * kb2, dt, lane);
-        sacc[dt] = mfma_bf16(as_bf16x8(hi), as_bf16x8(vb), sacc[dt]);
-        sacc[dt] = mfma_bf16(as_bf16x8(lo), as_bf16x8(vb), sacc[dt]);
-      }
+      kv_accumulate(sm, buf, 32 * st, pacc, fs[ft], lane);
     }
   }
 }
@@ -179,21 +211,19 @@ __device__ __forceinline__ void kv_tile(KvSmem<NW>& sm, int buf, int tile0, int 
 // One pass over the key range.  Tiles are loaded into registers two tiles
 // ahead of use (one tile of compute does not cover the load latency), staged
 // into the LDS buffer the next tile reads, and computed from LDS.
-template <int NW, int MODE>
+template <int NW, int FT, int MODE>
 __device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int ntok,
                                         KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
-                                        const u32x4 (&wB)[4], const u32x4 augB, float& c,
-                                        float& z, f32x16 (&sacc)[2], bool& cinit, int tid,
-                                        int lane) {
+                                        const u32x4 augB, KvFeat (&fs)[FT], int tid, int lane) {
   // Lane-dependent LDS addresses are recomputed per tile rather than held in
   // loop-invariant registers.
   int ln = lane;
   asm volatile("" : "+v"(ln));
   const int lcol = ln & 31, lhalf = ln >> 5;
   if ((t + 1) * kKT <= ntok)
-    kv_tile<NW, MODE, false>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, lcol, lhalf, ln);
+    kv_tile<NW, FT, MODE, false>(sm, t & 1, t * kKT, ntok, augB, fs, lcol, lhalf, ln);
   else if (t < ntiles)
-    kv_tile<NW, MODE, true>(sm, t & 1, t * kKT, ntok, wB, augB, c, z, sacc, cinit, lcol, lhalf, ln);
+    kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, augB, fs, lcol, lhalf, ln);
   // r holds tile t + 1: stage it, then reuse r for tile t + 3.  The load is
   // issued on every path (past the end it re-reads the clamped last key), so
   // the wait before the next stage can leave the other tile's load in flight.
@@ -202,11 +232,12 @@ __device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int n
   lds_barrier();
 }
 
-template <int NW, int MODE>
+// FIRST_C: c is first set from tile 0 alone (a max over its keys), then the
+// range is accumulated with c fixed; otherwise MODE applies to every tile.
+template <int NW, int FT, int MODE, bool FIRST_C>
 __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb,
-                                         int ntok, const u32x4 (&wB)[4], const u32x4 augB,
-                                         float& c, float& z, f32x16 (&sacc)[2], bool& cinit,
-                                         int tid, int lane) {
+                                         int ntok, const u32x4 augB, KvFeat (&fs)[FT], int tid,
+                                         int lane) {
   const int ntiles = (ntok + kKT - 1) / kKT;
   if (ntiles == 0) return;
   KvRegs<NW> ra, rb;   // ra: odd tiles, rb: even tiles (after tile 0)
@@ -215,17 +246,27 @@ __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, con
   load_kv<NW>(ra, Kb, Vb, kKT, ntok, tid);
   load_kv<NW>(rb, Kb, Vb, 2 * kKT, ntok, tid);
   lds_barrier();
+  if (FIRST_C) {
+    const int col = lane & 31, half = lane >> 5;
+    if (kKT <= ntok)
+      kv_tile<NW, FT, kModeMax, false>(sm, 0, 0, ntok, augB, fs, col, half, lane);
+    else
+      kv_tile<NW, FT, kModeMax, true>(sm, 0, 0, ntok, augB, fs, col, half, lane);
+  }
   for (int t = 0; t < ntiles; t += 2) {
-    kv_step<NW, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, wB, augB, c, z, sacc, cinit, tid, lane);
-    kv_step<NW, MODE>(sm, t + 1, ntiles, ntok, rb, Kb, Vb, wB, augB, c, z, sacc, cinit, tid, lane);
+    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, augB, fs, tid, lane);
+    kv_step<NW, FT, MODE>(sm, t + 1, ntiles, ntok, rb, Kb, Vb, augB, fs, tid, lane);
   }
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
+// NW waves of FT 32-feature tiles each cover all m = 32 NW FT features.  With
+// FT = 2 a workgroup has half the waves, so two workgroups (independent key
+// ranges, not in barrier lockstep) share each CU.
+template <int NW, int FT>
+__global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void k_kv_state(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
     float* __restrict__ part_S, float* __restrict__ part_zc, int H, int n, int splits, int span) {
-  constexpr int M = NW * 32;
+  constexpr int M = NW * 32 * FT;
   __shared__ __attribute__((aligned(16))) KvSmem<NW> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -237,62 +278,77 @@ __global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
   const int ntok = max(0, min(n, j0 + span) - j0);
   const uint16_t* Kb = K + (static_cast<size_t>(bh) * n + j0) * kD;
   const uint16_t* Vb = V + (static_cast<size_t>(bh) * n + j0) * kD;
-  const int f = 32 * wave + col;   // this lane's feature (B operand column of the projection)
 
-  u32x4 wB[4];
+  KvFeat fs[FT];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    wB[kb] = *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD + 16 * kb +
-                                             8 * half);
-    // Keep W resident: an opaque definition stops the compiler from re-loading
-    // it inside the key loop (whose vmcnt waits would also stall on the prefetch).
-    asm volatile("" : "+v"(wB[kb]));
+  for (int ft = 0; ft < FT; ++ft) {
+    const int f = 32 * (FT * wave + ft) + col;   // B operand column of the projection
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      fs[ft].wB[kb] = *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD +
+                                                      16 * kb + 8 * half);
+      // Keep W resident: an opaque definition stops the compiler from re-loading
+      // it inside the key loop (whose vmcnt waits would also stall on the prefetch).
+      asm volatile("" : "+v"(fs[ft].wB[kb]));
+    }
+    fs[ft].c = -kFInf;
+    fs[ft].z = 0.f;
+    fs[ft].sacc[0] = f32x16{};
+    fs[ft].sacc[1] = f32x16{};
   }
   const u32x4 augB = half == 0 ? u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u}
                                : u32x4{0u, 0u, 0u, 0u};
 
-  float c = -kFInf, z = 0.f;
-  f32x16 sacc[2] = {};
-  bool cinit = false;
   // Pass 0 accumulates with c fixed from the first tile.  If a later key sat
   // far above that tile's maximum, phi, z or S overflowed: then a max-only
   // pass finds the exact maximum over the range and the range is accumulated
   // again with it.
-  kv_range<NW, 0>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane);
-  bool bad = !(fabsf(z) <= 3.0e38f);
+  kv_range<NW, FT, kModeAcc, true>(sm, Kb, Vb, ntok, augB, fs, tid, lane);
+  bool bad = false;
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+  for (int ft = 0; ft < FT; ++ft) {
+    bad |= !(fabsf(fs[ft].z) <= 3.0e38f);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bad |= !(fabsf(sacc[dt][i]) <= 3.0e38f);
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bad |= !(fabsf(fs[ft].sacc[dt][i]) <= 3.0e38f);
+  }
   if (tid == 0) sm.flag = 0;
   __syncthreads();
   if (bad) sm.flag = 1;
   __syncthreads();
   if (sm.flag) {
-    c = -kFInf;
-    z = 0.f;
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
-    kv_range<NW, 1>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane);
-    kv_range<NW, 2>(sm, Kb, Vb, ntok, wB, augB, c, z, sacc, cinit, tid, lane);
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      fs[ft].c = -kFInf;
+      fs[ft].z = 0.f;
+      fs[ft].sacc[0] = f32x16{};
+      fs[ft].sacc[1] = f32x16{};
+    }
+    kv_range<NW, FT, kModeMax, false>(sm, Kb, Vb, ntok, augB, fs, tid, lane);
+    kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, augB, fs, tid, lane);
   }
 
   // write this range's partial state
   const size_t base = static_cast<size_t>(bh) * splits + split;
   float* zc = part_zc + base * 2 * M;
-  const float zt = z + __shfl_xor(z, 32);
-  if (half == 0) {
-    zc[f] = zt;
-    zc[M + f] = c;
-  }
   float* Sb = part_S + base * M * kD;
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int fr = 32 * wave + 8 * (i >> 2) + 4 * half + (i & 3);
-      Sb[static_cast<size_t>(fr) * kD + 32 * dt + col] = sacc[dt][i];
+  for (int ft = 0; ft < FT; ++ft) {
+    const int f0 = 32 * (FT * wave + ft);
+    const float zt = pair_sum(fs[ft].z);
+    if (half == 0) {
+      zc[f0 + col] = zt;
+      zc[M + f0 + col] = fs[ft].c;
     }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int fr = f0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        Sb[static_cast<size_t>(fr) * kD + 32 * dt + col] = fs[ft].sacc[dt][i];
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -457,20 +513,20 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
     // weights sit near 1 with the whole fp16 normal range below them.  A later
     // feature more than 2^15 above it would overflow fp16; that case is
     // detected and the tile is redone with the exact row maximum.
-    f32x16 p0 = out_proj(wsh, 0, col, half, qB, augB);
+    f32x16 pa = out_proj(wsh, 0, col, half, qB, augB);
     if (tb + 128 < t1) load_q(tb + 128, qN);  // next tile's queries, in flight during this one
-    float mx = p0[0];
+    float mx = pa[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, p0[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pa[i]);
+    mx = pair_max(mx);
     float off = -mx * kLog2e;
     f32x16 yacc0 = {}, yacc1 = {}, dacc = {};
     float tmax = -kFInf;
-    out_accumulate(p0, off, 0, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
+    out_accumulate(pa, off, 0, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
 #pragma unroll 1
     for (int ft = 1; ft < MT; ++ft) {
-      const f32x16 pa = out_proj(wsh, ft, col, half, qB, augB);
-      out_accumulate(pa, off, ft, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
+      const f32x16 pn = out_proj(wsh, ft, col, half, qB, augB);
+      out_accumulate(pn, off, ft, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
     }
     if (__ballot(tmax > 15.0f) != 0) {
       // exact row maximum, then redo the tile
@@ -481,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, pa[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair_max(mx);
       off = -mx * kLog2e;
       yacc0 = f32x16{};
       yacc1 = f32x16{};
@@ -517,12 +573,13 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   }
 }
 
-template <int NW>
+template <int NW, int FT>
 hipError_t launch_kv(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W,
                      float* pS, float* pzc, hipStream_t s) {
   // the causal path runs the same kernel over its segments; it is timed under its own name
-  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", k_kv_state<NW>, dim3(p.B * p.H * p.splits),
-               dim3(NW * 64), 0, s, k, v, W, pS, pzc, p.H, p.n, p.splits, p.span);
+  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, FT>),
+               dim3(p.B * p.H * p.splits), dim3(NW * 64), 0, s, k, v, W, pS, pzc, p.H, p.n,
+               p.splits, p.span);
   return hipGetLastError();
 }
 
@@ -537,6 +594,15 @@ hipError_t launch_out(const Bf16Plan& p, const uint16_t* q, const uint16_t* W, c
 }
 
 }  // namespace
+
+// Feature tiles per state wave: the non-causal pass (many key ranges) uses
+// two per wave so that two independent workgroups share a CU; the causal
+// segment pass (one range per CU) keeps one.
+#ifndef FAVOR_KV_FT
+#define FAVOR_KV_FT 1
+#endif
+static int kv_features_per_wave(int m, int causal) { return (!causal && m >= 128) ? FAVOR_KV_FT : 1; }
+static int kv_features_per_wave(const Bf16Plan& p) { return kv_features_per_wave(p.m, p.causal); }
 
 bool bf16_supported(int d, int m) { return d == kD && (m == 64 || m == 128 || m == 256); }
 
@@ -555,8 +621,8 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
     // one chunk-walking workgroup per CU: segments per (b, h)
     splits = (256 + BH - 1) / BH;
   } else {
-    // about 2048 state waves (8 per CU); a workgroup has m/32 waves
-    const long long wgs = 2048 / (m / 32);
+    // about 2048 state waves (8 per CU); a workgroup has m/(32 FT) waves
+    const long long wgs = 2048 / (m / (32 * kv_features_per_wave(m, causal)));
     splits = (wgs + BH - 1) / BH;
   }
   if (splits > max_splits) splits = max_splits;
@@ -595,9 +661,15 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   hipError_t e = hipSuccess;
   if (!p.causal || p.splits > 1) {
     switch (p.m) {
-      case 64: e = launch_kv<2>(p, k, v, W, pS, pzc, s); break;
-      case 128: e = launch_kv<4>(p, k, v, W, pS, pzc, s); break;
-      case 256: e = launch_kv<8>(p, k, v, W, pS, pzc, s); break;
+      case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, s); break;
+      case 128:
+        e = kv_features_per_wave(p) == 2 ? launch_kv<2, 2>(p, k, v, W, pS, pzc, s)
+                                         : launch_kv<4, 1>(p, k, v, W, pS, pzc, s);
+        break;
+      case 256:
+        e = kv_features_per_wave(p) == 2 ? launch_kv<4, 2>(p, k, v, W, pS, pzc, s)
+                                         : launch_kv<8, 1>(p, k, v, W, pS, pzc, s);
+        break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
