@@ -19,8 +19,10 @@
 //
 // Precision plan (worst-case |y - y_ref| / max|y_ref| per (b, h) below 5e-4 on
 // the measured workloads, against a 2e-3 budget):
-//   * key features exp(e - c) are split into bf16 hi + lo (16 significant
-//     bits) for the S = Phi(K)^T V MFMA; V is used exactly as given (bf16).
+//   * key features exp(e - c) are rounded to fp16 (11 significant bits) for
+//     the S = Phi(K)^T V MFMA, with V scaled by a power of two into fp16 range
+//     (exact for bf16 values); z sums the same rounded features, so each
+//     yhat_f = S_f / z_f is an exact weighted average of the values.
 //   * query softmax weights are in (0, 1] and go to fp16; yhat columns are
 //     scaled by a power of two into (-1, 1) and go to fp16; the denominator is
 //     the same fp16 weights times 1.0, so rounding of a weight moves numerator
@@ -39,28 +41,29 @@ namespace {
 using namespace bf16k;
 
 // ---------------------------------------------------------------------------
-// k_kv_state: one workgroup = NW = m/32 waves (all m features) of one (b, h)
-// over one contiguous key range.  Wave w owns features [32w, 32w+32), one
-// 32-feature MFMA tile.
+// k_kv_state: one workgroup = NW waves of FT 32-feature tiles (all m features)
+// of one (b, h) over one contiguous key range.
 //
 // Per 32-key tile and feature tile:
 //   proj (32x32 MFMA, k = 64 d + 1 aug block) -> D[key, feature] =
 //        w_f.k_j - |k_j|^2/2                    (lane = feature column)
-//   phi  = exp2(D log2e - c_f)                   (c_f: per feature, set from the
-//                                                 first tile of the range)
-//   S_f += (phi_hi + phi_lo)^T V                 (output registers reused as the
-//                                                 A operand; V staged transposed)
-//   z_f += phi
-// If any phi overflowed (a later key far above the first tile), the range is
-// recomputed with c_f set by a max-only pass.
+//   phi  = exp2(D log2e - c_f) -> fp16           (c_f: per feature, the first
+//                                                 tile's maximum + 8)
+//   S_f += phi^T (V / sigma_v)                   (fp16 MFMA; output registers
+//                                                 reused as the A operand)
+//   z_f += phi                                   (same rounded values)
+// sigma_v is a power of two above the first tile's largest |v|.  If anything
+// overflowed (a later key or value far above the first tile's), the range is
+// recomputed with c_f and sigma_v from an exact max-only pass.
 // ---------------------------------------------------------------------------
 constexpr int kKBuf = 2;   // staged key/value tiles (double buffering)
 
 template <int NW>
 struct KvSmem {
-  uint16_t k[kKBuf][kKT * kD];
-  uint16_t v[kKBuf][kKT * kD];
+  uint16_t k[kKBuf][kKT * kD];     // keys, bf16
+  uint16_t v[kKBuf][kKT * kD];     // values / sigma_v, fp16
   uint32_t aug[kKBuf][kKT * 2];   // per key: bf16 parts of -|k|^2/2, packed (p0 | p1 << 16, p2)
+  float vred[NW];
   int flag;
 };
 
@@ -85,16 +88,33 @@ __device__ __forceinline__ void load_kv(KvRegs<NW>& r, const uint16_t* Kb, const
   }
 }
 
-// Registers -> swizzled LDS tile, plus -|k|^2/2 of each key as three bf16
-// parts (the 8 threads holding a key's 8 chunks are adjacent lanes).
+// Largest |v| among the 8 bf16 values of a chunk.
+__device__ __forceinline__ float chunk_absmax(const u32x4& c) {
+  float m = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    m = fmaxf(m, fmaxf(fabsf(bf16_lo_as_f32(c[w])), fabsf(bf16_hi_as_f32(c[w]))));
+  return m;
+}
+
+// Registers -> swizzled LDS tile: keys as given (bf16), values times vinv (a
+// power of two) as fp16, plus -|k|^2/2 of each key as three bf16 parts (the 8
+// threads holding a key's 8 chunks are adjacent lanes).  vmx tracks the
+// largest |v| staged.
 template <int NW>
-__device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<NW>& r, int tid) {
+__device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<NW>& r, int tid,
+                                         float vinv, float& vmx) {
 #pragma unroll
   for (int i = 0; i < KvRegs<NW>::R; ++i) {
     const int c = tid + NW * 64 * i;
     const int key = c >> 3, ch = c & 7;
     *reinterpret_cast<u32x4*>(&sm.k[buf][swz(key, ch)]) = r.k[i];
-    *reinterpret_cast<u32x4*>(&sm.v[buf][swz(key, ch)]) = r.v[i];
+    u32x4 vh;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      vh[w] = pack_f16(bf16_lo_as_f32(r.v[i][w]) * vinv, bf16_hi_as_f32(r.v[i][w]) * vinv);
+    *reinterpret_cast<u32x4*>(&sm.v[buf][swz(key, ch)]) = vh;
+    vmx = fmaxf(vmx, chunk_absmax(r.v[i]));
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -102,9 +122,7 @@ __device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<N
       s = fmaf(a, a, s);
       s = fmaf(b, b, s);
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
+    s = sum8(s);
     if (ch == 0) {
       uint32_t w01, w23;
       split3_bf16(-0.5f * s, w01, w23);
@@ -113,12 +131,33 @@ __device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<N
   }
 }
 
+// Workgroup maximum of x (one barrier).  Every thread gets the result.
+template <int NW>
+__device__ __forceinline__ float block_max(KvSmem<NW>& sm, float x, int tid) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  if ((tid & 63) == 0) sm.vred[tid >> 6] = x;
+  __syncthreads();
+  float m = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m = fmaxf(m, sm.vred[w]);
+  return m;
+}
+
+// 1 / (smallest power of two above m); 1 for m = 0.
+__device__ __forceinline__ float inv_pow2_above(float m) {
+  int ex = 0;
+  if (m > 0.f && m <= 3.0e38f) frexpf(m, &ex);
+  return ldexpf(1.0f, -ex);
+}
+
 // Per-wave state of one 32-feature tile: W operand (B, lane = feature), the
 // shift c_f, the running z_f and S_f (D layout, rows = features).
 struct KvFeat {
   u32x4 wB[4];
-  float c, z;
+  float c;
   f32x16 sacc[2];
+  f32x16 zacc;   // z_f in every column of D-layout row f
 };
 
 // Projection of 32 keys (rows row0 .. row0+31 of a staged tile) on one
@@ -137,29 +176,29 @@ __device__ __forceinline__ f32x16 kv_proj(const KvSmem<NW>& sm, int buf, int row
   return mfma_bf16(as_bf16x8(ka4), as_bf16x8(augB), acc);
 }
 
-// phi = 2^(D log2e - c) for 32 keys, z += phi, S += (phi_hi + phi_lo)^T V.
+// phi = 2^(D log2e - c) for 32 keys, rounded to fp16; S += phi^T (V / sigma_v)
+// and z += phi^T 1 on fp16 MFMA from the same rounded values, so every
+// S_f / z_f is an exact average of the staged values with the rounded weights.
 template <int NW>
 __device__ __forceinline__ void kv_accumulate(const KvSmem<NW>& sm, int buf, int row0,
                                               const f32x16& pacc, KvFeat& fs, int lane) {
   const float nc = -fs.c;
+  const uint32_t h1 = 0x3c003c00u;  // fp16 (1.0, 1.0)
+  const u32x4 ones = u32x4{h1, h1, h1, h1};
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
-    u32x4 hi, lo;
+    u32x4 a;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float p0 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w], kLog2e, nc));
       const float p1 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w + 1], kLog2e, nc));
-      fs.z += p0 + p1;
-      uint32_t h_, l_;
-      split_bf16_trunc(p0, p1, h_, l_);
-      hi[w] = h_;
-      lo[w] = l_;
+      a[w] = pack_f16(p0, p1);
     }
+    fs.zacc = mfma_f16(as_f16x8(a), as_f16x8(ones), fs.zacc);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       const u32x4 vb = v_operand(sm.v[buf], row0 + 16 * kb2, dt, lane);
-      fs.sacc[dt] = mfma_bf16(as_bf16x8(hi), as_bf16x8(vb), fs.sacc[dt]);
-      fs.sacc[dt] = mfma_bf16(as_bf16x8(lo), as_bf16x8(vb), fs.sacc[dt]);
+      fs.sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), fs.sacc[dt]);
     }
   }
 }
@@ -214,49 +253,72 @@ __device__ __forceinline__ void kv_tile(KvSmem<NW>& sm, int buf, int tile0, int 
 template <int NW, int FT, int MODE>
 __device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int ntok,
                                         KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
-                                        const u32x4 augB, KvFeat (&fs)[FT], int tid, int lane) {
+                                        const u32x4 augB, KvFeat (&fs)[FT], float vinv, float& vmx,
+                                        int tid, int lane) {
   // Lane-dependent LDS addresses are recomputed per tile rather than held in
   // loop-invariant registers.
   int ln = lane;
   asm volatile("" : "+v"(ln));
   const int lcol = ln & 31, lhalf = ln >> 5;
-  if ((t + 1) * kKT <= ntok)
-    kv_tile<NW, FT, MODE, false>(sm, t & 1, t * kKT, ntok, augB, fs, lcol, lhalf, ln);
-  else if (t < ntiles)
-    kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, augB, fs, lcol, lhalf, ln);
+  kv_tile<NW, FT, MODE, false>(sm, t & 1, t * kKT, ntok, augB, fs, lcol, lhalf, ln);
   // r holds tile t + 1: stage it, then reuse r for tile t + 3.  The load is
   // issued on every path (past the end it re-reads the clamped last key), so
   // the wait before the next stage can leave the other tile's load in flight.
-  if (t + 1 < ntiles) stage_kv<NW>(sm, (t + 1) & 1, r, tid);
+  if (t + 1 < ntiles) stage_kv<NW>(sm, (t + 1) & 1, r, tid, vinv, vmx);
   load_kv<NW>(r, Kb, Vb, (t + 3) * kKT, ntok, tid);
   lds_barrier();
 }
 
-// FIRST_C: c is first set from tile 0 alone (a max over its keys), then the
-// range is accumulated with c fixed; otherwise MODE applies to every tile.
-template <int NW, int FT, int MODE, bool FIRST_C>
+// FIRST: c is first set from tile 0 alone (a max over its keys) and the value
+// scale from tile 0's largest |v|, then the range is accumulated with both
+// fixed; otherwise MODE applies to every tile with the given vinv.  vmx
+// returns the largest |v| of the range (MAX passes).
+template <int NW, int FT, int MODE, bool FIRST>
 __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb,
-                                         int ntok, const u32x4 augB, KvFeat (&fs)[FT], int tid,
-                                         int lane) {
+                                         int ntok, const u32x4 augB, KvFeat (&fs)[FT], float& vinv,
+                                         float& vmx, int tid, int lane) {
   const int ntiles = (ntok + kKT - 1) / kKT;
-  if (ntiles == 0) return;
-  KvRegs<NW> ra, rb;   // ra: odd tiles, rb: even tiles (after tile 0)
+  if (ntiles == 0) return;   // uniform over the workgroup
+  KvRegs<NW> ra, rb;
   load_kv<NW>(ra, Kb, Vb, 0, ntok, tid);
-  stage_kv<NW>(sm, 0, ra, tid);
+  if (FIRST) {
+    // values are staged as fp16 after scaling by 1 / sigma_v, a power of two
+    // above tile 0's largest |v| (a later tile over 2^15 larger overflows
+    // and sends the range to the exact pass)
+    float m0 = 0.f;
+#pragma unroll
+    for (int i = 0; i < KvRegs<NW>::R; ++i) m0 = fmaxf(m0, chunk_absmax(ra.v[i]));
+    vinv = inv_pow2_above(block_max<NW>(sm, m0, tid));
+  }
+  stage_kv<NW>(sm, 0, ra, tid, vinv, vmx);
   load_kv<NW>(ra, Kb, Vb, kKT, ntok, tid);
   load_kv<NW>(rb, Kb, Vb, 2 * kKT, ntok, tid);
   lds_barrier();
-  if (FIRST_C) {
+  if (FIRST) {
     const int col = lane & 31, half = lane >> 5;
     if (kKT <= ntok)
       kv_tile<NW, FT, kModeMax, false>(sm, 0, 0, ntok, augB, fs, col, half, lane);
     else
       kv_tile<NW, FT, kModeMax, true>(sm, 0, 0, ntok, augB, fs, col, half, lane);
+    // 2^8 of headroom: fp16 features of later keys overflow only 2^24 above
+    // tile 0's largest
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) fs[ft].c += 8.0f;
   }
-  for (int t = 0; t < ntiles; t += 2) {
-    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, augB, fs, tid, lane);
-    kv_step<NW, FT, MODE>(sm, t + 1, ntiles, ntok, rb, Kb, Vb, augB, fs, tid, lane);
+  // full tiles in pairs (ra holds the odd tiles, rb the even ones), then at
+  // most one more full tile and the partial last tile
+  const int nfull = ntok / kKT;
+  int t = 0;
+  for (; t + 2 <= nfull; t += 2) {
+    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
+    kv_step<NW, FT, MODE>(sm, t + 1, ntiles, ntok, rb, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
   }
+  if (t < nfull) {
+    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
+    ++t;
+  }
+  if (t < ntiles)
+    kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, augB, fs, lane & 31, lane >> 5, lane);
 }
 
 // NW waves of FT 32-feature tiles each cover all m = 32 NW FT features.  With
@@ -292,7 +354,7 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
       asm volatile("" : "+v"(fs[ft].wB[kb]));
     }
     fs[ft].c = -kFInf;
-    fs[ft].z = 0.f;
+    fs[ft].zacc = f32x16{};
     fs[ft].sacc[0] = f32x16{};
     fs[ft].sacc[1] = f32x16{};
   }
@@ -303,11 +365,13 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
   // far above that tile's maximum, phi, z or S overflowed: then a max-only
   // pass finds the exact maximum over the range and the range is accumulated
   // again with it.
-  kv_range<NW, FT, kModeAcc, true>(sm, Kb, Vb, ntok, augB, fs, tid, lane);
+  float vinv = 1.0f, vmx = 0.f;
+  kv_range<NW, FT, kModeAcc, true>(sm, Kb, Vb, ntok, augB, fs, vinv, vmx, tid, lane);
   bool bad = false;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
-    bad |= !(fabsf(fs[ft].z) <= 3.0e38f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bad |= !(fabsf(fs[ft].zacc[i]) <= 3.0e38f);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -321,32 +385,35 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       fs[ft].c = -kFInf;
-      fs[ft].z = 0.f;
+      fs[ft].zacc = f32x16{};
       fs[ft].sacc[0] = f32x16{};
       fs[ft].sacc[1] = f32x16{};
     }
-    kv_range<NW, FT, kModeMax, false>(sm, Kb, Vb, ntok, augB, fs, tid, lane);
-    kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, augB, fs, tid, lane);
+    vmx = 0.f;
+    kv_range<NW, FT, kModeMax, false>(sm, Kb, Vb, ntok, augB, fs, vinv, vmx, tid, lane);
+    vinv = inv_pow2_above(block_max<NW>(sm, vmx, tid));
+    kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, augB, fs, vinv, vmx, tid, lane);
   }
 
-  // write this range's partial state
+  // write this range's partial state (S back in value units)
+  const float sig = 1.0f / vinv;
   const size_t base = static_cast<size_t>(bh) * splits + split;
   float* zc = part_zc + base * 2 * M;
   float* Sb = part_S + base * M * kD;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
     const int f0 = 32 * (FT * wave + ft);
-    const float zt = pair_sum(fs[ft].z);
-    if (half == 0) {
-      zc[f0 + col] = zt;
-      zc[M + f0 + col] = fs[ft].c;
+    if (half == 0) zc[M + f0 + col] = fs[ft].c;
+    if (col == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zc[f0 + 8 * (i >> 2) + 4 * half + (i & 3)] = fs[ft].zacc[i];
     }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int fr = f0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        Sb[static_cast<size_t>(fr) * kD + 32 * dt + col] = fs[ft].sacc[dt][i];
+        Sb[static_cast<size_t>(fr) * kD + 32 * dt + col] = fs[ft].sacc[dt][i] * sig;
       }
   }
 }
