@@ -327,7 +327,8 @@ __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, con
 template <int NW, int FT>
 __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void k_kv_state(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
-    float* __restrict__ part_S, float* __restrict__ part_zc, int H, int n, int splits, int span) {
+    float* __restrict__ part_S, float* __restrict__ part_zc, float* __restrict__ part_vmax, int H,
+    int n, int splits, int span) {
   constexpr int M = NW * 32 * FT;
   __shared__ __attribute__((aligned(16))) KvSmem<NW> sm;
   const int tid = threadIdx.x;
@@ -395,9 +396,13 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
     kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, augB, fs, vinv, vmx, tid, lane);
   }
 
-  // write this range's partial state (S back in value units)
+  // write this range's partial state (S back in value units) and its largest |v|
   const float sig = 1.0f / vinv;
   const size_t base = static_cast<size_t>(bh) * splits + split;
+  {
+    const float vm = block_max<NW>(sm, vmx, tid);
+    if (tid == 0) part_vmax[base] = vm;
+  }
   float* zc = part_zc + base * 2 * M;
   float* Sb = part_S + base * M * kD;
 #pragma unroll
@@ -642,10 +647,10 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
 
 template <int NW, int FT>
 hipError_t launch_kv(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W,
-                     float* pS, float* pzc, hipStream_t s) {
+                     float* pS, float* pzc, float* pvm, hipStream_t s) {
   // the causal path runs the same kernel over its segments; it is timed under its own name
   FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, FT>),
-               dim3(p.B * p.H * p.splits), dim3(NW * 64), 0, s, k, v, W, pS, pzc, p.H, p.n,
+               dim3(p.B * p.H * p.splits), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, p.H, p.n,
                p.splits, p.span);
   return hipGetLastError();
 }
@@ -702,6 +707,8 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
   o = align_up(o + sizeof(float) * BH * p.splits * m * kD, 256);
   p.off_part_zc = o;
   o = align_up(o + sizeof(float) * BH * p.splits * 2 * m, 256);
+  p.off_vmax = o;
+  o = align_up(o + sizeof(float) * BH * p.splits, 256);
   p.off_yhat = o;
   o = align_up(o + sizeof(uint16_t) * BH * kD * m, 256);
   p.off_beta = o;
@@ -722,20 +729,21 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   char* base = static_cast<char*>(ws);
   float* pS = reinterpret_cast<float*>(base + p.off_part_S);
   float* pzc = reinterpret_cast<float*>(base + p.off_part_zc);
+  float* pvm = reinterpret_cast<float*>(base + p.off_vmax);
   uint16_t* yh = reinterpret_cast<uint16_t*>(base + p.off_yhat);
   float* beta = reinterpret_cast<float*>(base + p.off_beta);
   float* sigma = reinterpret_cast<float*>(base + p.off_sigma);
   hipError_t e = hipSuccess;
   if (!p.causal || p.splits > 1) {
     switch (p.m) {
-      case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, s); break;
+      case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, pvm, s); break;
       case 128:
-        e = kv_features_per_wave(p) == 2 ? launch_kv<2, 2>(p, k, v, W, pS, pzc, s)
-                                         : launch_kv<4, 1>(p, k, v, W, pS, pzc, s);
+        e = kv_features_per_wave(p) == 2 ? launch_kv<2, 2>(p, k, v, W, pS, pzc, pvm, s)
+                                         : launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s);
         break;
       case 256:
-        e = kv_features_per_wave(p) == 2 ? launch_kv<4, 2>(p, k, v, W, pS, pzc, s)
-                                         : launch_kv<8, 1>(p, k, v, W, pS, pzc, s);
+        e = kv_features_per_wave(p) == 2 ? launch_kv<4, 2>(p, k, v, W, pS, pzc, pvm, s)
+                                         : launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s);
         break;
       default: return hipErrorInvalidValue;
     }
@@ -748,7 +756,7 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
       e = launch_causal_scan(p, pS, pzc, cS, czc, s);
       if (e != hipSuccess) return e;
     }
-    return launch_causal_chunks(p, q, k, v, W, cS, czc, out, s);
+    return launch_causal_chunks(p, q, k, v, W, cS, czc, p.splits > 1 ? pvm : nullptr, out, s);
   }
   FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * 4), dim3(256), 0, s, pS, pzc, yh, beta, sigma,
                p.m, p.splits);

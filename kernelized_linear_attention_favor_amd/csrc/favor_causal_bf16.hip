@@ -107,7 +107,7 @@ struct CsSmem {
   uint16_t w[M * kD];                // W rows (swizzled like the token tiles)
   uint16_t ysh[kD * YS];             // yhat_f / sigma_d, [value column][feature slot], fp16
   uint16_t k[kKT * kD];              // chunk tiles, bf16, swizzled
-  uint16_t v[kKT * kD];
+  uint16_t v[kKT * kD];              // values / sigma_v, fp16
   uint16_t q[kKT * kD];
   float knorm[kKT];                  // -|k|^2/2 in log2 units; -inf past the segment end
   float gam[M];                      // log2 of the running feature sums z_f (with shift)
@@ -137,15 +137,21 @@ __device__ __forceinline__ void cs_load(CsRegs<NW>& r, const uint16_t* Kb, const
   }
 }
 
-// Tiles to LDS; per key -|k|^2/2 (log2 units), or -inf for keys past the end.
+// Tiles to LDS (values times vinv as fp16); per key -|k|^2/2 (log2 units), or
+// -inf for keys past the end.
 template <int NW>
-__device__ __forceinline__ void cs_stage(CsSmem<NW>& sm, const CsRegs<NW>& r, int tid, int nvalid) {
+__device__ __forceinline__ void cs_stage(CsSmem<NW>& sm, const CsRegs<NW>& r, int tid, int nvalid,
+                                         float vinv) {
 #pragma unroll
   for (int i = 0; i < CsRegs<NW>::R; ++i) {
     const int c = tid + NW * 64 * i;
     const int key = c >> 3, ch = c & 7;
     *reinterpret_cast<u32x4*>(&sm.k[swz(key, ch)]) = r.k[i];
-    *reinterpret_cast<u32x4*>(&sm.v[swz(key, ch)]) = r.v[i];
+    u32x4 vh;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      vh[w] = pack_f16(bf16_lo_as_f32(r.v[i][w]) * vinv, bf16_hi_as_f32(r.v[i][w]) * vinv);
+    *reinterpret_cast<u32x4*>(&sm.v[swz(key, ch)]) = vh;
     *reinterpret_cast<u32x4*>(&sm.q[swz(key, ch)]) = r.q[i];
     float s = 0.f;
 #pragma unroll
@@ -342,7 +348,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       nc1 = mfma_f16(as_f16x8(ua[ft][kb2]), as_f16x8(b1), nc1);
     }
 
-  // chunk term: P (bf16 hi + lo, A operand with lane = query) times V
+  // chunk term: P (fp16, at most 1, A operand with lane = query) times V / sigma_v;
+  // the denominator sums the same rounded weights
   f32x16 np0 = {}, np1 = {};
   float dsp = 0.f;
 #pragma unroll
@@ -350,21 +357,18 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
     if (kt > qt) break;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      u32x4 hi, lo;
+      u32x4 a;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        uint32_t h_, l_;
-        split_bf16_trunc(pt[kt][8 * kb2 + 2 * w] * fac, pt[kt][8 * kb2 + 2 * w + 1] * fac, h_, l_);
-        hi[w] = h_;
-        lo[w] = l_;
-        dsp += (bf16_lo_as_f32(h_) + bf16_lo_as_f32(l_)) + (bf16_hi_as_f32(h_) + bf16_hi_as_f32(l_));
+        const f16x2 hv = {static_cast<_Float16>(pt[kt][8 * kb2 + 2 * w] * fac),
+                          static_cast<_Float16>(pt[kt][8 * kb2 + 2 * w + 1] * fac)};
+        dsp += static_cast<float>(hv[0]) + static_cast<float>(hv[1]);
+        a[w] = __builtin_bit_cast(uint32_t, hv);
       }
       const u32x4 v0 = v_operand(sm.v, 32 * kt + 16 * kb2, 0, lane);
       const u32x4 v1 = v_operand(sm.v, 32 * kt + 16 * kb2, 1, lane);
-      np0 = mfma_bf16(as_bf16x8(hi), as_bf16x8(v0), np0);
-      np0 = mfma_bf16(as_bf16x8(lo), as_bf16x8(v0), np0);
-      np1 = mfma_bf16(as_bf16x8(hi), as_bf16x8(v1), np1);
-      np1 = mfma_bf16(as_bf16x8(lo), as_bf16x8(v1), np1);
+      np0 = mfma_f16(as_f16x8(a), as_f16x8(v0), np0);
+      np1 = mfma_f16(as_f16x8(a), as_f16x8(v1), np1);
     }
   }
   float dsum = fmaf(cfac, dsc, dsp);
@@ -401,8 +405,8 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ W, const float* __restrict__ carry_S,
-    const float* __restrict__ carry_zc, float* __restrict__ out, int H, int n, int nseg,
-    int seglen, int has_carry) {
+    const float* __restrict__ carry_zc, const float* __restrict__ seg_vmax,
+    float* __restrict__ out, int H, int n, int nseg, int seglen, int has_carry) {
   constexpr int M = NW * 32;
   constexpr int YS = CsSmem<NW>::YS;
   constexpr int NQ = NW / 2;  // feature groups per query tile
@@ -428,6 +432,32 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
         *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD + ch * 8);
   }
 
+  // Values are staged as fp16 after scaling by 1 / sigma_v, a power of two
+  // above the largest |v| of the segment (from the state pass when there is
+  // one, else from a pass over the segment's values).  Every S, yhat and
+  // partial numerator below is in units of sigma_v.
+  float vm;
+  if (has_carry) {
+    vm = seg_vmax[static_cast<size_t>(bh) * nseg + seg];
+  } else {
+    vm = 0.f;
+    for (int cc = tid; cc < ntok * 8; cc += NW * 64) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(cc >> 3) * kD + (cc & 7) * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) vm = fmaxf(vm, fmaxf(fabsf(bf16_lo_as_f32(x[w])), fabsf(bf16_hi_as_f32(x[w]))));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) vm = fmaxf(vm, __shfl_xor(vm, o));
+    if (lane == 0) sm.colmax[wave][0] = vm;
+    __syncthreads();
+    vm = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) vm = fmaxf(vm, sm.colmax[w][0]);
+    __syncthreads();
+  }
+  const float vsig = pow2_above(vm);
+  const float vinv = 1.0f / vsig;
+
   // Running state of the keys before the current chunk for the wave's 32
   // features: S (D layout, rows = features, lanes = value columns), z and the
   // shift c (lane = feature).  sum_j exp(w_f.k_j - |k_j|^2/2) = z_f 2^c_f.
@@ -442,7 +472,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        sacc[dt][i] = carry_S[(base * M + 32 * wave + drow(i, half)) * kD + 32 * dt + col];
+        sacc[dt][i] = carry_S[(base * M + 32 * wave + drow(i, half)) * kD + 32 * dt + col] * vinv;
   }
 
   const int nchunks = (ntok + kKT - 1) / kKT;
@@ -505,7 +535,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   summarize(col, half);
   lds_barrier();
   publish(col, half);
-  cs_stage<NW>(sm, regs, tid, ntok);
+  cs_stage<NW>(sm, regs, tid, ntok, vinv);
   // Prefetch loads are issued on every path (past the end they re-read the
   // clamped last token), which keeps the compiler's wait before each stage
   // from also waiting on the output stores issued after the loads.
@@ -570,37 +600,30 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
         }
       }
     }
+    // S += Phi(K_t)^T V_t / sigma_v with fp16 key features (at most 2^8); z
+    // sums the same rounded features
     const float cs = c == -kFInf ? 0.f : c;
     float zc = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pk[st][i] = fast_exp2(pk[st][i] - cs);
-        zc += pk[st][i];
-      }
-    zc = pair_sum(zc);
-    z += zc;
-    // S += Phi(K_t)^T V_t (bf16 hi + lo key features)
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        u32x4 hi, lo;
+        u32x4 a;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          uint32_t h_, l_;
-          split_bf16_trunc(pk[st][8 * kb2 + 2 * w], pk[st][8 * kb2 + 2 * w + 1], h_, l_);
-          hi[w] = h_;
-          lo[w] = l_;
+          const f16x2 hv = {static_cast<_Float16>(fast_exp2(pk[st][8 * kb2 + 2 * w] - cs)),
+                            static_cast<_Float16>(fast_exp2(pk[st][8 * kb2 + 2 * w + 1] - cs))};
+          zc += static_cast<float>(hv[0]) + static_cast<float>(hv[1]);
+          a[w] = __builtin_bit_cast(uint32_t, hv);
         }
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
           const u32x4 vb = v_operand(sm.v, 32 * st + 16 * kb2, dt, ln);
-          sacc[dt] = mfma_bf16(as_bf16x8(hi), as_bf16x8(vb), sacc[dt]);
-          sacc[dt] = mfma_bf16(as_bf16x8(lo), as_bf16x8(vb), sacc[dt]);
+          sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), sacc[dt]);
         }
       }
+    zc = pair_sum(zc);
+    z += zc;
     const bool more = t + 1 < nchunks;
     if (more) summarize(col, half);
     lds_barrier();
@@ -631,13 +654,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
           n1[j] = fmaf(wt, b[j], n1[j]);
         }
       }
-      const float inv = 1.0f / den;
+      const float inv = vsig / den;
       f32x4* dst = reinterpret_cast<f32x4*>(Ob + static_cast<size_t>(t0 + qrow) * kD + d0);
       __builtin_nontemporal_store(n0 * inv, dst);
       __builtin_nontemporal_store(n1 * inv, dst + 1);
     }
     if (more) {
-      cs_stage<NW>(sm, regs, tid, ntok - t0 - kKT);
+      cs_stage<NW>(sm, regs, tid, ntok - t0 - kKT, vinv);
       cs_load<NW>(regs, Kb, Vb, Qb, t0 + 2 * kKT, ntok, tid);
     }
     lds_barrier();
@@ -647,9 +670,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
 template <int NW>
 hipError_t launch_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const uint16_t* W, const float* cS, const float* czc,
-                         float* out, hipStream_t s) {
+                         const float* vmax, float* out, hipStream_t s) {
   FAVOR_LAUNCH("k_causal_output", k_causal_chunks<NW>, dim3(p.B * p.H * p.splits), dim3(NW * 64), 0,
-               s, q, k, v, W, cS, czc, out, p.H, p.n, p.splits, p.span, p.splits > 1 ? 1 : 0);
+               s, q, k, v, W, cS, czc, vmax, out, p.H, p.n, p.splits, p.span, p.splits > 1 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -664,11 +687,12 @@ hipError_t launch_causal_scan(const Bf16Plan& p, const float* part_S, const floa
 
 hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const uint16_t* W, const float* carry_S,
-                                const float* carry_zc, float* out, hipStream_t s) {
+                                const float* carry_zc, const float* vmax, float* out,
+                                hipStream_t s) {
   switch (p.m) {
-    case 64: return launch_chunks<2>(p, q, k, v, W, carry_S, carry_zc, out, s);
-    case 128: return launch_chunks<4>(p, q, k, v, W, carry_S, carry_zc, out, s);
-    case 256: return launch_chunks<8>(p, q, k, v, W, carry_S, carry_zc, out, s);
+    case 64: return launch_chunks<2>(p, q, k, v, W, carry_S, carry_zc, vmax, out, s);
+    case 128: return launch_chunks<4>(p, q, k, v, W, carry_S, carry_zc, vmax, out, s);
+    case 256: return launch_chunks<8>(p, q, k, v, W, carry_S, carry_zc, vmax, out, s);
   }
   return hipErrorInvalidValue;
 }
