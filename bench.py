@@ -244,7 +244,7 @@ def main() -> int:
     kernels = {k: {"launches": c, "mean_us": round(t / c * 1e3, 2)} for k, (c, t) in prof.items()}
     per_call = {}
     groups = {"noncausal": ("k_kv_state", "k_merge", "k_output"),
-              "causal": ("k_causal_state", "k_causal_scan", "k_causal_output")}
+              "causal": ("k_causal_state", "k_causal_output")}
     for g, names in groups.items():
         us = sum(kernels[k]["mean_us"] for k in names if k in kernels)
         if us > 0:

@@ -715,10 +715,6 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
   o = align_up(o + sizeof(float) * BH * m, 256);
   p.off_sigma = o;
   o = align_up(o + sizeof(float) * BH * kD, 256);
-  p.off_carry_S = o;
-  if (causal) o = align_up(o + sizeof(float) * BH * p.splits * m * kD, 256);
-  p.off_carry_zc = o;
-  if (causal) o = align_up(o + sizeof(float) * BH * p.splits * 2 * m, 256);
   p.off_end = o;
   return p;
 }
@@ -750,13 +746,7 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
     if (e != hipSuccess) return e;
   }
   if (p.causal) {
-    float* cS = reinterpret_cast<float*>(base + p.off_carry_S);
-    float* czc = reinterpret_cast<float*>(base + p.off_carry_zc);
-    if (p.splits > 1) {
-      e = launch_causal_scan(p, pS, pzc, cS, czc, s);
-      if (e != hipSuccess) return e;
-    }
-    return launch_causal_chunks(p, q, k, v, W, cS, czc, p.splits > 1 ? pvm : nullptr, out, s);
+    return launch_causal_chunks(p, q, k, v, W, pS, pzc, p.splits > 1 ? pvm : nullptr, out, s);
   }
   FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * 4), dim3(256), 0, s, pS, pzc, yh, beta, sigma,
                p.m, p.splits);

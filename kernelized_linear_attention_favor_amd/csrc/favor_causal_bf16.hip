@@ -8,9 +8,9 @@
 // segment into chunks of 64 tokens:
 //   phase 1 (k_kv_state, shared with the non-causal path): per-segment state
 //            (S, z, per-feature shift c) of the segment's own keys;
-//   phase 2 (k_causal_scan): exclusive prefix over segments in index order,
-//            giving every segment the state of all keys before it;
-//   phase 3 (k_causal_chunks): walk the segment's chunks in order.  Query i of
+//   phase 2 (k_causal_chunks): each segment's workgroup first merges the
+//            states of all segments before it, in index order, into its carry;
+//            then it walks the segment's chunks in order.  Query i of
 //            chunk t sums two terms,
 //     carry  phi(q_i)^T S and phi(q_i)^T z over the keys before the chunk, as a
 //            softmax over features with weights phi(q_i)_f z_f and values
@@ -32,70 +32,6 @@ namespace favor {
 namespace {
 
 using namespace bf16k;
-
-// ---------------------------------------------------------------------------
-// phase 2: carry_in[s] = merge of segment partials 0..s-1, in index order.
-// One workgroup per (b, h, 64 features); thread t owns feature 64 blk + t/4
-// and value columns [16 (t%4), 16 (t%4) + 16), so four adjacent threads read
-// and write one 256-byte state row.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_causal_scan(const float* __restrict__ part_S,
-                                                     const float* __restrict__ part_zc,
-                                                     float* __restrict__ carry_S,
-                                                     float* __restrict__ carry_zc, int m,
-                                                     int nseg) {
-  const int nblk = m >> 6;
-  const int bh = blockIdx.x / nblk;
-  const int f = 64 * (blockIdx.x - bh * nblk) + (threadIdx.x >> 2);
-  const int q = threadIdx.x & 3;
-  float c = -kFInf, z = 0.f;
-  float S[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) S[k] = 0.f;
-  for (int s = 0; s < nseg; ++s) {
-    const size_t base = static_cast<size_t>(bh) * nseg + s;
-    const size_t row = (base * m + f) * kD + 16 * q;
-    f32x4* dst = reinterpret_cast<f32x4*>(carry_S + row);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = f32x4{S[4 * j], S[4 * j + 1], S[4 * j + 2], S[4 * j + 3]};
-    if (q == 0) {
-      carry_zc[base * 2 * m + f] = z;
-      carry_zc[base * 2 * m + m + f] = c;
-    }
-    // Segment partials may be far from 1 (the state kernel only bounds them
-    // below overflow), so each one is first renormalised to z = 1 by folding
-    // log2 z into its shift; the running state is renormalised the same way.
-    float cp = part_zc[base * 2 * m + m + f];
-    const float zp = part_zc[base * 2 * m + f];
-    const f32x4* src = reinterpret_cast<const f32x4*>(part_S + row);
-    f32x4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = src[j];
-    float bscale = 0.f;
-    if (cp != -kFInf && zp > 0.f) {
-      bscale = 1.0f / zp;
-      cp += log2f(zp);
-    } else {
-      cp = -kFInf;
-    }
-    const float cn = fmaxf(c, cp);
-    const float a = (c == -kFInf) ? 0.f : exp2f(c - cn);
-    const float b = (cp == -kFInf) ? 0.f : exp2f(cp - cn) * bscale;
-    z = fmaf(a, z, b * zp);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) S[4 * j + k] = fmaf(a, S[4 * j + k], b * r[j][k]);
-    c = cn;
-    if (z > 0.f) {
-      const float iz = 1.0f / z;
-      c += log2f(z);
-      z = 1.0f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) S[k] *= iz;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // phase 3
@@ -404,8 +340,8 @@ __device__ __forceinline__ float pow2_above(float x) {
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ W, const float* __restrict__ carry_S,
-    const float* __restrict__ carry_zc, const float* __restrict__ seg_vmax,
+    const uint16_t* __restrict__ W, const float* __restrict__ part_S,
+    const float* __restrict__ part_zc, const float* __restrict__ seg_vmax,
     float* __restrict__ out, int H, int n, int nseg, int seglen, int has_carry) {
   constexpr int M = NW * 32;
   constexpr int YS = CsSmem<NW>::YS;
@@ -464,15 +400,65 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   const int fk = 32 * wave + col;
   float c = -kFInf, z = 0.f;
   f32x16 sacc[2] = {};
-  if (has_carry) {
-    const size_t base = static_cast<size_t>(bh) * nseg + seg;
-    z = carry_zc[base * 2 * M + fk];
-    c = carry_zc[base * 2 * M + M + fk];
+  if (has_carry && seg > 0) {
+    // Carry = ordered merge of the states of segments 0 .. seg-1 (from the
+    // state pass).  Each partial, and the running state, is renormalised to
+    // z = 1 by folding log2 z into its shift.  Two threads per feature, 32
+    // value columns each; the result goes through the (still unused) partial
+    // slots into the key side's register layout.
+    const int f = tid >> 1, hq = tid & 1;
+    float cr = -kFInf, zr = 0.f;
+    f32x4 Sr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Sr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int s2 = 0; s2 < seg; ++s2) {
+      const size_t base = static_cast<size_t>(bh) * nseg + s2;
+      float cp = part_zc[base * 2 * M + M + f];
+      const float zp = part_zc[base * 2 * M + f];
+      const f32x4* src = reinterpret_cast<const f32x4*>(part_S + (base * M + f) * kD + 32 * hq);
+      f32x4 r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = src[j];
+      float bscale = 0.f;
+      if (cp != -kFInf && zp > 0.f) {
+        bscale = 1.0f / zp;
+        cp += log2f(zp);
+      } else {
+        cp = -kFInf;
+      }
+      const float cn = fmaxf(cr, cp);
+      const float a = (cr == -kFInf) ? 0.f : exp2f(cr - cn);
+      const float b = (cp == -kFInf) ? 0.f : exp2f(cp - cn) * bscale;
+      zr = fmaf(a, zr, b * zp);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Sr[j] = a * Sr[j] + b * r[j];
+      cr = cn;
+      if (zr > 0.f) {
+        const float iz = 1.0f / zr;
+        cr += log2f(zr);
+        zr = 1.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Sr[j] *= iz;
+      }
+    }
+    float* cbuf = &sm.np[0][0];
+    float* zcb = &sm.colmax[0][0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4*>(&cbuf[f * kD + 32 * hq + 4 * j]) = Sr[j];
+    if (hq == 0) {
+      zcb[f] = zr;
+      zcb[M + f] = cr;
+    }
+    __syncthreads();
+    z = zcb[fk];
+    c = zcb[M + fk];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        sacc[dt][i] = carry_S[(base * M + 32 * wave + drow(i, half)) * kD + 32 * dt + col] * vinv;
+        sacc[dt][i] = cbuf[(32 * wave + drow(i, half)) * kD + 32 * dt + col] * vinv;
+    __syncthreads();
   }
 
   const int nchunks = (ntok + kKT - 1) / kKT;
@@ -669,30 +655,23 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
 
 template <int NW>
 hipError_t launch_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
-                         const uint16_t* v, const uint16_t* W, const float* cS, const float* czc,
+                         const uint16_t* v, const uint16_t* W, const float* pS, const float* pzc,
                          const float* vmax, float* out, hipStream_t s) {
   FAVOR_LAUNCH("k_causal_output", k_causal_chunks<NW>, dim3(p.B * p.H * p.splits), dim3(NW * 64), 0,
-               s, q, k, v, W, cS, czc, vmax, out, p.H, p.n, p.splits, p.span, p.splits > 1 ? 1 : 0);
+               s, q, k, v, W, pS, pzc, vmax, out, p.H, p.n, p.splits, p.span, p.splits > 1 ? 1 : 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_causal_scan(const Bf16Plan& p, const float* part_S, const float* part_zc,
-                              float* carry_S, float* carry_zc, hipStream_t s) {
-  FAVOR_LAUNCH("k_causal_scan", k_causal_scan, dim3(p.B * p.H * (p.m / 64)), dim3(256), 0, s, part_S,
-               part_zc, carry_S, carry_zc, p.m, p.splits);
-  return hipGetLastError();
-}
-
 hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
-                                const uint16_t* v, const uint16_t* W, const float* carry_S,
-                                const float* carry_zc, const float* vmax, float* out,
+                                const uint16_t* v, const uint16_t* W, const float* part_S,
+                                const float* part_zc, const float* vmax, float* out,
                                 hipStream_t s) {
   switch (p.m) {
-    case 64: return launch_chunks<2>(p, q, k, v, W, carry_S, carry_zc, vmax, out, s);
-    case 128: return launch_chunks<4>(p, q, k, v, W, carry_S, carry_zc, vmax, out, s);
-    case 256: return launch_chunks<8>(p, q, k, v, W, carry_S, carry_zc, vmax, out, s);
+    case 64: return launch_chunks<2>(p, q, k, v, W, part_S, part_zc, vmax, out, s);
+    case 128: return launch_chunks<4>(p, q, k, v, W, part_S, part_zc, vmax, out, s);
+    case 256: return launch_chunks<8>(p, q, k, v, W, part_S, part_zc, vmax, out, s);
   }
   return hipErrorInvalidValue;
 }

@@ -48,16 +48,13 @@ struct Bf16Plan {
   int splits;     // key ranges per (b,h): state splits (non-causal) or segments (causal)
   int span;       // tokens per split / segment (multiple of 64)
   // workspace carve-up (byte offsets)
-  size_t off_part_S, off_part_zc, off_vmax, off_yhat, off_beta, off_sigma, off_carry_S, off_carry_zc,
-      off_end;
+  size_t off_part_S, off_part_zc, off_vmax, off_yhat, off_beta, off_sigma, off_end;
 };
 bool bf16_supported(int d, int m);
 Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal);
-hipError_t launch_causal_scan(const Bf16Plan& p, const float* part_S, const float* part_zc,
-                              float* carry_S, float* carry_zc, hipStream_t s);
 hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
-                                const uint16_t* v, const uint16_t* W, const float* carry_S,
-                                const float* carry_zc, const float* vmax, float* out,
+                                const uint16_t* v, const uint16_t* W, const float* part_S,
+                                const float* part_zc, const float* vmax, float* out,
                                 hipStream_t s);
 hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                                  const uint16_t* v, const uint16_t* W, float* out, void* ws,
