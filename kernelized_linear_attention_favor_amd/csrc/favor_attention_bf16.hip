@@ -1,7 +1,7 @@
 // bf16-input FAVOR+ attention on gfx950 MFMA (non-causal), three kernels:
 //
 //   k_kv_state  : per (key-range split, b, h): Phi(K)^T [V | 1] partial sums.
-//   k_merge     : per (b, h, 8 value columns): combine splits in fixed order,
+//   k_merge     : per (b, h, 16 features): combine splits in fixed order,
 //                 form yhat_f = S_f / z_f and beta_f = log z_f.
 //   k_output    : per query tile: y_i = sum_f softmax_f(w_f.q_i + beta_f) yhat_f.
 //
@@ -23,8 +23,8 @@
 //     the S = Phi(K)^T V MFMA, with V scaled by a power of two into fp16 range
 //     (exact for bf16 values); z sums the same rounded features, so each
 //     yhat_f = S_f / z_f is an exact weighted average of the values.
-//   * query softmax weights are in (0, 1] and go to fp16; yhat columns are
-//     scaled by a power of two into (-1, 1) and go to fp16; the denominator is
+//   * query softmax weights are in (0, 1] and go to fp16; yhat is scaled by
+//     one power of two per (b, h) into (-1, 1) and goes to fp16; the denominator is
 //     the same fp16 weights times 1.0, so rounding of a weight moves numerator
 //     and denominator together.
 //   * projections w.x (+ the -|k|^2/2 or beta term, carried as three bf16
@@ -424,90 +424,67 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
 }
 
 // ---------------------------------------------------------------------------
-// k_merge: one workgroup per (b, h, group of 16 value columns); thread f owns
-// feature f and reads 64 contiguous bytes of each partial row.  Splits are
-// combined in index order (deterministic):
+// k_merge: one workgroup per (b, h, block of 16 features); thread = (feature,
+// group of 4 value columns), so 16 adjacent lanes read one 256-byte partial
+// row.  Splits are combined in index order (deterministic):
 //   c_f = max_s c_fs;  z_f = sum_s 2^{c_fs - c_f} z_fs;  S_f likewise;
 //   yhat_f = S_f / z_f;  beta_f = (c_f + log2 z_f) ln 2  (natural-log units).
-// yhat is stored as fp16 after dividing each column by sigma_c, a power of two
-// above the column's largest |yhat|, transposed to [dv][slot] in the slot
-// order the output kernel's B operand reads.
+// Every yhat_f is a weighted average of the (b, h)'s values, so |yhat_f| stays
+// below sigma, the power of two above the largest |v| of the (b, h) (from the
+// state pass's per-range maxima).  yhat / sigma is stored as fp16, transposed
+// to [dv][slot] in the slot order the output kernel's B operand reads; sigma
+// goes to every column of the output kernel's per-column scale.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
                                                const float* __restrict__ part_zc,
+                                               const float* __restrict__ part_vmax,
                                                uint16_t* __restrict__ yhat,
                                                float* __restrict__ beta,
                                                float* __restrict__ sigma, int m, int splits) {
-  __shared__ float red[4][16];
-  const int bh = blockIdx.x >> 2;
-  const int g = blockIdx.x & 3;
-  const int f = threadIdx.x;
-  float y[16], am[16];
-  if (f < m) {
-    const float* zc0 = part_zc + static_cast<size_t>(bh) * splits * 2 * m;
-    float cm = -kFInf;
-    for (int s = 0; s < splits; ++s) cm = fmaxf(cm, zc0[static_cast<size_t>(s) * 2 * m + m + f]);
-    float zt = 0.f;
-    float acc[16];
+  __shared__ __attribute__((aligned(16))) uint16_t ys[kD][16];
+  const int nfb = m >> 4;
+  const int bh = blockIdx.x / nfb;
+  const int fb = blockIdx.x - bh * nfb;
+  const int t = threadIdx.x;
+  const int f = 16 * fb + (t >> 4), cq = t & 15;
+  float vm = 0.f;
+  for (int s = 0; s < splits; ++s) vm = fmaxf(vm, part_vmax[static_cast<size_t>(bh) * splits + s]);
+  int ex = 0;   // smallest power of two strictly above vm (1 for all-zero values)
+  if (vm > 0.f && vm <= 3.0e38f) frexpf(vm, &ex);
+  const float sg = ldexpf(1.0f, ex);
+
+  const float* zc0 = part_zc + static_cast<size_t>(bh) * splits * 2 * m;
+  float cm = -kFInf;
+  for (int s = 0; s < splits; ++s) cm = fmaxf(cm, zc0[static_cast<size_t>(s) * 2 * m + m + f]);
+  float zt = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 4 * cq;
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) {
+    const float cs = zc0[static_cast<size_t>(s) * 2 * m + m + f];
+    const float zs = zc0[static_cast<size_t>(s) * 2 * m + f];
+    const f32x4 r = *reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
+    // an empty range has c = -inf and contributes nothing
+    const float a = (cs == -kFInf) ? 0.f : exp2f(cs - cm);
+    zt = fmaf(a, zs, zt);
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) acc[cc] = 0.f;
-    const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 16 * g;
-#pragma unroll 4
-    for (int s = 0; s < splits; ++s) {
-      const float cs = zc0[static_cast<size_t>(s) * 2 * m + m + f];
-      const float zs = zc0[static_cast<size_t>(s) * 2 * m + f];
-      const f32x4* row = reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
-      f32x4 r[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = row[j];
-      // an empty range has c = -inf and contributes nothing
-      const float a = (cs == -kFInf) ? 0.f : exp2f(cs - cm);
-      zt = fmaf(a, zs, zt);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) acc[4 * j + cc] = fmaf(a, r[j][cc], acc[4 * j + cc]);
-    }
-    const float inv = 1.0f / zt;
-#pragma unroll
-    for (int cc = 0; cc < 16; ++cc) {
-      y[cc] = acc[cc] * inv;
-      am[cc] = fabsf(y[cc]);
-    }
-    if (g == 0) beta[static_cast<size_t>(bh) * m + f] = (cm + log2f(zt)) * kLn2;
-  } else {
-#pragma unroll
-    for (int cc = 0; cc < 16; ++cc) {
-      y[cc] = 0.f;
-      am[cc] = 0.f;
-    }
+    for (int cc = 0; cc < 4; ++cc) acc[cc] = fmaf(a, r[cc], acc[cc]);
   }
-  // column maxima over the m features
+  const float inv = 1.0f / zt;
+  const int pos = kblock_pos(f & 15);
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc)
-    for (int o = 32; o > 0; o >>= 1) am[cc] = fmaxf(am[cc], __shfl_xor(am[cc], o));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0)
-#pragma unroll
-    for (int cc = 0; cc < 16; ++cc) red[wave][cc] = am[cc];
+  for (int cc = 0; cc < 4; ++cc) {
+    const _Float16 hv = static_cast<_Float16>((acc[cc] * inv) / sg);
+    ys[4 * cq + cc][pos] = __builtin_bit_cast(uint16_t, hv);
+  }
+  if (cq == 0) beta[static_cast<size_t>(bh) * m + f] = (cm + log2f(zt)) * kLn2;
   __syncthreads();
-  float sc[16];
-#pragma unroll
-  for (int cc = 0; cc < 16; ++cc) {
-    const float mx = fmaxf(fmaxf(red[0][cc], red[1][cc]), fmaxf(red[2][cc], red[3][cc]));
-    int ex = 0;  // smallest power of two strictly above mx (1 for an all-zero column)
-    if (mx > 0.f && mx <= 3.0e38f) frexpf(mx, &ex);
-    sc[cc] = ldexpf(1.0f, ex);
+  {
+    const int c = t >> 2, q = t & 3;   // 4 slots of one column per thread
+    *reinterpret_cast<u32x2*>(yhat + (static_cast<size_t>(bh) * kD + c) * m + 16 * fb + 4 * q) =
+        *reinterpret_cast<const u32x2*>(&ys[c][4 * q]);
   }
-  if (f < m) {
-    const int pos = (f & ~15) | kblock_pos(f & 15);
-#pragma unroll
-    for (int cc = 0; cc < 16; ++cc) {
-      const _Float16 hv = static_cast<_Float16>(y[cc] / sc[cc]);
-      yhat[(static_cast<size_t>(bh) * kD + 16 * g + cc) * m + pos] = __builtin_bit_cast(uint16_t, hv);
-    }
-  }
-  if (threadIdx.x < 16) sigma[static_cast<size_t>(bh) * kD + 16 * g + threadIdx.x] = sc[threadIdx.x];
+  if (fb == 0 && t < kD) sigma[static_cast<size_t>(bh) * kD + t] = sg;
 }
 
 // ---------------------------------------------------------------------------
@@ -748,8 +725,8 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   if (p.causal) {
     return launch_causal_chunks(p, q, k, v, W, pS, pzc, p.splits > 1 ? pvm : nullptr, out, s);
   }
-  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * 4), dim3(256), 0, s, pS, pzc, yh, beta, sigma,
-               p.m, p.splits);
+  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * (p.m / 16)), dim3(256), 0, s, pS, pzc, pvm, yh,
+               beta, sigma, p.m, p.splits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // output: about 512 workgroups, each a contiguous run of query tiles
   const long long BH = static_cast<long long>(p.B) * p.H;
