@@ -183,8 +183,7 @@ template <int NW>
 __device__ __forceinline__ void kv_accumulate(const KvSmem<NW>& sm, int buf, int row0,
                                               const f32x16& pacc, KvFeat& fs, int lane) {
   const float nc = -fs.c;
-  const uint32_t h1 = 0x3c003c00u;  // fp16 (1.0, 1.0)
-  const u32x4 ones = u32x4{h1, h1, h1, h1};
+  const u32x4 ones = u32x4{kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     u32x4 a;
@@ -541,8 +540,7 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
 
   const u32x4 augB = half == 0 ? u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u}
                                : u32x4{0u, 0u, 0u, 0u};
-  const uint32_t h1 = 0x3c003c00u;  // fp16 (1.0, 1.0)
-  const u32x4 onesB = u32x4{h1, h1, h1, h1};
+  const u32x4 onesB = u32x4{kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
   const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * kD;
   float* Ob = out + static_cast<size_t>(bh) * n * kD;
 

@@ -12,6 +12,7 @@ namespace bf16k {
 constexpr int kD = 64;          // head dimension supported by the MFMA path
 constexpr int kKT = 64;         // key tokens staged per iteration (two 32-token MFMA tiles)
 constexpr uint32_t kBf16One = 0x3f80u;
+constexpr uint32_t kF16OnePair = 0x3c003c00u;   // fp16 (1.0, 1.0)
 constexpr float kFInf = __builtin_huge_valf();
 
 // Waves per SIMD the state kernel is compiled for (register budget 512 / this).

@@ -132,8 +132,7 @@ __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 *
 // L_i = max(mc_i, alpha_i + B_i + log2 max_j P_ij).  The factor
 // exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
 template <int NW, int QT>
-__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float sg0,
-                                               float sg1) {
+__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float sgy) {
   constexpr int YS = CsSmem<NW>::YS;
   constexpr int qt = QT;
   const int col = lane & 31, half = lane >> 5;
@@ -144,6 +143,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   f32x16 pa[2];
   pa[0] = w_proj(sm.w, f0 + col, half, xB);
   pa[1] = w_proj(sm.w, f0 + 32 + col, half, xB);
+  // maxima of the raw projections, scaled afterwards (rounding is monotone)
   float amax = -kFInf, mc = -kFInf;
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
@@ -153,12 +153,11 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * g4 + j;
-        pa[ft][i] *= kLog2e;
         amax = fmaxf(amax, pa[ft][i]);
-        mc = fmaxf(mc, pa[ft][i] + g[j]);
+        mc = fmaxf(mc, fmaf(pa[ft][i], kLog2e, g[j]));
       }
     }
-  amax = pair_max(amax);
+  amax = pair_max(amax) * kLog2e;
   mc = pair_max(mc);
   const float mcs = mc == -kFInf ? 0.f : mc;
 
@@ -173,8 +172,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
         const int i = 4 * g4 + j;
-        const f16x2 hv = {static_cast<_Float16>(fast_exp2(pa[ft][i] + g[j] - mcs)),
-                          static_cast<_Float16>(fast_exp2(pa[ft][i + 1] + g[j + 1] - mcs))};
+        const f16x2 hv = {static_cast<_Float16>(fast_exp2(fmaf(pa[ft][i], kLog2e, g[j]) - mcs)),
+                          static_cast<_Float16>(fast_exp2(fmaf(pa[ft][i + 1], kLog2e, g[j + 1]) - mcs))};
         dsc += static_cast<float>(hv[0]) + static_cast<float>(hv[1]);
         ua[ft][g4 >> 1][2 * (g4 & 1) + (j >> 1)] = __builtin_bit_cast(uint32_t, hv);
       }
@@ -188,8 +187,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t h_, l_;
-        split_bf16_trunc(fast_exp2(pa[ft][8 * kb2 + 2 * w] - amax),
-                         fast_exp2(pa[ft][8 * kb2 + 2 * w + 1] - amax), h_, l_);
+        split_bf16_trunc(fast_exp2(fmaf(pa[ft][8 * kb2 + 2 * w], kLog2e, -amax)),
+                         fast_exp2(fmaf(pa[ft][8 * kb2 + 2 * w + 1], kLog2e, -amax)), h_, l_);
         ahi[ft][kb2][w] = h_;
         alo[ft][kb2][w] = l_;
       }
@@ -206,13 +205,11 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
     float bm = -kFInf;
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft) {
-      f32x16 pk = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pk[i] *= kLog2e;
+      const f32x16 pk = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
       if (ft == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) bm = fmaxf(bm, pk[i]);
-        bm = pair_max(bm);
+        bm = pair_max(bm) * kLog2e;
       }
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -220,8 +217,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t h_, l_;
-          split_bf16_trunc(fast_exp2(pk[8 * kb2 + 2 * w] - bm), fast_exp2(pk[8 * kb2 + 2 * w + 1] - bm),
-                           h_, l_);
+          split_bf16_trunc(fast_exp2(fmaf(pk[8 * kb2 + 2 * w], kLog2e, -bm)),
+                           fast_exp2(fmaf(pk[8 * kb2 + 2 * w + 1], kLog2e, -bm)), h_, l_);
           bhi[w] = h_;
           blo[w] = l_;
         }
@@ -317,12 +314,12 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = drow(i, half);
-    const float cf = cf4[i >> 2][i & 3];
+    const float cf = cf4[i >> 2][i & 3] * sgy;
     // row r's 64 values with their 8-float blocks XOR-swizzled by r & 7, so
     // that the combine step's reads of 8 rows hit different banks
     const int sw = (r & 7) << 3;
-    scr[r * kD + (col ^ sw)] = fmaf(nc0[i], sg0 * cf, np0[i]);
-    scr[r * kD + ((32 + col) ^ sw)] = fmaf(nc1[i], sg1 * cf, np1[i]);
+    scr[r * kD + (col ^ sw)] = fmaf(nc0[i], cf, np0[i]);
+    scr[r * kD + ((32 + col) ^ sw)] = fmaf(nc1[i], cf, np1[i]);
   }
   if (half == 0) {
     sm.dp[wave][col] = dsum;
@@ -371,10 +368,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   // Values are staged as fp16 after scaling by 1 / sigma_v, a power of two
   // above the largest |v| of the segment (from the state pass when there is
   // one, else from a pass over the segment's values).  Every S, yhat and
-  // partial numerator below is in units of sigma_v.
-  float vm;
+  // partial numerator below is in units of sigma_v.  yhat, a weighted average
+  // of the values up to the current chunk, is published as fp16 divided by
+  // sgy, a power of two above the largest |v| of this and earlier segments.
+  float vm, vmp;
   if (has_carry) {
     vm = seg_vmax[static_cast<size_t>(bh) * nseg + seg];
+    vmp = vm;
+    for (int s2 = 0; s2 < seg; ++s2) vmp = fmaxf(vmp, seg_vmax[static_cast<size_t>(bh) * nseg + s2]);
   } else {
     vm = 0.f;
     for (int cc = tid; cc < ntok * 8; cc += NW * 64) {
@@ -389,10 +390,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     vm = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) vm = fmaxf(vm, sm.colmax[w][0]);
+    vmp = vm;
     __syncthreads();
   }
   const float vsig = pow2_above(vm);
   const float vinv = 1.0f / vsig;
+  const float sgy = pow2_above(vmp * vinv);   // exact: vinv is a power of two
+  const float isgy = 1.0f / sgy;
 
   // Running state of the keys before the current chunk for the wave's 32
   // features: S (D layout, rows = features, lanes = value columns), z and the
@@ -465,55 +469,35 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   CsRegs<NW> regs;
   cs_load<NW>(regs, Kb, Vb, Qb, 0, ntok, tid);
 
-  float izr[16];   // 1/z of the feature held in D-layout register i
+  float izr[16];   // 1/(z sgy) of the feature held in D-layout register i
   float gam = -kFInf;
-  // state summary: yhat = S / z, its column maxima, gam = c + log2 z
+  // state summary: 1/z in the D layout (through the wave's scalar slots) and
+  // gam = c + log2 z; z >= 1 whenever it is nonzero (the shift keeps the
+  // largest key feature at 1 or above), so the hardware reciprocal is safe
   auto summarize = [&](int col, int half) {
-    const float iz = z > 0.f ? 1.0f / z : 0.f;
+    const float iz = z > 0.f ? fast_rcp(z) * isgy : 0.f;
     gam = z > 0.f ? c + __log2f(z) : -kFInf;
     if (half == 0) sm.xs[wave][col] = iz;
-    float cm0 = 0.f, cm1 = 0.f;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 z4 = *reinterpret_cast<const f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g4 + j;
-        izr[i] = z4[j];
-        cm0 = fmaxf(cm0, fabsf(sacc[0][i] * izr[i]));
-        cm1 = fmaxf(cm1, fabsf(sacc[1][i] * izr[i]));
-      }
-    }
-    cm0 = pair_max(cm0);
-    cm1 = pair_max(cm1);
-    if (half == 0) {
-      sm.colmax[wave][col] = cm0;
-      sm.colmax[wave][32 + col] = cm1;
+      for (int j = 0; j < 4; ++j) izr[4 * g4 + j] = z4[j];
     }
   };
-  // after a barrier: per-column fp16 scale sigma, then yhat' = yhat / sigma and gam to LDS
-  float sg0 = 1.f, sg1 = 1.f;
+  // after a barrier (the previous chunk's readers are done): yhat / sgy and gam to LDS
   auto publish = [&](int col, int half) {
-    float m0 = 0.f, m1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      m0 = fmaxf(m0, sm.colmax[w][col]);
-      m1 = fmaxf(m1, sm.colmax[w][32 + col]);
-    }
-    sg0 = pow2_above(m0);
-    sg1 = pow2_above(m1);
-    const float is0 = 1.0f / sg0, is1 = 1.0f / sg1;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int fr = 32 * wave + 8 * g4 + 4 * half;
       const int pos = (fr & ~15) | kblock_pos(fr & 15);
       const int i = 4 * g4;
-      const float y0 = izr[i] * is0, y1 = izr[i + 1] * is0, y2 = izr[i + 2] * is0, y3 = izr[i + 3] * is0;
       *reinterpret_cast<u32x2*>(&sm.ysh[col * YS + pos]) =
-          u32x2{pack_f16(sacc[0][i] * y0, sacc[0][i + 1] * y1), pack_f16(sacc[0][i + 2] * y2, sacc[0][i + 3] * y3)};
-      const float x0 = izr[i] * is1, x1 = izr[i + 1] * is1, x2 = izr[i + 2] * is1, x3 = izr[i + 3] * is1;
+          u32x2{pack_f16(sacc[0][i] * izr[i], sacc[0][i + 1] * izr[i + 1]),
+                pack_f16(sacc[0][i + 2] * izr[i + 2], sacc[0][i + 3] * izr[i + 3])};
       *reinterpret_cast<u32x2*>(&sm.ysh[(32 + col) * YS + pos]) =
-          u32x2{pack_f16(sacc[1][i] * x0, sacc[1][i + 1] * x1), pack_f16(sacc[1][i + 2] * x2, sacc[1][i + 3] * x3)};
+          u32x2{pack_f16(sacc[1][i] * izr[i], sacc[1][i + 1] * izr[i + 1]),
+                pack_f16(sacc[1][i + 2] * izr[i + 2], sacc[1][i + 3] * izr[i + 3])};
     }
     if (half == 0) sm.gam[32 * wave + col] = gam;
   };
@@ -537,9 +521,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const int col = ln & 31, half = ln >> 5;
     const int fk = 32 * wave + col;
     if (wave < NW / 2)
-      cs_query_phase<NW, 0>(sm, wave, ln, sg0, sg1);
+      cs_query_phase<NW, 0>(sm, wave, ln, sgy);
     else
-      cs_query_phase<NW, 1>(sm, wave, ln, sg0, sg1);
+      cs_query_phase<NW, 1>(sm, wave, ln, sgy);
 
     // ---- key side: this chunk's keys into the wave's features
     f32x16 pk[2];
@@ -587,29 +571,34 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
       }
     }
     // S += Phi(K_t)^T V_t / sigma_v with fp16 key features (at most 2^8); z
-    // sums the same rounded features
+    // sums the same rounded features on the same MFMA (times a ones operand)
     const float cs = c == -kFInf ? 0.f : c;
-    float zc = 0.f;
+    f32x16 zacc = {};
+    const u32x4 ones = {kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         u32x4 a;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f16x2 hv = {static_cast<_Float16>(fast_exp2(pk[st][8 * kb2 + 2 * w] - cs)),
-                            static_cast<_Float16>(fast_exp2(pk[st][8 * kb2 + 2 * w + 1] - cs))};
-          zc += static_cast<float>(hv[0]) + static_cast<float>(hv[1]);
-          a[w] = __builtin_bit_cast(uint32_t, hv);
-        }
+        for (int w = 0; w < 4; ++w)
+          a[w] = pack_f16(fast_exp2(pk[st][8 * kb2 + 2 * w] - cs), fast_exp2(pk[st][8 * kb2 + 2 * w + 1] - cs));
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
           const u32x4 vb = v_operand(sm.v, 32 * st + 16 * kb2, dt, ln);
           sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), sacc[dt]);
         }
+        zacc = mfma_f16(as_f16x8(a), as_f16x8(ones), zacc);
       }
-    zc = pair_sum(zc);
-    z += zc;
+    // every column of zacc holds the chunk's z of the feature in that row:
+    // rows to lanes through the wave's scalar slots
+    if (col == 0) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]) =
+            f32x4{zacc[4 * g4], zacc[4 * g4 + 1], zacc[4 * g4 + 2], zacc[4 * g4 + 3]};
+    }
+    z += sm.xs[wave][col];
     const bool more = t + 1 < nchunks;
     if (more) summarize(col, half);
     lds_barrier();
@@ -640,7 +629,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
           n1[j] = fmaf(wt, b[j], n1[j]);
         }
       }
-      const float inv = vsig / den;
+      const float inv = vsig * fast_rcp(den);
       f32x4* dst = reinterpret_cast<f32x4*>(Ob + static_cast<size_t>(t0 + qrow) * kD + d0);
       __builtin_nontemporal_store(n0 * inv, dst);
       __builtin_nontemporal_store(n1 * inv, dst + 1);
