@@ -41,13 +41,13 @@ struct CsSmem {
   static constexpr int M = NW * 32;
   static constexpr int YS = M + 8;   // fp16 per row of the transposed yhat' table (padded)
   uint16_t w[M * kD];                // W rows (swizzled like the token tiles)
-  uint16_t ysh[kD * YS];             // yhat_f / sigma_d, [value column][feature slot], fp16
+  uint16_t ysh[kD * YS];             // yhat_f (units of sigma_v), [value column][feature slot], fp16
   uint16_t k[kKT * kD];              // chunk tiles, bf16, swizzled
   uint16_t v[kKT * kD];              // values / sigma_v, fp16
   uint16_t q[kKT * kD];
   float knorm[kKT];                  // -|k|^2/2 in log2 units; -inf past the segment end
   float gam[M];                      // log2 of the running feature sums z_f (with shift)
-  float colmax[NW][kD];              // per wave: max_f |yhat_fd|
+  float colmax[NW][kD];              // prologue scratch: |v| maxima, carry z and c
   float np[NW][32 * kD];             // per wave: partial numerators [query][value, swizzled]
   float dp[NW][32];                  // per wave: partial denominators
   float lp[NW][32];                  // per wave: log2 scale of the partials
@@ -123,7 +123,7 @@ __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 *
 // Query side of one chunk for the wave's 32 queries (tile qt) and 64 features
 // (group fg): partial numerator, denominator and their log2 scale L_i.
 //   carry:  u_if = 2^(a_if + gam_f - mc_i) (fp16), mc_i = max_f (a_if + gam_f);
-//           sum_f u_if yhat'_f sigma and sum_f u_if, both times 2^(mc_i - L_i)
+//           sum_f u_if yhat_f and sum_f u_if, both times 2^(mc_i - L_i)
 //   chunk:  P_ij = sum_f 2^(a_if - alpha_i) 2^(b_jf - bmax_j)   (bf16 hi/lo, three MFMAs;
 //           bmax_j is the key's largest b_jf over the first 32 of the features)
 //           times 2^(beta_j - B_i), B_i = max of beta over the keys row i sees, and
@@ -132,7 +132,7 @@ __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 *
 // L_i = max(mc_i, alpha_i + B_i + log2 max_j P_ij).  The factor
 // exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
 template <int NW, int QT>
-__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float sgy) {
+__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane) {
   constexpr int YS = CsSmem<NW>::YS;
   constexpr int qt = QT;
   const int col = lane & 31, half = lane >> 5;
@@ -161,9 +161,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   mc = pair_max(mc);
   const float mcs = mc == -kFInf ? 0.f : mc;
 
-  // carry weights (fp16, A operand: lane = query, k = feature) and their sum
+  // carry weights (fp16, A operand: lane = query, k = feature)
   u32x4 ua[2][2];
-  float dsc = 0.f;
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
@@ -172,10 +171,9 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
         const int i = 4 * g4 + j;
-        const f16x2 hv = {static_cast<_Float16>(fast_exp2(fmaf(pa[ft][i], kLog2e, g[j]) - mcs)),
-                          static_cast<_Float16>(fast_exp2(fmaf(pa[ft][i + 1], kLog2e, g[j + 1]) - mcs))};
-        dsc += static_cast<float>(hv[0]) + static_cast<float>(hv[1]);
-        ua[ft][g4 >> 1][2 * (g4 & 1) + (j >> 1)] = __builtin_bit_cast(uint32_t, hv);
+        ua[ft][g4 >> 1][2 * (g4 & 1) + (j >> 1)] =
+            pack_f16(fast_exp2(fmaf(pa[ft][i], kLog2e, g[j]) - mcs),
+                     fast_exp2(fmaf(pa[ft][i + 1], kLog2e, g[j + 1]) - mcs));
       }
     }
   // query features of the chunk term, bf16 hi + lo (B operand: k = feature, n = query)
@@ -268,8 +266,14 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   const float fac = rmax > 0.f ? fast_exp2(amax + bvis - Ls) : 0.f;
   const float cfac = mc == -kFInf ? 0.f : fast_exp2(mc - Ls);
 
-  // carry term
-  f32x16 nc0 = {}, nc1 = {};
+  // Both terms accumulate into one numerator (and one denominator, against a
+  // ones operand) from fp16 weights already at the row's scale L: the carry
+  // weights times cfac (packed fp16; a weight under fp16 range is under 2^-24
+  // of the row's largest and drops out), the chunk weights times fac.  The
+  // denominator sums exactly the rounded weights the numerator uses.
+  f32x16 np0 = {}, np1 = {}, den = {};
+  const u32x4 ones = {kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
+  const f16x2 cf2 = {static_cast<_Float16>(cfac), static_cast<_Float16>(cfac)};
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
@@ -277,14 +281,14 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       const int kpos = f0 + 32 * ft + 16 * kb2 + 8 * half;
       const u32x4 b0 = *reinterpret_cast<const u32x4*>(&sm.ysh[col * YS + kpos]);
       const u32x4 b1 = *reinterpret_cast<const u32x4*>(&sm.ysh[(32 + col) * YS + kpos]);
-      nc0 = mfma_f16(as_f16x8(ua[ft][kb2]), as_f16x8(b0), nc0);
-      nc1 = mfma_f16(as_f16x8(ua[ft][kb2]), as_f16x8(b1), nc1);
+      u32x4 a;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        a[w] = mul_f16x2(ua[ft][kb2][w], cf2);
+      np0 = mfma_f16(as_f16x8(a), as_f16x8(b0), np0);
+      np1 = mfma_f16(as_f16x8(a), as_f16x8(b1), np1);
+      den = mfma_f16(as_f16x8(a), as_f16x8(ones), den);
     }
-
-  // chunk term: P (fp16, at most 1, A operand with lane = query) times V / sigma_v;
-  // the denominator sums the same rounded weights
-  f32x16 np0 = {}, np1 = {};
-  float dsp = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     if (kt > qt) break;
@@ -292,39 +296,33 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       u32x4 a;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f16x2 hv = {static_cast<_Float16>(pt[kt][8 * kb2 + 2 * w] * fac),
-                          static_cast<_Float16>(pt[kt][8 * kb2 + 2 * w + 1] * fac)};
-        dsp += static_cast<float>(hv[0]) + static_cast<float>(hv[1]);
-        a[w] = __builtin_bit_cast(uint32_t, hv);
-      }
+      for (int w = 0; w < 4; ++w)
+        a[w] = pack_f16(pt[kt][8 * kb2 + 2 * w] * fac, pt[kt][8 * kb2 + 2 * w + 1] * fac);
       const u32x4 v0 = v_operand(sm.v, 32 * kt + 16 * kb2, 0, lane);
       const u32x4 v1 = v_operand(sm.v, 32 * kt + 16 * kb2, 1, lane);
       np0 = mfma_f16(as_f16x8(a), as_f16x8(v0), np0);
       np1 = mfma_f16(as_f16x8(a), as_f16x8(v1), np1);
+      den = mfma_f16(as_f16x8(a), as_f16x8(ones), den);
     }
   }
-  float dsum = fmaf(cfac, dsc, dsp);
-  dsum = pair_sum(dsum);
 
-  if (half == 0) scr[64 + col] = cfac;
-  f32x4 cf4[4];
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) cf4[g4] = *reinterpret_cast<const f32x4*>(&scr[64 + 8 * g4 + 4 * half]);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = drow(i, half);
-    const float cf = cf4[i >> 2][i & 3] * sgy;
     // row r's 64 values with their 8-float blocks XOR-swizzled by r & 7, so
     // that the combine step's reads of 8 rows hit different banks
     const int sw = (r & 7) << 3;
-    scr[r * kD + (col ^ sw)] = fmaf(nc0[i], cf, np0[i]);
-    scr[r * kD + ((32 + col) ^ sw)] = fmaf(nc1[i], cf, np1[i]);
+    scr[r * kD + (col ^ sw)] = np0[i];
+    scr[r * kD + ((32 + col) ^ sw)] = np1[i];
   }
-  if (half == 0) {
-    sm.dp[wave][col] = dsum;
-    sm.lp[wave][col] = L;
+  // every column of den holds the row sums (D layout: register i = row drow(i, half))
+  if (col == 0) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4*>(&sm.dp[wave][8 * g4 + 4 * half]) =
+          f32x4{den[4 * g4], den[4 * g4 + 1], den[4 * g4 + 2], den[4 * g4 + 3]};
   }
+  if (half == 0) sm.lp[wave][col] = L;
 }
 
 // Power of two >= x (x >= 0); 1 for x = 0.
@@ -366,16 +364,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   }
 
   // Values are staged as fp16 after scaling by 1 / sigma_v, a power of two
-  // above the largest |v| of the segment (from the state pass when there is
-  // one, else from a pass over the segment's values).  Every S, yhat and
-  // partial numerator below is in units of sigma_v.  yhat, a weighted average
-  // of the values up to the current chunk, is published as fp16 divided by
-  // sgy, a power of two above the largest |v| of this and earlier segments.
-  float vm, vmp;
+  // above the largest |v| of this and the earlier segments (from the state
+  // pass when there is one, else from a pass over the segment's values).
+  // Every S, yhat and partial numerator below is in units of sigma_v; yhat, a
+  // weighted average of values up to the current chunk, stays inside (-1, 1).
+  float vm;
   if (has_carry) {
-    vm = seg_vmax[static_cast<size_t>(bh) * nseg + seg];
-    vmp = vm;
-    for (int s2 = 0; s2 < seg; ++s2) vmp = fmaxf(vmp, seg_vmax[static_cast<size_t>(bh) * nseg + s2]);
+    vm = 0.f;
+    for (int s2 = 0; s2 <= seg; ++s2) vm = fmaxf(vm, seg_vmax[static_cast<size_t>(bh) * nseg + s2]);
   } else {
     vm = 0.f;
     for (int cc = tid; cc < ntok * 8; cc += NW * 64) {
@@ -390,13 +386,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     vm = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) vm = fmaxf(vm, sm.colmax[w][0]);
-    vmp = vm;
     __syncthreads();
   }
   const float vsig = pow2_above(vm);
   const float vinv = 1.0f / vsig;
-  const float sgy = pow2_above(vmp * vinv);   // exact: vinv is a power of two
-  const float isgy = 1.0f / sgy;
 
   // Running state of the keys before the current chunk for the wave's 32
   // features: S (D layout, rows = features, lanes = value columns), z and the
@@ -469,13 +462,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   CsRegs<NW> regs;
   cs_load<NW>(regs, Kb, Vb, Qb, 0, ntok, tid);
 
-  float izr[16];   // 1/(z sgy) of the feature held in D-layout register i
+  float izr[16];   // 1/z of the feature held in D-layout register i
   float gam = -kFInf;
   // state summary: 1/z in the D layout (through the wave's scalar slots) and
   // gam = c + log2 z; z >= 1 whenever it is nonzero (the shift keeps the
   // largest key feature at 1 or above), so the hardware reciprocal is safe
   auto summarize = [&](int col, int half) {
-    const float iz = z > 0.f ? fast_rcp(z) * isgy : 0.f;
+    const float iz = z > 0.f ? fast_rcp(z) : 0.f;
     gam = z > 0.f ? c + __log2f(z) : -kFInf;
     if (half == 0) sm.xs[wave][col] = iz;
 #pragma unroll
@@ -485,7 +478,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
       for (int j = 0; j < 4; ++j) izr[4 * g4 + j] = z4[j];
     }
   };
-  // after a barrier (the previous chunk's readers are done): yhat / sgy and gam to LDS
+  // after a barrier (the previous chunk's readers are done): yhat and gam to LDS
   auto publish = [&](int col, int half) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -521,9 +514,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const int col = ln & 31, half = ln >> 5;
     const int fk = 32 * wave + col;
     if (wave < NW / 2)
-      cs_query_phase<NW, 0>(sm, wave, ln, sgy);
+      cs_query_phase<NW, 0>(sm, wave, ln);
     else
-      cs_query_phase<NW, 1>(sm, wave, ln, sgy);
+      cs_query_phase<NW, 1>(sm, wave, ln);
 
     // ---- key side: this chunk's keys into the wave's features
     f32x16 pk[2];

@@ -64,6 +64,12 @@ __device__ __forceinline__ void split_bf16_trunc(float a, float b, uint32_t& hi,
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
+// Two packed fp16 values times (s.x, s.y), rounded to fp16.  The word comes in
+// by value: bit-casting a vector element in place (v[i]) reads element 0
+// with this compiler.
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t u, f16x2 s) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, u) * s);
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
