@@ -124,12 +124,13 @@ __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 *
 // (group fg): partial numerator, denominator and their log2 scale L_i.
 //   carry:  u_if = 2^(a_if + gam_f - mc_i) (fp16), mc_i = max_f (a_if + gam_f);
 //           sum_f u_if yhat_f and sum_f u_if, both times 2^(mc_i - L_i)
-//   chunk:  P_ij = sum_f 2^(a_if - alpha_i) 2^(b_jf - bmax_j)   (bf16 hi/lo, three MFMAs;
-//           bmax_j is the key's largest b_jf over the first 32 of the features)
-//           times 2^(beta_j - B_i), B_i = max of beta over the keys row i sees, and
-//           times 2^(alpha_i + B_i - L_i);  sum_j P_ij v_j and sum_j P_ij
-// with a_if = log2e w_f.q_i, b_jf = log2e w_f.k_j, beta_j = bmax_j - log2e |k_j|^2/2,
-// L_i = max(mc_i, alpha_i + B_i + log2 max_j P_ij).  The factor
+//   chunk:  P_ij = sum_f 2^(a_if - alpha_i) 2^(b_jf + n_j - T)   (bf16 hi/lo, three
+//           MFMAs per 16 features), alpha_i = max_f a_if, T = the key tile's
+//           largest beta_j (or, on the diagonal tile with a wide beta spread,
+//           per-key shifts and a per-row factor, see below), times
+//           2^(alpha_i + T - L_i);  sum_j P_ij v_j and sum_j P_ij
+// with a_if = log2e w_f.q_i, b_jf = log2e w_f.k_j, n_j = -log2e |k_j|^2/2,
+// L_i = max(mc_i, alpha_i + T + log2 max_j P_ij) over the tiles.  The factor
 // exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
 template <int NW, int QT>
 __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane) {
@@ -191,23 +192,44 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         alo[ft][kb2][w] = l_;
       }
 
-  // P^T[key, query] for key tiles kt <= qt; beta_j per key (lane = key)
+  // P^T[key, query] for key tiles kt <= qt (lane = query, registers = keys).
+  // Key features carry one exponent shift per key:
+  //   shared: n_j - T, T = max_j beta_j over the tile, beta_j = bmax_j + n_j
+  //           (n_j = -log2e |k_j|^2/2, bmax_j the key's largest log2e w_f.k_j over
+  //           the first 32 of the features).  Every row of the tile then has
+  //           the common scale 2^T.  Always used for the tile below the
+  //           diagonal, whose keys every query of the wave sees.
+  //   per key: -bmax_j, then each entry times 2^(beta_j - B_i), B_i the largest
+  //           beta among the keys <= i; used for the diagonal tile when some
+  //           key's beta lies more than 2^kSpread below T (the first rows
+  //           would otherwise see only keys far below the tile's scale).
+  // s[kt] is the log2 scale of tile kt's entries for this lane's query row.
+  constexpr float kSpread = 32.f;
   f32x16 pt[2] = {};
   float bj[2] = {-kFInf, -kFInf};
+  float s[2] = {-kFInf, -kFInf};
+  bool perkey = false;   // wave-uniform: the diagonal tile uses per-key shifts
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     if (kt > qt) break;
     tile_rows(sm.k, 32 * kt + col, half, xB);
-    // per-key shift: the key's largest projection on the first 32 features
-    // (the second tile may exceed it; bf16 and fp32 keep that range)
-    float bm = -kFInf;
+    float sh = 0.f;
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft) {
       const f32x16 pk = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
       if (ft == 0) {
+        float bm = -kFInf;
 #pragma unroll
         for (int i = 0; i < 16; ++i) bm = fmaxf(bm, pk[i]);
         bm = pair_max(bm) * kLog2e;
+        const float kn = sm.knorm[32 * kt + col];   // -inf past the segment end
+        const float beta = bm + kn;
+        const float T = max32_uniform(beta);
+        bj[kt] = beta;
+        if (kt == qt) perkey = __ballot(beta > -kFInf && beta < T - kSpread) != 0;
+        const bool pk_shift = kt == qt && perkey;
+        sh = pk_shift ? -bm : (T == -kFInf ? -kFInf : kn - T);
+        s[kt] = T;
       }
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -215,8 +237,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t h_, l_;
-          split_bf16_trunc(fast_exp2(fmaf(pk[8 * kb2 + 2 * w], kLog2e, -bm)),
-                           fast_exp2(fmaf(pk[8 * kb2 + 2 * w + 1], kLog2e, -bm)), h_, l_);
+          split_bf16_trunc(fast_exp2(fmaf(pk[8 * kb2 + 2 * w], kLog2e, sh)),
+                           fast_exp2(fmaf(pk[8 * kb2 + 2 * w + 1], kLog2e, sh)), h_, l_);
           bhi[w] = h_;
           blo[w] = l_;
         }
@@ -225,45 +247,52 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         pt[kt] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(alo[ft][kb2]), pt[kt]);
       }
     }
-    bj[kt] = bm + sm.knorm[32 * kt + col];
   }
 
-  // B_i: largest beta among the keys query i sees (all of tile 0 when qt = 1,
-  // keys <= i of the diagonal tile): inclusive prefix max over key lanes.
-  float bvis = prefix_max32(bj[QT], lane);
-  if (QT == 1) {
-    const float t = prefix_max32(bj[0], lane);
-    bvis = fmaxf(bvis, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 31)));
-  }
-  // beta of the key in each register (lane -> register layout through the
-  // wave's own partial slot, which is written only at the end)
+  // causal mask on the diagonal tile (keys after the query drop out), the
+  // per-key factors where used, and each tile's row maximum
   float* scr = sm.np[wave];
-  if (half == 0) {
-    scr[col] = bj[0];
-    scr[32 + col] = bj[1];
-  }
-  float rmax = 0.f;
+  float rmx[2] = {0.f, 0.f};
+  if (qt == 1) {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    if (kt > qt) break;
+    for (int i = 0; i < 16; ++i) rmx[0] = fmaxf(rmx[0], pt[0][i]);
+    rmx[0] = pair_max(rmx[0]);
+  }
+  if (perkey) {
+    // beta of the key in each register (lane -> register layout through the
+    // wave's own partial slot, which is written only at the end)
+    if (half == 0) scr[col] = bj[qt];
+    s[qt] = prefix_max32(bj[qt], lane);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&scr[32 * kt + 8 * g4 + 4 * half]);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&scr[8 * g4 + 4 * half]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * g4 + j;
-        const bool vis = kt < qt || drow(i, half) <= col;
-        const float p = vis ? pt[kt][i] * fast_exp2(b4[j] - bvis) : 0.f;
-        pt[kt][i] = p;
-        rmax = fmaxf(rmax, p);
+        const float p = drow(i, half) <= col ? pt[qt][i] * fast_exp2(b4[j] - s[qt]) : 0.f;
+        pt[qt][i] = p;
+        rmx[qt] = fmaxf(rmx[qt], p);
       }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = drow(i, half) <= col ? pt[qt][i] : 0.f;
+      pt[qt][i] = p;
+      rmx[qt] = fmaxf(rmx[qt], p);
+    }
   }
-  rmax = pair_max(rmax);
-  const float ic = rmax > 0.f ? amax + bvis + __log2f(rmax) : -kFInf;
-  const float L = fmaxf(mc, ic);
+  rmx[qt] = pair_max(rmx[qt]);
+  float ic = -kFInf;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+    if (kt <= qt && rmx[kt] > 0.f) ic = fmaxf(ic, s[kt] + __log2f(rmx[kt]));
+  const float L = fmaxf(mc, amax + ic);
   const float Ls = L == -kFInf ? 0.f : L;
-  const float fac = rmax > 0.f ? fast_exp2(amax + bvis - Ls) : 0.f;
+  float fac[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+    if (kt <= qt && rmx[kt] > 0.f) fac[kt] = fast_exp2(amax + s[kt] - Ls);
   const float cfac = mc == -kFInf ? 0.f : fast_exp2(mc - Ls);
 
   // Both terms accumulate into one numerator (and one denominator, against a
@@ -297,7 +326,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       u32x4 a;
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        a[w] = pack_f16(pt[kt][8 * kb2 + 2 * w] * fac, pt[kt][8 * kb2 + 2 * w + 1] * fac);
+        a[w] = pack_f16(pt[kt][8 * kb2 + 2 * w] * fac[kt], pt[kt][8 * kb2 + 2 * w + 1] * fac[kt]);
       const u32x4 v0 = v_operand(sm.v, 32 * kt + 16 * kb2, 0, lane);
       const u32x4 v1 = v_operand(sm.v, 32 * kt + 16 * kb2, 1, lane);
       np0 = mfma_f16(as_f16x8(a), as_f16x8(v0), np0);

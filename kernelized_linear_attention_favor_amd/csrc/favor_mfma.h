@@ -102,6 +102,16 @@ __device__ __forceinline__ float prefix_max32(float x, int lane) {
   if (lane & 16) x = fmaxf(x, (lane & 32) ? r47 : r15);
   return x;
 }
+// Maximum over lanes 0..31, returned to every lane (a wave-uniform value);
+// lanes 32..63 are assumed to hold the same values as lanes 0..31.
+__device__ __forceinline__ float max32_uniform(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));   // lane ^ 1
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));   // lane ^ 2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)));  // 7 - lane
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false)));  // 15 - lane
+  return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
+               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
+}
 // Sum over each aligned group of 8 lanes (quad swaps, then the half-row mirror).
 __device__ __forceinline__ float sum8(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));  // lane ^ 1

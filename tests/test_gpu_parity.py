@@ -267,6 +267,23 @@ def test_bf16_causal_stress(scale):
     assert oracle.max_rel_err(y, oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
 
 
+@pytest.mark.parametrize("scale", [4.0, 6.0])
+def test_bf16_causal_wide_key_spread(scale):
+    """The first 8 keys of every 32-key tile have `scale` times the norm, so
+    the keys of a diagonal tile differ by far more than 2^32 in their largest
+    feature: the chunk term takes per-key shifts there, and rows 0-7 of a
+    tile see only the large-norm keys of their own tile."""
+    cfg = fi.config("C2", H=2, n=2000, causal=True)
+    x = fi.make_inputs(cfg)
+    k = x["k"].astype(np.float64)
+    sel = (np.arange(k.shape[-2]) % 32) < 8
+    k[:, :, sel, :] *= scale
+    x["k"] = fi.round_bf16(k)
+    y = run(x, torch.bfloat16, causal=True)
+    assert np.all(np.isfinite(y))
+    assert oracle.max_rel_err(y, oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
+
+
 def test_bf16_causal_growing_keys():
     """Key norms grow along the sequence, so later chunks raise the running
     per-feature shift many times (the rescale path)."""
