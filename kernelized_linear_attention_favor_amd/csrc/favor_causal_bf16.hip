@@ -47,11 +47,15 @@ struct CsSmem {
   uint16_t q[kKT * kD];
   float knorm[kKT];                  // -|k|^2/2 in log2 units; -inf past the segment end
   float gam[M];                      // log2 of the running feature sums z_f (with shift)
-  float colmax[NW][kD];              // prologue scratch: |v| maxima, carry z and c
+  float colmax[NW][kD];              // prologue scratch (|v| maxima, carry z and c), then
+                                     // G_f = 2^(gam_f - Gm) (M) and per-wave max gam (NW)
   float np[NW][32 * kD];             // per wave: partial numerators [query][value, swizzled]
   float dp[NW][32];                  // per wave: partial denominators
   float lp[NW][32];                  // per wave: log2 scale of the partials
   float xs[NW][32];                  // per wave: per-feature scalars, lane -> register layout
+  __device__ float* gexp() { return &colmax[0][0]; }
+  __device__ const float* gexp() const { return &colmax[0][0]; }
+  __device__ float* gwmax() { return &colmax[0][0] + M; }
 };
 
 template <int NW>
@@ -120,6 +124,51 @@ __device__ __forceinline__ void tile_rows(const uint16_t* t, int row, int half, 
 // Row of D-layout register i inside a 32 x 32 tile, for lane half `half`.
 __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
+// Carry weights u_if = 2^(a_if + gam_f - mc_i) and mc_i straight from the
+// projections (the rarely taken path; kept out of line so that its registers
+// do not weigh on the common path).
+struct CarryW {
+  u32x4 ua[2][2];
+  float mc;
+};
+template <int NW>
+__device__ __attribute__((noinline)) CarryW carry_weights_exact(const CsSmem<NW>& sm, int f0, int qt,
+                                                                int lane) {
+  const int col = lane & 31, half = lane >> 5;
+  CarryW r;
+  u32x4 xB[4];
+  tile_rows(sm.q, 32 * qt + col, half, xB);
+  float mc = -kFInf;
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft) {
+    const f32x16 pr = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.gam[f0 + 32 * ft + 8 * g4 + 4 * half]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mc = fmaxf(mc, fmaf(pr[4 * g4 + j], kLog2e, g[j]));
+    }
+  }
+  mc = pair_max(mc);
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft) {
+    const f32x16 pr = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.gam[f0 + 32 * ft + 8 * g4 + 4 * half]);
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const int i = 4 * g4 + j;
+        r.ua[ft][g4 >> 1][2 * (g4 & 1) + (j >> 1)] =
+            pack_f16(fast_exp2(fmaf(pr[i], kLog2e, g[j]) - mc),
+                     fast_exp2(fmaf(pr[i + 1], kLog2e, g[j + 1]) - mc));
+      }
+    }
+  }
+  r.mc = mc;
+  return r;
+}
+
 // Query side of one chunk for the wave's 32 queries (tile qt) and 64 features
 // (group fg): partial numerator, denominator and their log2 scale L_i.
 //   carry:  u_if = 2^(a_if + gam_f - mc_i) (fp16), mc_i = max_f (a_if + gam_f);
@@ -133,8 +182,9 @@ __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 *
 // L_i = max(mc_i, alpha_i + T + log2 max_j P_ij) over the tiles.  The factor
 // exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
 template <int NW, int QT>
-__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane) {
+__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float Gm) {
   constexpr int YS = CsSmem<NW>::YS;
+  const float* gexp = sm.gexp();
   constexpr int qt = QT;
   const int col = lane & 31, half = lane >> 5;
   const int f0 = 64 * (wave % (NW / 2));
@@ -144,39 +194,63 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   f32x16 pa[2];
   pa[0] = w_proj(sm.w, f0 + col, half, xB);
   pa[1] = w_proj(sm.w, f0 + 32 + col, half, xB);
-  // maxima of the raw projections, scaled afterwards (rounding is monotone)
-  float amax = -kFInf, mc = -kFInf;
+  // query features 2^(a_if - alpha_i), alpha_i = max_f a_if (the maximum of
+  // the raw projections, scaled afterwards: rounding is monotone), in place
+  float amax = -kFInf;
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.gam[f0 + 32 * ft + 8 * g4 + 4 * half]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g4 + j;
-        amax = fmaxf(amax, pa[ft][i]);
-        mc = fmaxf(mc, fmaf(pa[ft][i], kLog2e, g[j]));
-      }
-    }
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, pa[ft][i]);
   amax = pair_max(amax) * kLog2e;
-  mc = pair_max(mc);
-  const float mcs = mc == -kFInf ? 0.f : mc;
-
-  // carry weights (fp16, A operand: lane = query, k = feature)
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pa[ft][i] = fast_exp2(fmaf(pa[ft][i], kLog2e, -amax));
+  // carry weights u_if = 2^(a_if + gam_f - mc_i) (fp16, A operand: lane =
+  // query, k = feature), mc_i = max_f (a_if + gam_f).  From the features
+  // above: u_if = 2^(a_if - alpha_i) G_f / max_f (...), G_f = 2^(gam_f - Gm)
+  // (published with the state, Gm = max_f gam_f), so mc_i = alpha_i + Gm +
+  // log2 max_f (...).  When some row's maximum product falls below 2^-60
+  // (its strongest state features are far from its own), the weights are
+  // taken from the projections directly, after the chunk term (where fewer
+  // registers are live).
   u32x4 ua[2][2];
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.gam[f0 + 32 * ft + 8 * g4 + 4 * half]);
+    for (int kb2 = 0; kb2 < 2; ++kb2) ua[ft][kb2] = u32x4{0u, 0u, 0u, 0u};
+  float mc = -kFInf;
+  bool exact_carry = false;   // wave-uniform
+  if (Gm != -kFInf) {         // else no keys before this chunk: no carry
+    float pmx = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        const int i = 4 * g4 + j;
-        ua[ft][g4 >> 1][2 * (g4 & 1) + (j >> 1)] =
-            pack_f16(fast_exp2(fmaf(pa[ft][i], kLog2e, g[j]) - mcs),
-                     fast_exp2(fmaf(pa[ft][i + 1], kLog2e, g[j + 1]) - mcs));
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 G = *reinterpret_cast<const f32x4*>(&gexp[f0 + 32 * ft + 8 * g4 + 4 * half]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pmx = fmaxf(pmx, pa[ft][4 * g4 + j] * G[j]);
       }
+    pmx = pair_max(pmx);
+    exact_carry = __ballot(!(pmx >= 0x1p-60f)) != 0;
+    if (!exact_carry) {
+      const float kap = fast_rcp(pmx);
+      mc = __log2f(pmx) + amax + Gm;
+#pragma unroll
+      for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 G = *reinterpret_cast<const f32x4*>(&gexp[f0 + 32 * ft + 8 * g4 + 4 * half]);
+#pragma unroll
+          for (int j = 0; j < 4; j += 2) {
+            const int i = 4 * g4 + j;
+            ua[ft][g4 >> 1][2 * (g4 & 1) + (j >> 1)] =
+                pack_f16(pa[ft][i] * G[j] * kap, pa[ft][i + 1] * G[j + 1] * kap);
+          }
+        }
     }
+  }
+
   // query features of the chunk term, bf16 hi + lo (B operand: k = feature, n = query)
   u32x4 ahi[2][2], alo[2][2];
 #pragma unroll
@@ -186,8 +260,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t h_, l_;
-        split_bf16_trunc(fast_exp2(fmaf(pa[ft][8 * kb2 + 2 * w], kLog2e, -amax)),
-                         fast_exp2(fmaf(pa[ft][8 * kb2 + 2 * w + 1], kLog2e, -amax)), h_, l_);
+        split_bf16_trunc(pa[ft][8 * kb2 + 2 * w], pa[ft][8 * kb2 + 2 * w + 1], h_, l_);
         ahi[ft][kb2][w] = h_;
         alo[ft][kb2][w] = l_;
       }
@@ -247,6 +320,15 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         pt[kt] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(alo[ft][kb2]), pt[kt]);
       }
     }
+  }
+
+  if (exact_carry) {
+    const CarryW cw = carry_weights_exact<NW>(sm, f0, qt, lane);
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) ua[ft][kb2] = cw.ua[ft][kb2];
+    mc = cw.mc;
   }
 
   // causal mask on the diagonal tile (keys after the query drop out), the
@@ -500,6 +582,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const float iz = z > 0.f ? fast_rcp(z) : 0.f;
     gam = z > 0.f ? c + __log2f(z) : -kFInf;
     if (half == 0) sm.xs[wave][col] = iz;
+    const float gw = max32_uniform(gam);
+    if (lane == 0) sm.gwmax()[wave] = gw;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 z4 = *reinterpret_cast<const f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]);
@@ -507,8 +591,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
       for (int j = 0; j < 4; ++j) izr[4 * g4 + j] = z4[j];
     }
   };
-  // after a barrier (the previous chunk's readers are done): yhat and gam to LDS
+  // after a barrier (the previous chunk's readers are done): yhat, gam and
+  // G_f = 2^(gam_f - Gm) to LDS; Gm = max_f gam_f (-inf before any key)
+  float Gm = -kFInf;
   auto publish = [&](int col, int half) {
+    Gm = -kFInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Gm = fmaxf(Gm, sm.gwmax()[w]);
+    if (half == 0) sm.gexp()[32 * wave + col] = gam == -kFInf ? 0.f : fast_exp2(gam - Gm);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int fr = 32 * wave + 8 * g4 + 4 * half;
@@ -543,9 +633,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const int col = ln & 31, half = ln >> 5;
     const int fk = 32 * wave + col;
     if (wave < NW / 2)
-      cs_query_phase<NW, 0>(sm, wave, ln);
+      cs_query_phase<NW, 0>(sm, wave, ln, Gm);
     else
-      cs_query_phase<NW, 1>(sm, wave, ln);
+      cs_query_phase<NW, 1>(sm, wave, ln, Gm);
 
     // ---- key side: this chunk's keys into the wave's features
     f32x16 pk[2];
