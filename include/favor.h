@@ -136,8 +136,13 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
  * are static strings owned by the library), stops recording, clears the
  * record and returns the number of distinct kernels (which may exceed
  * capacity).  Returns -1 if a HIP event call failed.
+ * favor_profile_enable_only(name) does the same for the kernels of that one
+ * name only (the names favor_profile_collect reports, e.g. "k_output"), so
+ * that the events of the others stay out of the stream; NULL means all.  The
+ * string is copied.
  */
 favor_status_t favor_profile_enable(void);
+favor_status_t favor_profile_enable_only(const char* name);
 int favor_profile_collect(const char** names, int* counts, double* total_ms, int capacity);
 
 #ifdef __cplusplus

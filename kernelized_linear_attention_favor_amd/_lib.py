@@ -37,6 +37,7 @@ SIGNATURES = {
     "favor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "favor_attention_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "favor_profile_enable": (_i, []),
+    "favor_profile_enable_only": (_i, [ctypes.c_char_p]),
     "favor_profile_collect": (_i, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_i),
                                    ctypes.POINTER(ctypes.c_double), _i]),
 }
@@ -119,6 +120,10 @@ def favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, str
 
 def favor_profile_enable() -> int:
     return lib().favor_profile_enable()
+
+
+def favor_profile_enable_only(name) -> int:
+    return lib().favor_profile_enable_only(None if name is None else name.encode())
 
 
 def favor_profile_collect(capacity: int = 32) -> dict:

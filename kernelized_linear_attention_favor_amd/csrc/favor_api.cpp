@@ -21,6 +21,8 @@ struct ProfRec {
 struct Profiler {
   bool on = false;
   bool failed = false;
+  char only[64] = "";   // record only kernels of this name (empty: all)
+  bool open = false;    // the last prof_begin recorded a start event
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
   hipEvent_t get() {
@@ -38,14 +40,18 @@ thread_local Profiler g_prof;
 }  // namespace
 
 void prof_begin(hipStream_t s, const char* name) {
+  g_prof.open = false;
   if (!g_prof.on) return;
+  if (g_prof.only[0] && strcmp(g_prof.only, name) != 0) return;
+  g_prof.open = true;
   ProfRec r{name, g_prof.get(), g_prof.get()};
   if (r.start && hipEventRecord(r.start, s) != hipSuccess) g_prof.failed = true;
   g_prof.recs.push_back(r);
 }
 
 void prof_end(hipStream_t s) {
-  if (!g_prof.on || g_prof.recs.empty()) return;
+  if (!g_prof.on || !g_prof.open || g_prof.recs.empty()) return;
+  g_prof.open = false;
   hipEvent_t e = g_prof.recs.back().stop;
   if (e && hipEventRecord(e, s) != hipSuccess) g_prof.failed = true;
 }
@@ -159,8 +165,15 @@ extern "C" {
 
 int favor_version(void) { return 10000; }
 
-favor_status_t favor_profile_enable(void) {
-  favor::g_prof.on = true;
+favor_status_t favor_profile_enable(void) { return favor_profile_enable_only(nullptr); }
+
+favor_status_t favor_profile_enable_only(const char* name) {
+  auto& P = favor::g_prof;
+  if (name && strlen(name) >= sizeof(P.only))
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "kernel name longer than %zu characters", sizeof(P.only) - 1);
+  P.only[0] = '\0';
+  if (name) strcpy(P.only, name);
+  P.on = true;
   return ok();
 }
 
@@ -190,6 +203,8 @@ int favor_profile_collect(const char** names, int* counts, double* total_ms, int
   }
   P.recs.clear();
   P.on = false;
+  P.open = false;
+  P.only[0] = '\0';
   P.failed = false;
   for (size_t i = 0; i < uniq.size() && static_cast<int>(i) < capacity; ++i) {
     if (names) names[i] = uniq[i];

@@ -96,3 +96,13 @@ def test_no_cpu_path():
     W = torch.zeros(1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         favor.attention(q, q, q, W)
+
+
+def test_profile_filter_host_only():
+    # no kernel is launched: the hooks record nothing and collect reports 0 kernels
+    L = _lib()
+    assert L.favor_profile_enable_only("k" * 80) == 1   # name too long
+    assert L.favor_profile_enable_only("k_output") == 0
+    assert L.favor_profile_collect() == {}
+    assert L.favor_profile_enable_only(None) == 0
+    assert L.favor_profile_collect() == {}

@@ -295,3 +295,19 @@ def test_bf16_causal_growing_keys():
     y = run(x, torch.bfloat16, causal=True)
     assert np.all(np.isfinite(y))
     assert oracle.max_rel_err(y, oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
+
+
+def test_profile_filter_records_one_kernel():
+    x = fi.make_inputs(fi.config("C2", H=2, n=512))
+    t = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    _lib = favor._lib
+    _lib.check(_lib.favor_profile_enable_only("k_output"))
+    favor.attention(t["q"], t["k"], t["v"], t["W"])
+    torch.cuda.synchronize()
+    only = _lib.favor_profile_collect()
+    _lib.check(_lib.favor_profile_enable())
+    favor.attention(t["q"], t["k"], t["v"], t["W"])
+    torch.cuda.synchronize()
+    every = _lib.favor_profile_collect()
+    assert set(only) == {"k_output"} and only["k_output"][0] == 1
+    assert {"k_kv_state", "k_merge", "k_output"} <= set(every)
