@@ -53,6 +53,8 @@ struct CsSmem {
   float dp[NW][32];                  // per wave: partial denominators
   float lp[NW][32];                  // per wave: log2 scale of the partials
   float xs[NW][32];                  // per wave: per-feature scalars, lane -> register layout
+  int hflag[NW / 2];                 // per feature group: key tile 0 handed over (chunk + 1)
+  float htile[NW / 2];               // ... and its shift
   __device__ float* gexp() { return &colmax[0][0]; }
   __device__ const float* gexp() const { return &colmax[0][0]; }
   __device__ float* gwmax() { return &colmax[0][0] + M; }
@@ -182,7 +184,8 @@ __device__ __attribute__((noinline)) CarryW carry_weights_exact(const CsSmem<NW>
 // L_i = max(mc_i, alpha_i + T + log2 max_j P_ij) over the tiles.  The factor
 // exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
 template <int NW, int QT>
-__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float Gm) {
+__device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float Gm,
+                                               int chunk) {
   constexpr int YS = CsSmem<NW>::YS;
   const float* gexp = sm.gexp();
   constexpr int qt = QT;
@@ -282,11 +285,46 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   float bj[2] = {-kFInf, -kFInf};
   float s[2] = {-kFInf, -kFInf};
   bool perkey = false;   // wave-uniform: the diagonal tile uses per-key shifts
+  // Key tile 0 is the query tile 0 wave's diagonal tile and the query tile 1
+  // wave's off-diagonal one, with the same shared shift unless the former
+  // needs per-key shifts.  The tile 0 wave hands its operands over through the
+  // tile 1 wave's partial slot (free until that wave's own partials) and a
+  // per-chunk flag: +(chunk+1) handed over, -(chunk+1) not.  The tile 1 wave
+  // takes its diagonal tile first and computes tile 0 itself when nothing was
+  // handed over (or after a bounded wait).
+  const int grp = wave % (NW / 2);
+  uint32_t* hand = reinterpret_cast<uint32_t*>(sm.np[NW / 2 + grp]);
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    if (kt > qt) break;
+  for (int kk = 0; kk < 2; ++kk) {
+    const int kt = qt == 1 ? 1 - kk : kk;   // the diagonal tile first
+    if (kt > qt) continue;
+    if (qt == 1 && kt == 0) {
+      const int want = chunk + 1;
+      int f = 0;
+      for (int it = 0; it < 4096; ++it) {
+        f = *reinterpret_cast<volatile int*>(&sm.hflag[grp]);
+        if (f == want || f == -want) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (f == want) {
+        s[0] = sm.htile[grp];
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int blk = 2 * (2 * ft + kb2);
+            const u32x4 bhi = *reinterpret_cast<const u32x4*>(&hand[(blk * 64 + lane) * 4]);
+            const u32x4 blo = *reinterpret_cast<const u32x4*>(&hand[((blk + 1) * 64 + lane) * 4]);
+            pt[0] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(ahi[ft][kb2]), pt[0]);
+            pt[0] = mfma_bf16(as_bf16x8(blo), as_bf16x8(ahi[ft][kb2]), pt[0]);
+            pt[0] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(alo[ft][kb2]), pt[0]);
+          }
+        continue;
+      }
+    }
     tile_rows(sm.k, 32 * kt + col, half, xB);
     float sh = 0.f;
+    bool give = false;   // wave-uniform
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft) {
       const f32x16 pk = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
@@ -303,6 +341,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         const bool pk_shift = kt == qt && perkey;
         sh = pk_shift ? -bm : (T == -kFInf ? -kFInf : kn - T);
         s[kt] = T;
+        give = qt == 0 && !perkey;
       }
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -315,10 +354,20 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
           bhi[w] = h_;
           blo[w] = l_;
         }
+        if (give) {
+          const int blk = 2 * (2 * ft + kb2);
+          *reinterpret_cast<u32x4*>(&hand[(blk * 64 + lane) * 4]) = bhi;
+          *reinterpret_cast<u32x4*>(&hand[((blk + 1) * 64 + lane) * 4]) = blo;
+        }
         pt[kt] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(ahi[ft][kb2]), pt[kt]);
         pt[kt] = mfma_bf16(as_bf16x8(blo), as_bf16x8(ahi[ft][kb2]), pt[kt]);
         pt[kt] = mfma_bf16(as_bf16x8(bhi), as_bf16x8(alo[ft][kb2]), pt[kt]);
       }
+    }
+    if (qt == 0) {
+      // the flag after the operands (LDS operations of a wave complete in order)
+      if (give && lane == 0) sm.htile[grp] = s[0];
+      if (lane == 0) *reinterpret_cast<volatile int*>(&sm.hflag[grp]) = give ? chunk + 1 : -(chunk + 1);
     }
   }
 
@@ -614,6 +663,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     if (half == 0) sm.gam[32 * wave + col] = gam;
   };
 
+  if (tid < NW / 2) sm.hflag[tid] = 0;
   summarize(col, half);
   lds_barrier();
   publish(col, half);
@@ -633,9 +683,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const int col = ln & 31, half = ln >> 5;
     const int fk = 32 * wave + col;
     if (wave < NW / 2)
-      cs_query_phase<NW, 0>(sm, wave, ln, Gm);
+      cs_query_phase<NW, 0>(sm, wave, ln, Gm, t);
     else
-      cs_query_phase<NW, 1>(sm, wave, ln, Gm);
+      cs_query_phase<NW, 1>(sm, wave, ln, Gm, t);
 
     // ---- key side: this chunk's keys into the wave's features
     f32x16 pk[2];
