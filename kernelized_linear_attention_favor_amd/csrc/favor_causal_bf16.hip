@@ -302,7 +302,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       const int want = chunk + 1;
       int f = 0;
       for (int it = 0; it < 4096; ++it) {
-        f = *reinterpret_cast<volatile int*>(&sm.hflag[grp]);
+        f = __hip_atomic_load(&sm.hflag[grp], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (f == want || f == -want) break;
         __builtin_amdgcn_s_sleep(1);
       }
@@ -365,9 +365,11 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       }
     }
     if (qt == 0) {
-      // the flag after the operands (LDS operations of a wave complete in order)
+      // the flag is released after the operands and the shift
       if (give && lane == 0) sm.htile[grp] = s[0];
-      if (lane == 0) *reinterpret_cast<volatile int*>(&sm.hflag[grp]) = give ? chunk + 1 : -(chunk + 1);
+      if (lane == 0)
+        __hip_atomic_store(&sm.hflag[grp], give ? chunk + 1 : -(chunk + 1), __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
 
