@@ -684,10 +684,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     asm volatile("" : "+v"(ln));
     const int col = ln & 31, half = ln >> 5;
     const int fk = 32 * wave + col;
-    if (wave < NW / 2)
+    const bool tile0 = wave < NW / 2;   // wave-uniform
+    if (tile0)
       cs_query_phase<NW, 0>(sm, wave, ln, Gm, t);
     else
       cs_query_phase<NW, 1>(sm, wave, ln, Gm, t);
+    // Query tile 1 carries twice tile 0's chunk term.  Its waves therefore
+    // update their key state after the first barrier, while the tile 0 waves
+    // combine the partials; a second barrier then lets the tiles be restaged.
+    // (Every wave passes three barriers per chunk, at wave-uniform points.)
+    if (!tile0) lds_barrier();
 
     // ---- key side: this chunk's keys into the wave's features
     f32x16 pk[2];
@@ -765,40 +771,42 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     z += sm.xs[wave][col];
     const bool more = t + 1 < nchunks;
     if (more) summarize(col, half);
-    lds_barrier();
-
-    if (more) publish(col, half);
-    // ---- combine the partials of the chunk's rows and store
-    for (int it = tid; it < kKT * 8; it += NW * 64) {
-      const int qrow = it >> 3, d0 = (it & 7) * 8;
-      if (t0 + qrow >= ntok) continue;
-      const int qt = qrow >> 5, r = qrow & 31;
-      float lmax = -kFInf;
+    if (tile0) {
+      lds_barrier();
+      // ---- combine the partials of the chunk's rows and store
+      for (int it = tid; it < kKT * 8; it += NW / 2 * 64) {
+        const int qrow = it >> 3, d0 = (it & 7) * 8;
+        if (t0 + qrow >= ntok) continue;
+        const int qt = qrow >> 5, r = qrow & 31;
+        float lmax = -kFInf;
 #pragma unroll
-      for (int g = 0; g < NQ; ++g) lmax = fmaxf(lmax, sm.lp[qt * NQ + g][r]);
-      float den = 0.f;
-      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < NQ; ++g) lmax = fmaxf(lmax, sm.lp[qt * NQ + g][r]);
+        float den = 0.f;
+        f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < NQ; ++g) {
-        const int w = qt * NQ + g;
-        const float l = sm.lp[w][r];
-        const float wt = l == -kFInf ? 0.f : fast_exp2(l - lmax);
-        den = fmaf(wt, sm.dp[w][r], den);
-        const int ds = d0 ^ ((r & 7) << 3);
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + ds]);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + ds + 4]);
+        for (int g = 0; g < NQ; ++g) {
+          const int w = qt * NQ + g;
+          const float l = sm.lp[w][r];
+          const float wt = l == -kFInf ? 0.f : fast_exp2(l - lmax);
+          den = fmaf(wt, sm.dp[w][r], den);
+          const int ds = d0 ^ ((r & 7) << 3);
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + ds]);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.np[w][r * kD + ds + 4]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          n0[j] = fmaf(wt, a[j], n0[j]);
-          n1[j] = fmaf(wt, b[j], n1[j]);
+          for (int j = 0; j < 4; ++j) {
+            n0[j] = fmaf(wt, a[j], n0[j]);
+            n1[j] = fmaf(wt, b[j], n1[j]);
+          }
         }
+        const float inv = vsig * fast_rcp(den);
+        f32x4* dst = reinterpret_cast<f32x4*>(Ob + static_cast<size_t>(t0 + qrow) * kD + d0);
+        __builtin_nontemporal_store(n0 * inv, dst);
+        __builtin_nontemporal_store(n1 * inv, dst + 1);
       }
-      const float inv = vsig * fast_rcp(den);
-      f32x4* dst = reinterpret_cast<f32x4*>(Ob + static_cast<size_t>(t0 + qrow) * kD + d0);
-      __builtin_nontemporal_store(n0 * inv, dst);
-      __builtin_nontemporal_store(n1 * inv, dst + 1);
     }
+    lds_barrier();   // every key state updated and summarised
     if (more) {
+      publish(col, half);
       cs_stage<NW>(sm, regs, tid, ntok - t0 - kKT, vinv);
       cs_load<NW>(regs, Kb, Vb, Qb, t0 + 2 * kKT, ntok, tid);
     }
