@@ -33,7 +33,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "feature_map", "kv_state", "attention", "attention_causal", "attention_quadratic",
+    "feature_map", "kv_state", "attention", "attention_causal", "decode", "attention_quadratic",
     "attention_quadratic_rows", "softmax_attention", "max_rel_err",
 ]
 
@@ -132,6 +132,36 @@ def attention_causal(Q, K, V, W, block: int = 256) -> np.ndarray:
         S = Srun[..., -1, :, :]
         z = zrun[..., -1, :]
     return Y
+
+
+def decode(Q, K, V, W, S0=None, z0=None):
+    """Streaming (token-by-token) causal FAVOR+: the prefix sums carried as a
+    state and updated one token at a time.
+
+    Performer for vision, How It Works, Step 2 (running prefix sums, each token
+    seeing only earlier ones and itself), written as the recurrence over the
+    T new tokens t = 0 .. T-1, starting from the state (S0, z0) of the keys
+    before them (zero state if None):
+        S <- S + phi(k_t) v_t^T,   z <- z + phi(k_t),   y_t = phi(q_t)^T S / phi(q_t)^T z.
+    Returns (Y [..., T, d], S [..., m, d], z [..., m]); the state is the plain
+    (unshifted) one of kv_state.
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    phiQ = feature_map(Q, W)
+    phiK = feature_map(K, W)
+    lead = Q.shape[:-2]
+    T, d = Q.shape[-2], V.shape[-1]
+    m = phiQ.shape[-1]
+    S = np.zeros(lead + (m, d)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(lead + (m,)) if z0 is None else _f64(z0).copy()
+    Y = np.empty(lead + (T, d))
+    for t in range(T):
+        S = S + phiK[..., t, :, None] * V[..., t, None, :]
+        z = z + phiK[..., t, :]
+        num = np.einsum("...m,...md->...d", phiQ[..., t, :], S)
+        den = np.einsum("...m,...m->...", phiQ[..., t, :], z)
+        Y[..., t, :] = num / den[..., None]
+    return Y, S, z
 
 
 def attention_quadratic(Q, K, V, W, causal: bool = False) -> np.ndarray:

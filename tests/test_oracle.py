@@ -393,3 +393,53 @@ def test_max_rel_err_metric():
     assert abs(oracle.max_rel_err(y, ref) - 0.01) < 1e-15
     with pytest.raises(ValueError):
         oracle.max_rel_err(y[..., :3], ref)
+
+
+# ---------------------------------------------------------------- streaming decode
+def _small(seed, B=1, H=2, n=70, d=8, m=16, scale=1.0):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((B, H, n, d)) * scale * d ** -0.25
+    K = rng.standard_normal((B, H, n, d)) * scale * d ** -0.25
+    V = rng.standard_normal((B, H, n, d))
+    W = rng.standard_normal((H, m, d))
+    return Q, K, V, W
+
+
+def test_decode_from_empty_equals_causal_prefix_sums():
+    Q, K, V, W = _small(11)
+    Y, S, z = oracle.decode(Q, K, V, W)
+    np.testing.assert_allclose(Y, oracle.attention_causal(Q, K, V, W, block=16), rtol=1e-12, atol=1e-13)
+    Sk, zk = oracle.kv_state(K, V, W)
+    np.testing.assert_allclose(S, Sk, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(z, zk, rtol=1e-12)
+
+
+def test_decode_continues_a_prefix_state():
+    Q, K, V, W = _small(12, n=50)
+    p = 31
+    S0, z0 = oracle.kv_state(K[..., :p, :], V[..., :p, :], W)
+    Y, S, z = oracle.decode(Q[..., p:, :], K[..., p:, :], V[..., p:, :], W, S0, z0)
+    full = oracle.attention_quadratic(Q, K, V, W, causal=True)   # independent masked form
+    np.testing.assert_allclose(Y, full[..., p:, :], rtol=1e-11, atol=1e-12)
+    Sk, zk = oracle.kv_state(K, V, W)
+    np.testing.assert_allclose(S, Sk, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(z, zk, rtol=1e-12)
+
+
+def test_decode_first_token_and_constant_values():
+    Q, K, V, W = _small(13, n=20)
+    Y, _, _ = oracle.decode(Q, K, V, W)
+    np.testing.assert_allclose(Y[..., 0, :], V[..., 0, :], rtol=1e-12, atol=1e-13)   # y_0 = v_0
+    Vc = np.broadcast_to(np.linspace(-2.0, 3.0, V.shape[-1]), V.shape)
+    Yc, _, _ = oracle.decode(Q, K, Vc, W)
+    np.testing.assert_allclose(Yc, Vc, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_state_is_additive():
+    # the state of a sequence is the sum of its parts' states (associativity of the prefix sums)
+    Q, K, V, W = _small(14, n=40)
+    _, Sa, za = oracle.decode(Q[..., :17, :], K[..., :17, :], V[..., :17, :], W)
+    _, Sb, zb = oracle.decode(Q[..., 17:, :], K[..., 17:, :], V[..., 17:, :], W)
+    _, S, z = oracle.decode(Q, K, V, W)
+    np.testing.assert_allclose(Sa + Sb, S, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(za + zb, z, rtol=1e-12)
