@@ -128,6 +128,41 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Streaming decode -- the causal prefix sums carried from call to call
+ * (Performer for vision, How It Works, Step 2: each token adds its key
+ * features and value to running sums S, z and reads them with its query).
+ *
+ * A state holds, for each (b,h) and feature f, over the keys j absorbed so far:
+ *   S_f = sum_j 2^(e_jf - c_f) v_j   (d floats),   z_f = sum_j 2^(e_jf - c_f),   c_f,
+ * with e_jf = log2(e) (w_f.k_j - |k_j|^2/2): the key/value summary S = Phi(K)^T V
+ * and z = Phi(K)^T 1 (Performer notes, Kernel Attention View and Normalization)
+ * up to the factor 2^c_f / sqrt(m) per feature, which is carried (c_f) or
+ * cancels in y (1/sqrt(m)).  Layout: fp32, favor_state_bytes(B,H,d,m) bytes:
+ *   S [B,H,m,d], then z [B,H,m], then c [B,H,m] (log2 units).
+ * The empty state is S = 0, z = 0, c = -inf.  Shapes: d == 64, m in {64,128,256}
+ * (the bf16 path); q, k, v, W bf16; state and out 16-byte aligned.
+ *
+ * favor_state_bytes  -- bytes of a state (0 if the shape is not supported).
+ * favor_state_reset  -- write the empty state.
+ * favor_state_from_keys -- replace the state by that of the n keys k, v
+ *   ([B,H,n,d]; e.g. a prompt), computed in parallel over the keys.  Scratch is
+ *   allocated stream-ordered on `stream`.
+ * favor_decode -- T new tokens per (b,h) (q, k, v: [B,H,T,d]), in order: token
+ *   t's key and value join the state, then y_t = phi(q_t)^T S / phi(q_t)^T z
+ *   (inclusive, as in favor_attention with causal = 1) goes to out
+ *   (fp32 [B,H,T,d]).  The state is updated in place; a sequence decoded in any
+ *   split into calls gives the same outputs.  One workgroup per (b,h) walks its
+ *   T tokens in order.
+ */
+size_t favor_state_bytes(int B, int H, int d, int m);
+favor_status_t favor_state_reset(float* state, int B, int H, int d, int m, hipStream_t stream);
+favor_status_t favor_state_from_keys(const void* k, const void* v, const void* W, float* state,
+                                     int B, int H, int n, int d, int m, hipStream_t stream);
+favor_status_t favor_decode(const void* q, const void* k, const void* v, const void* W,
+                            float* state, float* out, int B, int H, int T, int d, int m,
+                            hipStream_t stream);
+
+/*
  * Diagnostics: per-kernel timing with HIP events.  favor_profile_enable()
  * starts recording on the calling thread: every kernel the library launches
  * from that thread is bracketed by two HIP events recorded on the launch

@@ -7,6 +7,8 @@ CPU path, and calls on CPU tensors raise.
     y = attention(q, k, v, W)                  # non-causal, bf16 or fp32 inputs
     y = attention(q, k, v, W, causal=True)     # causal (prefix-sum form)
     phi = feature_map(x, W)                    # exp(W x - |x|^2/2) / sqrt(m)
+    st = State(B, H, d, m); st.from_keys(k, v, W)   # streaming decode: state of a prompt,
+    y = decode(q1, k1, v1, W, st)              # then T new tokens at a time (bf16)
 
 Layouts: q, k, v, x [B, H, n, d]; W [H, m, d]; outputs float32.
 """
@@ -18,7 +20,7 @@ from . import _lib
 from ._lib import FavorError, check  # noqa: F401
 
 __all__ = ["feature_map", "attention", "attention_causal", "Workspace", "FavorError",
-           "workspace_bytes", "version"]
+           "workspace_bytes", "version", "State", "decode"]
 
 
 def version() -> int:
@@ -132,4 +134,59 @@ def attention_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch
         check(_lib.favor_attention_causal(*ptrs, B, H, n, d, m, chunk, s))
     else:
         raise TypeError("q must be bfloat16 or float32")
+    return out
+
+
+class State:
+    """Streaming-decode state (fp32): S [B,H,m,d], z [B,H,m], c [B,H,m] in one
+    buffer, starting empty.  The carried prefix sums of the causal path."""
+
+    def __init__(self, B: int, H: int, d: int, m: int, device="cuda", stream=None):
+        nbytes = _lib.favor_state_bytes(B, H, d, m)
+        if nbytes == 0:
+            raise FavorError(_lib.FAVOR_ERR_UNSUPPORTED, "shape not supported by the decode path")
+        self.B, self.H, self.d, self.m = B, H, d, m
+        self.buf = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+        self.reset(stream)
+
+    def reset(self, stream=None) -> "State":
+        check(_lib.favor_state_reset(self.buf.data_ptr(), self.B, self.H, self.d, self.m,
+                                     _stream_handle(stream)))
+        return self
+
+    def from_keys(self, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor, stream=None) -> "State":
+        """Replace the state by that of the keys k, v ([B,H,n,d], bf16)."""
+        B, H, n, d, m = _shapes(k, W)
+        if (B, H, d, m) != (self.B, self.H, self.d, self.m):
+            raise ValueError("k/W shapes do not match the state")
+        _need(k, "k", torch.bfloat16, (B, H, n, d))
+        _need(v, "v", torch.bfloat16, (B, H, n, d))
+        _need(W, "W", torch.bfloat16, (H, m, d))
+        check(_lib.favor_state_from_keys(k.data_ptr(), v.data_ptr(), W.data_ptr(), self.buf.data_ptr(),
+                                         B, H, n, d, m, _stream_handle(stream)))
+        return self
+
+    def tensors(self):
+        """Views (S [B,H,m,d], z [B,H,m], c [B,H,m]) of the buffer."""
+        B, H, d, m = self.B, self.H, self.d, self.m
+        ns, nz = B * H * m * d, B * H * m
+        return (self.buf[:ns].view(B, H, m, d), self.buf[ns:ns + nz].view(B, H, m),
+                self.buf[ns + nz:].view(B, H, m))
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor, state: State,
+           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """T new tokens (q, k, v [B,H,T,d], bf16): each joins the state in order and
+    reads it (inclusive); returns y float32 [B,H,T,d] and updates the state."""
+    B, H, T, d, m = _shapes(q, W)
+    if (B, H, d, m) != (state.B, state.H, state.d, state.m):
+        raise ValueError("q/W shapes do not match the state")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, (B, H, T, d))
+    _need(W, "W", torch.bfloat16, (H, m, d))
+    if out is None:
+        out = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, H, T, d))
+    check(_lib.favor_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), state.buf.data_ptr(),
+                            out.data_ptr(), B, H, T, d, m, _stream_handle(stream)))
     return out

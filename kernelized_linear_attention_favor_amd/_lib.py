@@ -36,6 +36,10 @@ SIGNATURES = {
     "favor_attention_causal_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "favor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "favor_attention_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "favor_state_bytes": (_sz, [_i, _i, _i, _i]),
+    "favor_state_reset": (_i, [_vp, _i, _i, _i, _i, _vp]),
+    "favor_state_from_keys": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "favor_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "favor_profile_enable": (_i, []),
     "favor_profile_enable_only": (_i, [ctypes.c_char_p]),
     "favor_profile_collect": (_i, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_i),
@@ -116,6 +120,22 @@ def favor_workspace_bytes(B, H, n, d, m, causal) -> int:
 
 def favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream) -> int:
     return lib().favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream)
+
+
+def favor_state_bytes(B, H, d, m) -> int:
+    return lib().favor_state_bytes(B, H, d, m)
+
+
+def favor_state_reset(state, B, H, d, m, stream) -> int:
+    return lib().favor_state_reset(state, B, H, d, m, stream)
+
+
+def favor_state_from_keys(k, v, W, state, B, H, n, d, m, stream) -> int:
+    return lib().favor_state_from_keys(k, v, W, state, B, H, n, d, m, stream)
+
+
+def favor_decode(q, k, v, W, state, out, B, H, T, d, m, stream) -> int:
+    return lib().favor_decode(q, k, v, W, state, out, B, H, T, d, m, stream)
 
 
 def favor_profile_enable() -> int:

@@ -159,6 +159,17 @@ favor_status_t run_bf16(const void* q, const void* k, const void* v, const void*
   return ok();
 }
 
+favor_status_t check_state_shape(const float* state, int B, int H, int d, int m) {
+  if (B < 1 || H < 1 || d < 1 || m < 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (B=%d H=%d d=%d m=%d)", B, H, d, m);
+  if (!state) return fail(FAVOR_ERR_INVALID_ARGUMENT, "state is null");
+  if (!aligned(state, 16)) return fail(FAVOR_ERR_UNSUPPORTED, "state is not 16-byte aligned");
+  if (!favor::bf16_supported(d, m))
+    return fail(FAVOR_ERR_UNSUPPORTED, "decode supports d = 64 and m in {64, 128, 256} (d=%d m=%d)",
+                d, m);
+  return FAVOR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,6 +303,59 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
   if (st != FAVOR_OK) return st;
   if (!ws) return fail(FAVOR_ERR_INVALID_ARGUMENT, "ws is null");
   return run_bf16(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream);
+}
+
+size_t favor_state_bytes(int B, int H, int d, int m) {
+  if (B < 1 || H < 1 || !favor::bf16_supported(d, m)) return 0;
+  return sizeof(float) * favor::state_floats(B, H, d, m);
+}
+
+
+favor_status_t favor_state_reset(float* state, int B, int H, int d, int m, hipStream_t stream) {
+  favor_status_t st = check_state_shape(state, B, H, d, m);
+  if (st != FAVOR_OK) return st;
+  hipError_t e = favor::launch_state_reset(state, B, H, d, m, stream);
+  if (e != hipSuccess) return hip_fail(e, "state reset launch");
+  return ok();
+}
+
+favor_status_t favor_state_from_keys(const void* k, const void* v, const void* W, float* state,
+                                     int B, int H, int n, int d, int m, hipStream_t stream) {
+  favor_status_t st = check_state_shape(state, B, H, d, m);
+  if (st != FAVOR_OK) return st;
+  if ((st = check_sizes(B, H, n, d, m)) != FAVOR_OK) return st;
+  const void* ps[3] = {k, v, W};
+  const char* names[3] = {"k", "v", "W"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ps[i]) return fail(FAVOR_ERR_INVALID_ARGUMENT, "%s is null", names[i]);
+    if (!aligned(ps[i], 16)) return fail(FAVOR_ERR_UNSUPPORTED, "%s is not 16-byte aligned", names[i]);
+  }
+  const favor::Bf16Plan plan = favor::bf16_plan(B, H, n, d, m, 0);
+  StreamScratch own(stream);
+  hipError_t e = own.alloc(plan.off_end);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FAVOR_ERR_OUT_OF_MEMORY, "scratch allocation of %zu bytes failed: %s", plan.off_end,
+                hipGetErrorString(e));
+  }
+  e = favor::launch_state_bf16(plan, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                               static_cast<const uint16_t*>(W), own.p, state, stream);
+  if (e != hipSuccess) return hip_fail(e, "state launch");
+  return ok();
+}
+
+favor_status_t favor_decode(const void* q, const void* k, const void* v, const void* W,
+                            float* state, float* out, int B, int H, int T, int d, int m,
+                            hipStream_t stream) {
+  favor_status_t st = check_state_shape(state, B, H, d, m);
+  if (st != FAVOR_OK) return st;
+  if ((st = check_sizes(B, H, T, d, m)) != FAVOR_OK) return st;
+  if ((st = check_ptrs(q, k, v, W, out, 16)) != FAVOR_OK) return st;
+  hipError_t e = favor::launch_decode(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(W),
+                                      state, out, B, H, T, m, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
 }
 
 favor_status_t favor_attention_f32(const float* q, const float* k, const float* v, const float* W,

@@ -487,6 +487,45 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
 }
 
 // ---------------------------------------------------------------------------
+// k_state_merge: the splits of one (b, h) merged in index order into a decode
+// state (same workgroup layout as k_merge): c_f = max_s c_fs, z_f and S_f the
+// sums rescaled to it (S in value units).  State layout: S [BH][m][64], then
+// z [BH][m], then c [BH][m].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ part_S,
+                                                     const float* __restrict__ part_zc,
+                                                     float* __restrict__ state, int BH, int m,
+                                                     int splits) {
+  const int nfb = m >> 4;
+  const int bh = blockIdx.x / nfb;
+  const int fb = blockIdx.x - bh * nfb;
+  const int t = threadIdx.x;
+  const int f = 16 * fb + (t >> 4), cq = t & 15;
+  const float* zc0 = part_zc + static_cast<size_t>(bh) * splits * 2 * m;
+  float cm = -kFInf;
+  for (int s = 0; s < splits; ++s) cm = fmaxf(cm, zc0[static_cast<size_t>(s) * 2 * m + m + f]);
+  float zt = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 4 * cq;
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) {
+    const float cs = zc0[static_cast<size_t>(s) * 2 * m + m + f];
+    const float zs = zc0[static_cast<size_t>(s) * 2 * m + f];
+    const f32x4 r = *reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
+    const float a = (cs == -kFInf) ? 0.f : exp2f(cs - cm);
+    zt = fmaf(a, zs, zt);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) acc[cc] = fmaf(a, r[cc], acc[cc]);
+  }
+  const size_t row = static_cast<size_t>(bh) * m + f;
+  *reinterpret_cast<f32x4*>(state + row * kD + 4 * cq) = acc;
+  if (cq == 0) {
+    state[static_cast<size_t>(BH) * m * kD + row] = zt;
+    state[static_cast<size_t>(BH) * m * kD + static_cast<size_t>(BH) * m + row] = cm;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_output: 4 waves; each wave handles 32 queries at a time with all m
 // features.  LDS holds W' = [W | beta parts] (A operand of the projection)
 // and yhat^T (B operand of the output product) for the workgroup's (b, h).
@@ -692,6 +731,31 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
   o = align_up(o + sizeof(float) * BH * kD, 256);
   p.off_end = o;
   return p;
+}
+
+hipError_t launch_state_bf16(const Bf16Plan& p, const uint16_t* k, const uint16_t* v,
+                            const uint16_t* W, void* ws, float* state, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  float* pS = reinterpret_cast<float*>(base + p.off_part_S);
+  float* pzc = reinterpret_cast<float*>(base + p.off_part_zc);
+  float* pvm = reinterpret_cast<float*>(base + p.off_vmax);
+  hipError_t e = hipSuccess;
+  switch (p.m) {
+    case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, pvm, s); break;
+    case 128:
+      e = kv_features_per_wave(p) == 2 ? launch_kv<2, 2>(p, k, v, W, pS, pzc, pvm, s)
+                                       : launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s);
+      break;
+    case 256:
+      e = kv_features_per_wave(p) == 2 ? launch_kv<4, 2>(p, k, v, W, pS, pzc, pvm, s)
+                                       : launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  FAVOR_LAUNCH("k_state_merge", k_state_merge, dim3(p.B * p.H * (p.m / 16)), dim3(256), 0, s, pS, pzc,
+               state, p.B * p.H, p.m, p.splits);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,

@@ -60,4 +60,13 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
                                  const uint16_t* v, const uint16_t* W, float* out, void* ws,
                                  hipStream_t s);
 
+// ---------------------------------------------------------------- decode
+// State of the keys of a non-causal plan's ranges, merged (k_kv_state + k_state_merge).
+hipError_t launch_state_bf16(const Bf16Plan& p, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* W, void* ws, float* state, hipStream_t s);
+size_t state_floats(int B, int H, int d, int m);
+hipError_t launch_state_reset(float* state, int B, int H, int d, int m, hipStream_t s);
+hipError_t launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* W,
+                         float* state, float* out, int B, int H, int T, int m, hipStream_t s);
+
 }  // namespace favor

@@ -106,3 +106,19 @@ def test_profile_filter_host_only():
     assert L.favor_profile_collect() == {}
     assert L.favor_profile_enable_only(None) == 0
     assert L.favor_profile_collect() == {}
+
+
+def test_decode_entries_host_only():
+    L = _lib()
+    assert L.favor_state_bytes(2, 3, 64, 256) == 4 * 2 * 3 * 256 * (64 + 2)
+    assert L.favor_state_bytes(1, 1, 32, 256) == 0      # d != 64
+    assert L.favor_state_bytes(1, 1, 64, 100) == 0      # m not in {64,128,256}
+    assert L.favor_state_reset(None, 1, 1, 64, 64, None) == 1
+    assert L.favor_state_reset(FAKE, 1, 1, 64, 96, None) == 2
+    assert L.favor_state_reset(FAKE, 0, 1, 64, 64, None) == 1
+    base = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.favor_decode(*base, 1, 1, 0, 64, 64, None) == 1          # T = 0
+    assert L.favor_decode(*base, 1, 1, 4, 48, 64, None) == 2          # d unsupported
+    assert L.favor_decode(None, *base[1:], 1, 1, 4, 64, 64, None) == 1
+    assert L.favor_state_from_keys(FAKE, FAKE, FAKE, None, 1, 1, 8, 64, 64, None) == 1
+    assert L.favor_state_from_keys(FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 64, 64, None) == 1
