@@ -127,6 +127,104 @@ def cpu_baseline(x, cfg, with_causal: bool, budget_s: float = 10.0) -> dict:
     }
 
 
+# ---------------------------------------------------------- streaming decode
+def decode_bytes(B: int, H: int, T: int, d: int, m: int) -> float:
+    """Algorithmic HBM bytes of one decode call: the fp32 state (S, z, c) read
+    and written once, W read once, T tokens of bf16 q, k, v in, fp32 y out."""
+    state = 4.0 * B * H * m * (d + 2)
+    return 2 * state + 2.0 * H * m * d + 3 * 2.0 * B * H * T * d + 4.0 * B * H * T * d
+
+
+def bench_decode(favor, _lib, torch, fi, cfg, t0, dev, calls: int = 256, t_long: int = 64,
+                 cpu_budget_s: float = 2.0) -> dict:
+    """Streaming decode on the workload's shape: the prompt (n keys of input set
+    0) into a state, then `calls` single-token calls and a few `t_long`-token
+    calls.  Kernel times from HIP events around each launch on its stream."""
+    B, H, n, d, m = cfg.B, cfg.H, cfg.n, cfg.d, cfg.m
+    W = t0["W"]
+    st = favor.State(B, H, d, m)
+    gen = torch.Generator(device="cpu").manual_seed(4242)
+
+    def toks(T):
+        s = (d ** -0.25)
+        return [(torch.randn((B, H, T, d), generator=gen) * sc).to(device=dev, dtype=torch.bfloat16)
+                for sc in (s, s, 1.0)]
+
+    one = [toks(1) for _ in range(calls)]
+    many = [toks(t_long) for _ in range(4)]
+    out1 = torch.empty((B, H, 1, d), dtype=torch.float32, device=dev)
+    outT = torch.empty((B, H, t_long, d), dtype=torch.float32, device=dev)
+
+    def prompt():
+        st.from_keys(t0["k"], t0["v"], W)
+
+    # warm every kernel once
+    prompt()
+    favor.decode(*one[0], W, st, out=out1)
+    favor.decode(*many[0], W, st, out=outT)
+    torch.cuda.synchronize()
+
+    _lib.check(_lib.favor_profile_enable())
+    for _ in range(3):
+        prompt()
+    torch.cuda.synchronize()
+    pp = _lib.favor_profile_collect()
+    prompt_us = sum(t / c for c, t in pp.values()) * 1e3
+
+    prompt()
+    _lib.check(_lib.favor_profile_enable_only("k_decode"))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for q, k, v in one:
+        favor.decode(q, k, v, W, st, out=out1)
+    e1.record()
+    torch.cuda.synchronize()
+    c1, tt1 = _lib.favor_profile_collect()["k_decode"]
+    us1 = tt1 / c1 * 1e3
+    wall1 = e0.elapsed_time(e1) / calls * 1e3
+
+    _lib.check(_lib.favor_profile_enable_only("k_decode"))
+    for q, k, v in many:
+        favor.decode(q, k, v, W, st, out=outT)
+    torch.cuda.synchronize()
+    cT, ttT = _lib.favor_profile_collect()["k_decode"]
+    usT = ttT / cT * 1e3
+    assert bool(torch.isfinite(outT).all()), "decode produced non-finite outputs"
+
+    b1 = decode_bytes(B, H, 1, d, m)
+    bT = decode_bytes(B, H, t_long, d, m)
+
+    # the oracle's recurrence, timed on a few whole (b, h) slices
+    import oracle  # cpu_baseline leg only
+    xs = {k: v.float().cpu().numpy() for k, v in zip("qkv", many[0])}
+    Wh = W.float().cpu().numpy()
+    slices, tc = 0, time.perf_counter()
+    while True:
+        b, h = divmod(slices % (B * H), H)
+        oracle.decode(xs["q"][b, h], xs["k"][b, h], xs["v"][b, h], Wh[h])
+        slices += 1
+        if time.perf_counter() - tc >= cpu_budget_s:
+            break
+    cpu_wall = time.perf_counter() - tc
+    return {
+        "workload": f"prompt n={n} into the state, then decode B={B} H={H} d={d} m={m}",
+        "state_bytes": int(_lib.favor_state_bytes(B, H, d, m)),
+        "prompt_to_state_us": round(prompt_us, 2),
+        "T1": {"kernel_us": round(us1, 2), "wall_us_per_call": round(wall1, 2),
+               "tokens_per_s": round(B / (us1 * 1e-6), 1), "bytes_per_launch": b1,
+               "hbm_frac": round(b1 / (us1 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        f"T{t_long}": {"kernel_us": round(usT, 2), "tokens_per_s": round(B * t_long / (usT * 1e-6), 1),
+                       "bytes_per_launch": bT,
+                       "hbm_frac": round(bT / (usT * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": {"value": round(slices * t_long / H / cpu_wall, 1), "unit": "tokens/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"{slices} (b,h) slices of {t_long} tokens through the fp64 oracle's "
+                                   f"decode recurrence in {cpu_wall:.1f} s, one process"},
+    }
+
+
 # ------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -136,6 +234,7 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--noncausal-only", action="store_true", help="time only the non-causal call")
+    ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="before timing, run a plain elementwise copy (negation) of MB MiB fp32 three "
                          "times; its HBM counters calibrate the per-kernel traffic figures")
@@ -274,6 +373,13 @@ def main() -> int:
                 "tflops": round(call_flops / (us * 1e-6) / 1e12, 2),
             }
 
+    dec = None
+    if not args.no_decode:
+        print("[bench] streaming decode", file=sys.stderr, flush=True)
+        dec = bench_decode(favor, _lib, torch, fi, cfg, sets[0], dev,
+                           cpu_budget_s=0.0 if args.no_cpu_baseline else 2.0)
+        print(f"[bench] decode: {json.dumps(dec)}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -302,6 +408,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "per_call": per_call,
         "kernels": kernels,
+        "decode": dec,
         "sources": digest,
     }
     print(json.dumps(out))

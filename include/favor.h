@@ -138,9 +138,12 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
  * and z = Phi(K)^T 1 (Performer notes, Kernel Attention View and Normalization)
  * up to the factor 2^c_f / sqrt(m) per feature, which is carried (c_f) or
  * cancels in y (1/sqrt(m)).  Layout: fp32, favor_state_bytes(B,H,d,m) bytes:
- *   S [B,H,m,d], then z [B,H,m], then c [B,H,m] (log2 units).
+ *   S [B,H,m,d], then z [B,H,m], then c [B,H,m] (log2 units), then one uint32
+ *   per (b,h) that favor_decode uses as a finish counter (zero between calls;
+ *   favor_state_reset and favor_state_from_keys set it to zero).
  * The empty state is S = 0, z = 0, c = -inf.  Shapes: d == 64, m in {64,128,256}
- * (the bf16 path); q, k, v, W bf16; state and out 16-byte aligned.
+ * (the bf16 path); q, k, v, W bf16; state and out 16-byte aligned.  Calls on
+ * one state must be ordered (one stream, or events between streams).
  *
  * favor_state_bytes  -- bytes of a state (0 if the shape is not supported).
  * favor_state_reset  -- write the empty state.
@@ -151,8 +154,9 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
  *   t's key and value join the state, then y_t = phi(q_t)^T S / phi(q_t)^T z
  *   (inclusive, as in favor_attention with causal = 1) goes to out
  *   (fp32 [B,H,T,d]).  The state is updated in place; a sequence decoded in any
- *   split into calls gives the same outputs.  One workgroup per (b,h) walks its
- *   T tokens in order.
+ *   split into calls gives the same outputs, bit for bit.  Each (b,h) is walked
+ *   in token order by 64/CC workgroups, one per slice of CC value columns (CC =
+ *   8 for up to 128 heads, wider for more).
  */
 size_t favor_state_bytes(int B, int H, int d, int m);
 favor_status_t favor_state_reset(float* state, int B, int H, int d, int m, hipStream_t stream);

@@ -138,8 +138,9 @@ def attention_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch
 
 
 class State:
-    """Streaming-decode state (fp32): S [B,H,m,d], z [B,H,m], c [B,H,m] in one
-    buffer, starting empty.  The carried prefix sums of the causal path."""
+    """Streaming-decode state (fp32): S [B,H,m,d], z [B,H,m], c [B,H,m] and one
+    bookkeeping word per (b, h) in one buffer, starting empty.  The carried
+    prefix sums of the causal path."""
 
     def __init__(self, B: int, H: int, d: int, m: int, device="cuda", stream=None):
         nbytes = _lib.favor_state_bytes(B, H, d, m)
@@ -171,7 +172,7 @@ class State:
         B, H, d, m = self.B, self.H, self.d, self.m
         ns, nz = B * H * m * d, B * H * m
         return (self.buf[:ns].view(B, H, m, d), self.buf[ns:ns + nz].view(B, H, m),
-                self.buf[ns + nz:].view(B, H, m))
+                self.buf[ns + nz:ns + 2 * nz].view(B, H, m))
 
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor, state: State,

@@ -490,7 +490,8 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
 // k_state_merge: the splits of one (b, h) merged in index order into a decode
 // state (same workgroup layout as k_merge): c_f = max_s c_fs, z_f and S_f the
 // sums rescaled to it (S in value units).  State layout: S [BH][m][64], then
-// z [BH][m], then c [BH][m].
+// z [BH][m], then c [BH][m], then one zero word per (b, h) (the decode
+// kernel's finish counter).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ part_S,
                                                      const float* __restrict__ part_zc,
@@ -523,6 +524,8 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
     state[static_cast<size_t>(BH) * m * kD + row] = zt;
     state[static_cast<size_t>(BH) * m * kD + static_cast<size_t>(BH) * m + row] = cm;
   }
+  if (fb == 0 && t == 0)
+    reinterpret_cast<uint32_t*>(state + static_cast<size_t>(BH) * m * (kD + 2))[bh] = 0u;
 }
 
 // ---------------------------------------------------------------------------

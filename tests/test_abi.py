@@ -110,7 +110,7 @@ def test_profile_filter_host_only():
 
 def test_decode_entries_host_only():
     L = _lib()
-    assert L.favor_state_bytes(2, 3, 64, 256) == 4 * 2 * 3 * 256 * (64 + 2)
+    assert L.favor_state_bytes(2, 3, 64, 256) == 4 * 2 * 3 * (256 * (64 + 2) + 1)
     assert L.favor_state_bytes(1, 1, 32, 256) == 0      # d != 64
     assert L.favor_state_bytes(1, 1, 64, 100) == 0      # m not in {64,128,256}
     assert L.favor_state_reset(None, 1, 1, 64, 64, None) == 1

@@ -67,6 +67,22 @@ def test_decode_from_empty_matches_oracle(m, sizes):
     np.testing.assert_allclose(z, zref, rtol=TOL_F32)
 
 
+@pytest.mark.parametrize("B,H", [(2, 128), (4, 128), (8, 128)])
+def test_decode_wide_column_slices(B, H):
+    """Grids of many heads give each workgroup a wider column slice (16, 32 and
+    64 value columns for 256, 512 and 1024 heads); 37 tokens cross a 32-token
+    block inside one call."""
+    cfg = fi.Config("dec", B, H, 37, 64, 64, "bf16", True, 64, "iid", 800 + B)
+    x = fi.make_inputs(cfg)
+    st = favor.State(B, H, 64, 64)
+    y = decode_in_calls(x, [3, 34], st)
+    yref, Sref, zref = oracle.decode(x["q"], x["k"], x["v"], x["W"])
+    assert oracle.max_rel_err(y, yref) < TOL_F32
+    S, z = plain_state(st)
+    assert oracle.max_rel_err(S, Sref) < TOL_F32
+    np.testing.assert_allclose(z, zref, rtol=TOL_F32)
+
+
 def test_decode_splits_are_bitwise_identical():
     cfg = fi.Config("dec", 2, 2, 96, 64, 256, "bf16", True, 64, "iid", 731)
     x = fi.make_inputs(cfg)
@@ -92,6 +108,7 @@ def test_state_from_keys_then_decode(m, n):
     cfg = fi.Config("dec", 1, 2, n + T, 64, m, "bf16", True, 64, "iid", 750 + n)
     x = fi.make_inputs(cfg)
     st = favor.State(1, 2, 64, m)
+    st.buf.fill_(7.0)   # from_keys replaces every word, the finish counters included
     st.from_keys(bf(x["k"][..., :n, :]), bf(x["v"][..., :n, :]), bf(x["W"]))
     torch.cuda.synchronize()
     Sref, zref = oracle.kv_state(x["k"][..., :n, :], x["v"][..., :n, :], x["W"])
