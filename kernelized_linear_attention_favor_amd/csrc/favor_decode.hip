@@ -177,7 +177,10 @@ __global__ __launch_bounds__(M) void k_decode(const uint16_t* __restrict__ Q,
   constexpr int GB = 6 - __builtin_ctz(CC);   // lane l holds column l >> GB after the butterfly
   __shared__ __attribute__((aligned(16))) DecSmem<M, CC> sm;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int bh = blockIdx.x / NS, cs = blockIdx.x % NS, hh = bh % H;
+  // Workgroups go to the 8 XCDs round-robin by index, so with BH a multiple of
+  // 8 the NS slices of one (b, h) share an XCD and its L2: the state rows, z, c
+  // and W of the head are fetched from memory once, not once per slice.
+  const int bh = blockIdx.x % BH, cs = blockIdx.x / BH, hh = bh % H;
   const int c0 = cs * CC;
 
   // W as the MFMA B operand (16 dims x 32 features per tile, two tiles per wave)
