@@ -16,7 +16,10 @@ Sources (pages on the method):
   * "Linear Attention and the Performer" lesson (creativeworksofknowledge):
     sections The kernelization trick and Code.
   * "Performer for vision" (chipfoundryservices): How It Works (Step 1, Step 2),
-    Kernel Choices.
+    Kernel Choices, What Is Performer?.
+  * "How do linear attention variants (Performer, Linformer) achieve O(n)
+    complexity" (zenaique quiz page): the comparison table and the list of
+    uses (the Linear Transformer's elu(x)+1 feature map).
 
 Readings taken where the pages are silent (all stated again in the design notes):
   * phi(x) = exp(W x - |x|^2/2) / sqrt(m) with the same W for queries and keys
@@ -25,6 +28,10 @@ Readings taken where the pages are silent (all stated again in the design notes)
   * The library applies no 1/sqrt(d) temperature; inputs carry it.
   * Causal attention is inclusive: token i aggregates keys j <= i.
   * d_v = d; the denominator has no epsilon.
+  * Deterministic feature maps (kind argument): "relu" is phi(x) = max(W x, 0)
+    / sqrt(m) with the same random W; "elu1" is phi(x) = elu(x) + 1 applied to
+    x itself (m = d, no W).  ReLU features can all be zero for a query; its
+    row then has no weight at all and y is defined as 0.
 """
 from __future__ import annotations
 
@@ -34,8 +41,10 @@ import numpy as np
 
 __all__ = [
     "feature_map", "kv_state", "attention", "attention_causal", "decode", "attention_quadratic",
-    "attention_quadratic_rows", "softmax_attention", "max_rel_err",
+    "attention_quadratic_rows", "softmax_attention", "max_rel_err", "PHI_KINDS",
 ]
+
+PHI_KINDS = ("exp", "relu", "elu1")
 
 
 def _f64(a) -> np.ndarray:
@@ -54,52 +63,72 @@ def _heads_W(W: np.ndarray, X: np.ndarray) -> np.ndarray:
     raise ValueError("W must be [m,d] or [H,m,d]")
 
 
-def feature_map(X, W) -> np.ndarray:
-    """Positive random features phi(x) = exp(W x - |x|^2 / 2) / sqrt(m).
+def feature_map(X, W, kind: str = "exp") -> np.ndarray:
+    """Feature map phi, applied to each row x of X.  Returns [..., n, m].
 
-    Performer notes, section FAVOR+ (positive features whose inner product
-    estimates exp(q.k)); Performer for vision, Kernel Choices (exp of Gaussian
-    projections keeps features positive).  Returns [..., n, m].
+    kind "exp": positive random features phi(x) = exp(W x - |x|^2 / 2) / sqrt(m).
+      Performer notes, section FAVOR+ (positive features whose inner product
+      estimates exp(q.k)); Performer for vision, Kernel Choices (exp of
+      Gaussian projections keeps features positive).
+    kind "relu": phi(x) = max(W x, 0) / sqrt(m).  Performer for vision, What Is
+      Performer? (ReLU features) and Kernel Choices (random projections).
+    kind "elu1": phi(x) = elu(x) + 1 = (x + 1 if x > 0 else exp(x)), each
+      coordinate of x itself, so m = d and W is not used.  Quiz page on linear
+      attention variants: the Linear Transformer's elu+1 feature map.
     """
     X = _f64(X)
+    if kind == "elu1":
+        return np.where(X > 0, X + 1.0, np.exp(np.minimum(X, 0.0)))
     W = _heads_W(W, X)
     m = W.shape[-2]
     if W.ndim == 2:
         proj = X @ W.T                                   # [..., n, m]
     else:
         proj = X @ np.swapaxes(W, -1, -2)               # [..., H, n, d] @ [H, d, m]
+    if kind == "relu":
+        return np.maximum(proj, 0.0) / math.sqrt(m)
+    if kind != "exp":
+        raise ValueError(f"unknown feature map {kind!r}")
     half_sq = 0.5 * np.sum(X * X, axis=-1, keepdims=True)
     return np.exp(proj - half_sq) / math.sqrt(m)
 
 
-def kv_state(K, V, W):
+def _ratio(num, den):
+    """num / den, with rows whose total weight den is 0 set to 0 (only ReLU
+    features can give a query no weight at all)."""
+    den = np.asarray(den)
+    safe = np.where(den > 0, den, 1.0)
+    return np.where(den > 0, num / safe, 0.0)
+
+
+def kv_state(K, V, W, kind: str = "exp"):
     """S = Phi(K)^T V ([..., m, d]) and z = Phi(K)^T 1 ([..., m]).
 
     Performer notes, Kernel Attention View (the key/value summary S computed
     once) and Normalization (the summed key features in the denominator).
     """
-    phiK = feature_map(K, W)
+    phiK = feature_map(K, W, kind)
     V = _f64(V)
     S = np.swapaxes(phiK, -1, -2) @ V
     z = np.sum(phiK, axis=-2)
     return S, z
 
 
-def attention(Q, K, V, W) -> np.ndarray:
+def attention(Q, K, V, W, kind: str = "exp") -> np.ndarray:
     """Non-causal FAVOR+ attention y_i = phi(q_i)^T S / phi(q_i)^T z.
 
     Performer notes, Normalization (associative form of the normalised
     output); lesson "Linear Attention and the Performer", Code (numerator
     phi(Q)(phi(K)^T V), denominator phi(Q)(phi(K)^T 1), output their ratio).
     """
-    S, z = kv_state(K, V, W)
-    phiQ = feature_map(Q, W)
+    S, z = kv_state(K, V, W, kind)
+    phiQ = feature_map(Q, W, kind)
     num = phiQ @ S
     den = phiQ @ z[..., :, None]
-    return num / den
+    return _ratio(num, den)
 
 
-def attention_causal(Q, K, V, W, block: int = 256) -> np.ndarray:
+def attention_causal(Q, K, V, W, block: int = 256, kind: str = "exp") -> np.ndarray:
     """Causal FAVOR+ attention by running prefix sums over tokens.
 
     Performer for vision, How It Works, Step 2 (prefix sums so each token sees
@@ -111,8 +140,8 @@ def attention_causal(Q, K, V, W, block: int = 256) -> np.ndarray:
     the last running value carries into the next block.
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
-    phiQ = feature_map(Q, W)
-    phiK = feature_map(K, W)
+    phiQ = feature_map(Q, W, kind)
+    phiK = feature_map(K, W, kind)
     n = Q.shape[-2]
     lead = Q.shape[:-2]
     m = phiQ.shape[-1]
@@ -128,13 +157,13 @@ def attention_causal(Q, K, V, W, block: int = 256) -> np.ndarray:
         pq = phiQ[..., s:e, :]
         num = np.einsum("...bm,...bmd->...bd", pq, Srun)
         den = np.einsum("...bm,...bm->...b", pq, zrun)
-        Y[..., s:e, :] = num / den[..., None]
+        Y[..., s:e, :] = _ratio(num, den[..., None])
         S = Srun[..., -1, :, :]
         z = zrun[..., -1, :]
     return Y
 
 
-def decode(Q, K, V, W, S0=None, z0=None):
+def decode(Q, K, V, W, S0=None, z0=None, kind: str = "exp"):
     """Streaming (token-by-token) causal FAVOR+: the prefix sums carried as a
     state and updated one token at a time.
 
@@ -147,8 +176,8 @@ def decode(Q, K, V, W, S0=None, z0=None):
     (unshifted) one of kv_state.
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
-    phiQ = feature_map(Q, W)
-    phiK = feature_map(K, W)
+    phiQ = feature_map(Q, W, kind)
+    phiK = feature_map(K, W, kind)
     lead = Q.shape[:-2]
     T, d = Q.shape[-2], V.shape[-1]
     m = phiQ.shape[-1]
@@ -160,28 +189,28 @@ def decode(Q, K, V, W, S0=None, z0=None):
         z = z + phiK[..., t, :]
         num = np.einsum("...m,...md->...d", phiQ[..., t, :], S)
         den = np.einsum("...m,...m->...", phiQ[..., t, :], z)
-        Y[..., t, :] = num / den[..., None]
+        Y[..., t, :] = _ratio(num, den[..., None])
     return Y, S, z
 
 
-def attention_quadratic(Q, K, V, W, causal: bool = False) -> np.ndarray:
+def attention_quadratic(Q, K, V, W, causal: bool = False, kind: str = "exp") -> np.ndarray:
     """Explicit quadratic form y = (A V) / (A 1) with A = Phi(Q) Phi(K)^T.
 
     Performer notes, Normalization (the ratio of sums over keys before
     reassociation) and Kernel Attention View (the n x n order that FAVOR+
     avoids).  causal=True keeps A_ij only for j <= i.  Small n only.
     """
-    phiQ = feature_map(Q, W)
-    phiK = feature_map(K, W)
+    phiQ = feature_map(Q, W, kind)
+    phiK = feature_map(K, W, kind)
     A = phiQ @ np.swapaxes(phiK, -1, -2)
     if causal:
         n = A.shape[-1]
         A = A * np.tril(np.ones((n, n)))
     V = _f64(V)
-    return (A @ V) / np.sum(A, axis=-1, keepdims=True)
+    return _ratio(A @ V, np.sum(A, axis=-1, keepdims=True))
 
 
-def attention_quadratic_rows(Q, K, V, W, rows, causal: bool) -> np.ndarray:
+def attention_quadratic_rows(Q, K, V, W, rows, causal: bool, kind: str = "exp") -> np.ndarray:
     """Rows `rows` of the explicit quadratic form for one (batch, head) slice.
 
     Q, K, V are [n, d] and W is [m, d].  For each requested row i the weights
@@ -191,13 +220,13 @@ def attention_quadratic_rows(Q, K, V, W, rows, causal: bool) -> np.ndarray:
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     rows = np.asarray(rows, dtype=np.int64)
-    phiq = feature_map(Q[rows], W)                      # [r, m]
-    phiK = feature_map(K, W)                            # [n, m]
+    phiq = feature_map(Q[rows], W, kind)                # [r, m]
+    phiK = feature_map(K, W, kind)                      # [n, m]
     out = np.empty((len(rows), V.shape[-1]))
     for t, i in enumerate(rows):
         hi = i + 1 if causal else K.shape[0]
         a = phiK[:hi] @ phiq[t]
-        out[t] = (a @ V[:hi]) / np.sum(a)
+        out[t] = _ratio(a @ V[:hi], np.sum(a))
     return out
 
 
