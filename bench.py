@@ -225,6 +225,65 @@ def bench_decode(favor, _lib, torch, fi, cfg, t0, dev, calls: int = 256, t_long:
     }
 
 
+# ---------------------------------------------------- deterministic feature maps
+def bench_phi(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s: float) -> dict:
+    """The ReLU (m = 256) and elu(x)+1 (m = d) feature maps on the workload's
+    shape: non-causal and causal calls, per-kernel HIP-event times, and the
+    oracle timed on whole (b, h) slices beside them."""
+    B, H, n, d = cfg.B, cfg.H, cfg.n, cfg.d
+    res = {}
+    for kind, m in (("relu", cfg.m), ("elu1", d)):
+        W = sets[0]["W"] if kind == "relu" else None
+        entry = {"m": m}
+        for causal in (False, True):
+            ws = favor.Workspace(B, H, n, d, m, causal=causal, phi=kind)
+            out = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+
+            def call(i):
+                t = sets[i % len(sets)]
+                favor.attention(t["q"], t["k"], t["v"], W, causal=causal, out=out, workspace=ws, phi=kind)
+
+            for i in range(3):
+                call(i)
+            torch.cuda.synchronize()
+            _lib.check(_lib.favor_profile_enable())
+            for i in range(steps):
+                call(i)
+            torch.cuda.synchronize()
+            prof = _lib.favor_profile_collect()
+            kernels = {k: round(t / c * 1e3, 2) for k, (c, t) in prof.items()}
+            us = sum(kernels.values())
+            call_bytes = 10.0 * B * H * n * d + (2.0 * H * m * d if kind == "relu" else 0.0)
+            dom = max(kernels, key=kernels.get)
+            entry["causal" if causal else "noncausal"] = {
+                "kernel_us": round(us, 2),
+                "tokens_per_s": round(B * n / (us * 1e-6), 1),
+                "hbm_frac": round(call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes_per_call": call_bytes,
+                "dominant": dom,
+                "kernels_us": kernels,
+            }
+            assert bool(torch.isfinite(out).all()), f"{kind} attention produced non-finite outputs"
+        if cpu_budget_s > 0:
+            import oracle  # cpu_baseline leg only
+            x = {k: sets[0][k][0, 0].float().cpu().numpy() for k in ("q", "k", "v")}
+            Wh = sets[0]["W"][0].float().cpu().numpy() if kind == "relu" else None
+            slices, t0 = 0, time.perf_counter()
+            while True:
+                oracle.attention(x["q"], x["k"], x["v"], Wh, kind=kind)
+                oracle.attention_causal(x["q"], x["k"], x["v"], Wh, kind=kind)
+                slices += 1
+                if time.perf_counter() - t0 >= cpu_budget_s:
+                    break
+            wall = time.perf_counter() - t0
+            entry["cpu_baseline"] = {
+                "value": round(slices * n / H / wall, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{slices} whole (b,h) slice(s) of n={n} through the fp64 oracle's non-causal and "
+                          f"causal {kind} attention in {wall:.1f} s, one process"}
+        res[kind] = entry
+    return res
+
+
 # ------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -235,6 +294,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--noncausal-only", action="store_true", help="time only the non-causal call")
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
+    ap.add_argument("--no-phi", action="store_true", help="skip the ReLU / elu+1 feature-map measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="before timing, run a plain elementwise copy (negation) of MB MiB fp32 three "
                          "times; its HBM counters calibrate the per-kernel traffic figures")
@@ -380,6 +440,13 @@ def main() -> int:
                            cpu_budget_s=0.0 if args.no_cpu_baseline else 2.0)
         print(f"[bench] decode: {json.dumps(dec)}", file=sys.stderr, flush=True)
 
+    phi = None
+    if not args.no_phi:
+        print("[bench] deterministic feature maps", file=sys.stderr, flush=True)
+        phi = bench_phi(favor, _lib, torch, cfg, sets, dev, steps=20,
+                        cpu_budget_s=0.0 if args.no_cpu_baseline else 1.0)
+        print(f"[bench] feature maps: {json.dumps(phi)}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -409,6 +476,7 @@ def main() -> int:
         "per_call": per_call,
         "kernels": kernels,
         "decode": dec,
+        "feature_maps": phi,
         "sources": digest,
     }
     print(json.dumps(out))

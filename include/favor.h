@@ -128,6 +128,31 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Deterministic feature maps on the same state / output / causal structure
+ * (Performer for vision, What Is Performer? and Kernel Choices: ReLU features of
+ * the random projections; quiz page on linear attention variants, comparison
+ * table: the Linear Transformer's elu(x)+1):
+ *   FAVOR_PHI_EXP   phi(x) = exp(W x - |x|^2/2) / sqrt(m)   (favor_attention)
+ *   FAVOR_PHI_RELU  phi(x) = max(W x, 0) / sqrt(m), W [H,m,d] bf16, m in {64,128,256}
+ *   FAVOR_PHI_ELU1  phi(x) = elu(x) + 1 on x itself: m must equal d; W is not read
+ *                   (may be NULL)
+ * y_i = phi(q_i)^T S / phi(q_i)^T z, non-causal or causal (j <= i) as for
+ * favor_attention; a query whose features are all zero (possible only with
+ * ReLU) gets y_i = 0.  bf16 q, k, v [B,H,n,d] with d = 64, fp32 out.
+ *
+ * favor_workspace_bytes_phi -- scratch bytes favor_attention_phi needs for a
+ *   shape (0 if unsupported).
+ * favor_attention_phi -- ws / ws_bytes as for favor_attention_ws, or ws = NULL
+ *   for scratch allocated stream-ordered on `stream`.  An unknown phi is
+ *   FAVOR_ERR_INVALID_ARGUMENT; FAVOR_PHI_EXP forwards to favor_attention(_ws).
+ */
+typedef enum { FAVOR_PHI_EXP = 0, FAVOR_PHI_RELU = 1, FAVOR_PHI_ELU1 = 2 } favor_phi_t;
+size_t favor_workspace_bytes_phi(int B, int H, int n, int d, int m, int causal, int phi);
+favor_status_t favor_attention_phi(const void* q, const void* k, const void* v, const void* W,
+                                   float* out, int B, int H, int n, int d, int m, int causal, int phi,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Streaming decode -- the causal prefix sums carried from call to call
  * (Performer for vision, How It Works, Step 2: each token adds its key
  * features and value to running sums S, z and reads them with its query).

@@ -76,22 +76,38 @@ def workspace_bytes(B: int, H: int, n: int, d: int, m: int, causal: bool = False
     return _lib.favor_workspace_bytes(B, H, n, d, m, int(bool(causal)))
 
 
+PHI = {"exp": _lib.FAVOR_PHI_EXP, "relu": _lib.FAVOR_PHI_RELU, "elu1": _lib.FAVOR_PHI_ELU1}
+
+
+def _phi_code(phi: str) -> int:
+    if phi not in PHI:
+        raise ValueError(f"phi must be one of {sorted(PHI)} (got {phi!r})")
+    return PHI[phi]
+
+
 class Workspace:
-    """Caller-owned scratch for the bf16 attention path (zero-filled once)."""
+    """Caller-owned scratch for the bf16 attention path (zero-filled once), for
+    one feature map phi ("exp" FAVOR+, "relu", "elu1")."""
 
     def __init__(self, B: int, H: int, n: int, d: int, m: int, causal: bool = False,
-                 device="cuda"):
-        nbytes = workspace_bytes(B, H, n, d, m, causal)
+                 device="cuda", phi: str = "exp"):
+        nbytes = _lib.favor_workspace_bytes_phi(B, H, n, d, m, int(bool(causal)), _phi_code(phi))
         if nbytes == 0:
             raise FavorError(_lib.FAVOR_ERR_UNSUPPORTED, "shape not supported by the bf16 path")
         self.nbytes = nbytes
+        self.phi = phi
         self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
-def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor,
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor | None,
               causal: bool = False, out: torch.Tensor | None = None,
-              workspace: Workspace | None = None, stream=None) -> torch.Tensor:
-    """FAVOR+ attention y = phi(Q) S / (phi(Q) z), float32 [B, H, n, d]."""
+              workspace: Workspace | None = None, stream=None, phi: str = "exp") -> torch.Tensor:
+    """Linear attention y = phi(Q) S / (phi(Q) z), float32 [B, H, n, d].
+
+    phi "exp" is FAVOR+ (bf16 or float32 inputs); "relu" (ReLU features of W)
+    and "elu1" (elu(x) + 1, m = d, W unused and may be None) take bf16 inputs."""
+    if phi != "exp":
+        return _attention_phi(q, k, v, W, causal, out, workspace, stream, _phi_code(phi))
     B, H, n, d, m = _shapes(q, W)
     dt = q.dtype
     if dt not in (torch.bfloat16, torch.float32):
@@ -112,6 +128,29 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor
                                       workspace.nbytes, s))
     else:
         check(_lib.favor_attention(*ptrs, B, H, n, d, m, c, s))
+    return out
+
+
+def _attention_phi(q, k, v, W, causal, out, workspace, stream, code):
+    if q.dim() != 4:
+        raise ValueError("expected q/k/v of shape [B, H, n, d]")
+    B, H, n, d = q.shape
+    if code == _lib.FAVOR_PHI_ELU1 and W is None:
+        m, wp = d, 0
+    elif W is None:
+        raise ValueError("this feature map needs W [H, m, d]")
+    else:
+        B, H, n, d, m = _shapes(q, W)
+        _need(W, "W", torch.bfloat16, (H, m, d))
+        wp = W.data_ptr()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, (B, H, n, d))
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, H, n, d))
+    ws, wsb = (workspace.buf.data_ptr(), workspace.nbytes) if workspace is not None else (None, 0)
+    check(_lib.favor_attention_phi(q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, out.data_ptr(), B, H, n, d, m,
+                                   int(bool(causal)), code, ws, wsb, _stream_handle(stream)))
     return out
 
 

@@ -19,6 +19,10 @@ FAVOR_ERR_UNSUPPORTED = 2
 FAVOR_ERR_HIP = 3
 FAVOR_ERR_OUT_OF_MEMORY = 4
 
+FAVOR_PHI_EXP = 0
+FAVOR_PHI_RELU = 1
+FAVOR_PHI_ELU1 = 2
+
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
@@ -36,6 +40,8 @@ SIGNATURES = {
     "favor_attention_causal_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "favor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "favor_attention_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "favor_workspace_bytes_phi": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "favor_attention_phi": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "favor_state_bytes": (_sz, [_i, _i, _i, _i]),
     "favor_state_reset": (_i, [_vp, _i, _i, _i, _i, _vp]),
     "favor_state_from_keys": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -120,6 +126,14 @@ def favor_workspace_bytes(B, H, n, d, m, causal) -> int:
 
 def favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream) -> int:
     return lib().favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream)
+
+
+def favor_workspace_bytes_phi(B, H, n, d, m, causal, phi) -> int:
+    return lib().favor_workspace_bytes_phi(B, H, n, d, m, causal, phi)
+
+
+def favor_attention_phi(q, k, v, W, out, B, H, n, d, m, causal, phi, ws, ws_bytes, stream) -> int:
+    return lib().favor_attention_phi(q, k, v, W, out, B, H, n, d, m, causal, phi, ws, ws_bytes, stream)
 
 
 def favor_state_bytes(B, H, d, m) -> int:

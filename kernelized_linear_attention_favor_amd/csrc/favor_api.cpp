@@ -170,6 +170,24 @@ favor_status_t check_state_shape(const float* state, int B, int H, int d, int m)
   return FAVOR_OK;
 }
 
+favor_status_t check_phi(const void* q, const void* k, const void* v, const void* W, float* out,
+                         int B, int H, int n, int d, int m, int causal, int phi) {
+  if (causal != 0 && causal != 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  if (phi != FAVOR_PHI_RELU && phi != FAVOR_PHI_ELU1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "unknown feature map %d", phi);
+  favor_status_t st = check_sizes(B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  const void* Wc = phi == FAVOR_PHI_ELU1 ? q : W;   // elu(x) + 1 takes no W
+  if ((st = check_ptrs(q, k, v, Wc, out, 16)) != FAVOR_OK) return st;
+  if (phi == FAVOR_PHI_ELU1 && (d != 64 || m != d))
+    return fail(FAVOR_ERR_UNSUPPORTED, "elu(x)+1 features need d = m = 64 (d=%d m=%d)", d, m);
+  if (phi == FAVOR_PHI_RELU && !favor::bf16_supported(d, m))
+    return fail(FAVOR_ERR_UNSUPPORTED, "ReLU features support d = 64 and m in {64, 128, 256} (d=%d m=%d)",
+                d, m);
+  return FAVOR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,6 +408,49 @@ favor_status_t favor_attention_causal_f32(const float* q, const float* k, const 
                                           int m, int chunk, hipStream_t stream) {
   if (chunk < 0) return fail(FAVOR_ERR_INVALID_ARGUMENT, "chunk must be >= 0 (got %d)", chunk);
   return favor_attention_f32(q, k, v, W, out, B, H, n, d, m, 1, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t favor_workspace_bytes_phi(int B, int H, int n, int d, int m, int causal, int phi) {
+  if (phi == FAVOR_PHI_EXP) return favor_workspace_bytes(B, H, n, d, m, causal);
+  if (B < 1 || H < 1 || n < 1 || d != 64 || (causal != 0 && causal != 1)) return 0;
+  if (phi == FAVOR_PHI_ELU1 && m != d) return 0;
+  if (phi == FAVOR_PHI_RELU && !favor::bf16_supported(d, m)) return 0;
+  if (phi != FAVOR_PHI_RELU && phi != FAVOR_PHI_ELU1) return 0;
+  return favor::lin::lin_plan(B, H, n, m, phi, causal).off_end;
+}
+
+favor_status_t favor_attention_phi(const void* q, const void* k, const void* v, const void* W,
+                                   float* out, int B, int H, int n, int d, int m, int causal, int phi,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (phi == FAVOR_PHI_EXP)
+    return ws ? favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream)
+              : favor_attention(q, k, v, W, out, B, H, n, d, m, causal, stream);
+  favor_status_t st = check_phi(q, k, v, W, out, B, H, n, d, m, causal, phi);
+  if (st != FAVOR_OK) return st;
+  const favor::lin::LinPlan plan = favor::lin::lin_plan(B, H, n, m, phi, causal);
+  StreamScratch own(stream);
+  if (!ws) {
+    hipError_t e = own.alloc(plan.off_end);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(FAVOR_ERR_OUT_OF_MEMORY, "scratch allocation of %zu bytes failed: %s", plan.off_end,
+                  hipGetErrorString(e));
+    }
+    ws = own.p;
+  } else if (ws_bytes < plan.off_end) {
+    return fail(FAVOR_ERR_OUT_OF_MEMORY, "workspace has %zu bytes, needs %zu", ws_bytes, plan.off_end);
+  } else if (!aligned(ws, 256)) {
+    return fail(FAVOR_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  }
+  hipError_t e = favor::lin::launch_linear_bf16(plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                                static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(W),
+                                                out, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "feature-map attention launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -69,4 +69,19 @@ hipError_t launch_state_reset(float* state, int B, int H, int d, int m, hipStrea
 hipError_t launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* W,
                          float* state, float* out, int B, int H, int T, int m, hipStream_t s);
 
+// ------------------------------------------- deterministic feature maps
+namespace lin {
+struct LinPlan {
+  int B, H, n, m;
+  int kind;       // 1 = ReLU features of W, 2 = elu(x) + 1 (m = d)
+  int causal;
+  int splits;     // key ranges per (b,h): state splits (non-causal) or segments (causal)
+  int span;       // tokens per split / segment (multiple of 64)
+  size_t off_part_S, off_part_z, off_sop, off_z, off_end;
+};
+LinPlan lin_plan(int B, int H, int n, int m, int kind, int causal);
+hipError_t launch_linear_bf16(const LinPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const uint16_t* W, float* out, void* ws, hipStream_t s);
+}  // namespace lin
+
 }  // namespace favor

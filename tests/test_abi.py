@@ -122,3 +122,29 @@ def test_decode_entries_host_only():
     assert L.favor_decode(None, *base[1:], 1, 1, 4, 64, 64, None) == 1
     assert L.favor_state_from_keys(FAKE, FAKE, FAKE, None, 1, 1, 8, 64, 64, None) == 1
     assert L.favor_state_from_keys(FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 64, 64, None) == 1
+
+
+def test_feature_map_kinds_host_only():
+    L = _lib()
+    # scratch sizes: the exp map forwards to the FAVOR+ path; ReLU and elu+1 have their own plan
+    assert L.favor_workspace_bytes_phi(4, 8, 16384, 64, 256, 0, 0) == L.favor_workspace_bytes(4, 8, 16384, 64, 256, 0)
+    for causal in (0, 1):
+        assert L.favor_workspace_bytes_phi(4, 8, 16384, 64, 256, causal, 1) > 0
+        assert L.favor_workspace_bytes_phi(4, 8, 16384, 64, 64, causal, 2) > 0
+    assert L.favor_workspace_bytes_phi(1, 1, 64, 64, 128, 0, 2) == 0     # elu+1 needs m = d
+    assert L.favor_workspace_bytes_phi(1, 1, 64, 32, 32, 0, 2) == 0      # d must be 64
+    assert L.favor_workspace_bytes_phi(1, 1, 64, 64, 100, 0, 1) == 0     # m unsupported
+    assert L.favor_workspace_bytes_phi(1, 1, 64, 64, 64, 0, 3) == 0      # unknown map
+    assert L.favor_workspace_bytes_phi(1, 1, 64, 64, 64, 2, 1) == 0      # causal not 0/1
+    F = FAKE
+    args = lambda W, m, causal, phi: (F, F, F, W, F, 1, 2, 64, 64, m, causal, phi, None, 0, None)
+    assert L.favor_attention_phi(*args(F, 64, 0, 3)) == L.FAVOR_ERR_INVALID_ARGUMENT
+    assert L.favor_attention_phi(*args(F, 64, 0, -1)) == L.FAVOR_ERR_INVALID_ARGUMENT
+    assert L.favor_attention_phi(*args(F, 64, 2, 1)) == L.FAVOR_ERR_INVALID_ARGUMENT
+    assert L.favor_attention_phi(*args(None, 64, 0, 1)) == L.FAVOR_ERR_INVALID_ARGUMENT   # ReLU needs W
+    assert L.favor_attention_phi(*args(F, 128, 0, 2)) == L.FAVOR_ERR_UNSUPPORTED          # elu+1: m = d
+    assert L.favor_attention_phi(*args(F, 96, 0, 1)) == L.FAVOR_ERR_UNSUPPORTED
+    assert L.favor_attention_phi(F + 8, F, F, F, F, 1, 2, 64, 64, 64, 0, 1, None, 0, None) == L.FAVOR_ERR_UNSUPPORTED
+    assert "feature map" in L.last_error() or "aligned" in L.last_error()
+    # an undersized workspace is refused before any launch
+    assert L.favor_attention_phi(F, F, F, F, F, 1, 2, 64, 64, 64, 0, 1, F, 16, None) == L.FAVOR_ERR_OUT_OF_MEMORY
