@@ -186,13 +186,14 @@ __global__ __launch_bounds__(128) void k_lin_merge(const float* __restrict__ par
   const int bh = blockIdx.x / kbs, kb = blockIdx.x % kbs;
   const int t = threadIdx.x, dt = t >> 6, lane = t & 63, h = lane >> 5;
   const int c = 32 * dt + (lane & 31);
-  float v[8];
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* P0 = part_S + static_cast<size_t>(bh) * splits * M * kD + c;
+  // splits in index order; the loads of 8 splits are issued before their adds
+#pragma unroll 8
+  for (int sp = 0; sp < splits; ++sp) {
+    const float* P = P0 + static_cast<size_t>(sp) * M * kD;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int f = 16 * kb + 8 * (s >> 2) + 4 * h + (s & 3);
-    float a = 0.f;
-    for (int sp = 0; sp < splits; ++sp) a += part_S[((static_cast<size_t>(bh) * splits + sp) * M + f) * kD + c];
-    v[s] = a;
+    for (int s = 0; s < 8; ++s) v[s] += P[(16 * kb + 8 * (s >> 2) + 4 * h + (s & 3)) * kD];
   }
   u32x4 hi, lo;
   split8(v, 0, hi, lo);
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(512) void k_lin_output(const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) u32x4 shi[KBS][2][64];
   __shared__ __attribute__((aligned(16))) u32x4 slo[KBS][2][64];
   __shared__ __attribute__((aligned(16))) uint16_t wl[KIND == kRelu ? M * kD : 8];
-  __shared__ float zl[M];
+  __shared__ __attribute__((aligned(16))) float zl[M];
   __shared__ float dl[NWV][32];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5;
   const int bh = blockIdx.x / qblocks, qb = blockIdx.x % qblocks, hh = bh % H;
@@ -266,9 +267,14 @@ __global__ __launch_bounds__(512) void k_lin_output(const uint16_t* __restrict__
       }
       float ph[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        ph[i] = phi_of<KIND>(pr[i]);
-        den = fmaf(ph[i], zl[32 * ft + drow(i, lane)], den);
+      for (int j = 0; j < 4; ++j) {
+        // registers 4j .. 4j+3 hold features 8j + 4h .. +3: one 16-byte read of z
+        const f32x4 zz = *reinterpret_cast<const f32x4*>(&zl[32 * ft + 8 * j + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ph[4 * j + e] = phi_of<KIND>(pr[4 * j + e]);
+          den = fmaf(ph[4 * j + e], zz[e], den);
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -284,18 +290,20 @@ __global__ __launch_bounds__(512) void k_lin_output(const uint16_t* __restrict__
       }
     }
     den = pair_sum(den);   // the two lane halves hold complementary features of one query
-    if (lane < 32) dl[wave][lane] = den;
+    if (lane < 32) dl[wave][lane] = den > 0.f ? 1.f / den : 0.f;   // y = 0 for a query without weight
     __builtin_amdgcn_wave_barrier();
+    float* orow = out + (rowbase + 32 * tile + 4 * h) * kD + (lane & 31);
+    const bool full = 32 * tile + 32 <= n;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = drow(i, lane), r = 32 * tile + q;
-        if (r < n) {
-          const float dq = dl[wave][q];
-          out[(rowbase + r) * kD + 32 * dt + (lane & 31)] = dq > 0.f ? num[dt][i] / dq : 0.f;
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int q = drow(i, lane);
+      const float rq = dl[wave][q];
+      if (full || 32 * tile + q < n) {
+        const int o = (8 * (i >> 2) + (i & 3)) * kD;
+        orow[o] = num[0][i] * rq;
+        orow[o + 32] = num[1][i] * rq;
       }
+    }
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -321,9 +329,10 @@ __global__ __launch_bounds__(2 * M) void k_lin_causal(const uint16_t* __restrict
   constexpr int NW = M / 32, NT = 2 * M;
   constexpr int VPT = (256 + NT - 1) / NT;   // 16-byte chunks of the 32 x 64 V tile per thread
   __shared__ __attribute__((aligned(16))) uint16_t vt[2][32 * 64];
-  __shared__ __attribute__((aligned(16))) float part[NW][32][kD];
+  constexpr int PLD = kD + 4;   // padded partial rows: the two lane halves' rows (4 apart) use different banks
+  __shared__ __attribute__((aligned(16))) float part[NW][32][PLD];
   __shared__ float dpart[NW][32];
-  __shared__ float zl[NW][32];
+  __shared__ __attribute__((aligned(16))) float zl[NW][32];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5;
   const int bh = blockIdx.x / segs, sg = blockIdx.x % segs, hh = bh % H;
   const int t0 = sg * span, t1 = min(n, t0 + span);
@@ -442,7 +451,11 @@ __global__ __launch_bounds__(2 * M) void k_lin_causal(const uint16_t* __restrict
       }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) den = fmaf(phq[i], zl[wave][drow(i, lane)], den);
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 zz = *reinterpret_cast<const f32x4*>(&zl[wave][8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) den = fmaf(phq[4 * j + e], zz[e], den);
+    }
     den = pair_sum(den);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -468,16 +481,28 @@ __global__ __launch_bounds__(2 * M) void k_lin_causal(const uint16_t* __restrict
     if (lane < 32) zl[wave][lane] += zs;
     if (c0 + 32 < t1) stage_v(par ^ 1);
     __syncthreads();
-    for (int o = t; o < 32 * kD; o += NT) {
-      const int q = o >> 6, c = o & 63, r = c0 + q;
+    {
+      // thread -> one query and CPQ consecutive columns: the waves' shares summed
+      // in wave order, one reciprocal per query
+      constexpr int CPQ = 32 * kD / NT;
+      const int q = t / (kD / CPQ), cb = (t % (kD / CPQ)) * CPQ, r = c0 + q;
       if (r < t1) {
-        float nsum = 0.f, dsum = 0.f;
+        float dsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          nsum += part[w][q][c];
-          dsum += dpart[w][q];
+        for (int w = 0; w < NW; ++w) dsum += dpart[w][q];
+        const float rq = dsum > 0.f ? 1.f / dsum : 0.f;   // y = 0 for a query without weight
+#pragma unroll
+        for (int j = 0; j < CPQ / 4; ++j) {
+          f32x4 acc4 = *reinterpret_cast<const f32x4*>(&part[0][q][cb + 4 * j]);
+#pragma unroll
+          for (int w = 1; w < NW; ++w) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&part[w][q][cb + 4 * j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc4[e] += p4[e];
+          }
+          *reinterpret_cast<f32x4*>(out + (rowbase + r) * kD + cb + 4 * j) =
+              f32x4{acc4[0] * rq, acc4[1] * rq, acc4[2] * rq, acc4[3] * rq};
         }
-        out[(rowbase + r) * kD + c] = dsum > 0.f ? nsum / dsum : 0.f;
       }
     }
     __syncthreads();
@@ -486,8 +511,12 @@ __global__ __launch_bounds__(2 * M) void k_lin_causal(const uint16_t* __restrict
 
 }  // namespace
 
-int lin_splits(int BH, int n) {
-  int s = (256 + BH - 1) / BH;
+// Key ranges per (b, h): about one workgroup per CU at m >= 128 (4 or 8 waves
+// each), two at m = 64 (2 waves each; its 16 KB range states keep the causal
+// carry reads small).
+int lin_splits(int BH, int n, int m) {
+  const int target = m >= 128 ? 256 : 512;
+  int s = (target + BH - 1) / BH;
   const int tiles = (n + 63) / 64;
   if (s > tiles) s = tiles;
   return s < 1 ? 1 : s;
@@ -502,7 +531,7 @@ LinPlan lin_plan(int B, int H, int n, int m, int kind, int causal) {
   p.kind = kind;
   p.causal = causal;
   const int BH = B * H;
-  int s = lin_splits(BH, n);
+  int s = lin_splits(BH, n, m);
   p.span = ((n + s - 1) / s + 63) / 64 * 64;
   p.splits = (n + p.span - 1) / p.span;
   size_t off = 0;
