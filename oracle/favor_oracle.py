@@ -42,6 +42,7 @@ import numpy as np
 __all__ = [
     "feature_map", "kv_state", "attention", "attention_causal", "decode", "attention_quadratic",
     "attention_quadratic_rows", "softmax_attention", "max_rel_err", "PHI_KINDS",
+    "philox4x64_10", "draw_normals", "draw_features",
 ]
 
 PHI_KINDS = ("exp", "relu", "elu1")
@@ -267,3 +268,83 @@ def max_rel_err(y, y_ref) -> float:
     with np.errstate(invalid="ignore", divide="ignore"):
         r = a / b
     return float(np.max(r)) if r.size else 0.0
+
+
+# ---------------------------------------------------------------------------
+# Orthogonal random features drawn from a counter-based generator.
+#
+# Performer for vision, Kernel Choices (orthogonal features: QR of random
+# projection matrices lowers the variance) and Performer notes, FAVOR+ (the
+# random directions w_f).  The random numbers come from Philox4x64-10 (Salmon,
+# Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", 2011),
+# written here from its published definition, and Box-Muller normals.
+# ---------------------------------------------------------------------------
+_PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)
+_PHILOX_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)
+_U64 = (1 << 64) - 1
+
+
+def philox4x64_10(counter, key):
+    """One Philox4x64 block with 10 rounds: four 64-bit words from a 256-bit
+    counter and a 128-bit key (Python integers).  Each round multiplies words 0
+    and 2 by the two constants, mixes the high halves with words 1 and 3 and the
+    key, and the key is bumped by the two Weyl constants after every round."""
+    c = [int(x) & _U64 for x in counter]
+    k = [int(x) & _U64 for x in key]
+    for _ in range(10):
+        p0 = _PHILOX_M[0] * c[0]
+        p1 = _PHILOX_M[1] * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k[0], p1 & _U64, (p0 >> 64) ^ c[3] ^ k[1], p0 & _U64]
+        k = [(k[0] + _PHILOX_W[0]) & _U64, (k[1] + _PHILOX_W[1]) & _U64]
+    return c
+
+
+def _unit(w: int) -> float:
+    """Top 53 bits of a word as a uniform number in (0, 1) (never 0 or 1)."""
+    return ((w >> 11) + 0.5) * (2.0 ** -53)
+
+
+def draw_normals(seed: int, step: int, head: int, block: int, kind: int, count: int) -> np.ndarray:
+    """Standard normals #0 .. count-1 of the stream (head, block, kind).
+
+    Normal j comes from the Philox block with counter (j // 4, block, head,
+    kind) and key (seed, step): its words (w0, w1) and (w2, w3) give two
+    Box-Muller pairs r cos(2 pi u2), r sin(2 pi u2) with r = sqrt(-2 ln u1), in
+    the order w0w1-cos, w0w1-sin, w2w3-cos, w2w3-sin.
+    """
+    out = np.empty(count)
+    for i in range((count + 3) // 4):
+        w = philox4x64_10((i, block, head, kind), (seed, step))
+        z = []
+        for a, b in ((w[0], w[1]), (w[2], w[3])):
+            r = math.sqrt(-2.0 * math.log(_unit(a)))
+            t = 2.0 * math.pi * _unit(b)
+            z += [r * math.cos(t), r * math.sin(t)]
+        for e in range(4):
+            if 4 * i + e < count:
+                out[4 * i + e] = z[e]
+    return out
+
+
+def draw_features(seed: int, step: int, H: int, m: int, d: int) -> np.ndarray:
+    """W [H, m, d] of orthogonal random features for key (seed, step).
+
+    For each head and block b = 0 .. ceil(m/d)-1: G[r][c] = normal r*d + c of
+    stream kind 0; G = Q R with R's diagonal positive (the QR that makes Q
+    unique and Haar distributed); row b*d + i of W (for the rows below m) is
+    s_i Q[:, i], where s_i = |g_i| and g_i holds normals i*d .. i*d + d-1 of
+    stream kind 1 (a chi(d) length, the norm of an independent Gaussian
+    vector).  A new step gives an independent draw (the per-call redraw).
+    """
+    nb = (m + d - 1) // d
+    W = np.empty((H, m, d))
+    for h in range(H):
+        for b in range(nb):
+            G = draw_normals(seed, step, h, b, 0, d * d).reshape(d, d)
+            Q, R = np.linalg.qr(G)
+            Q = Q * np.sign(np.diag(R))[None, :]
+            g = draw_normals(seed, step, h, b, 1, d * d).reshape(d, d)
+            rows = min(d, m - b * d)
+            for i in range(rows):
+                W[h, b * d + i] = np.linalg.norm(g[i]) * Q[:, i]
+    return W
