@@ -153,6 +153,29 @@ favor_status_t favor_attention_phi(const void* q, const void* k, const void* v, 
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Orthogonal random features drawn on the device (Performer for vision, Kernel
+ * Choices: orthogonal features by QR of random projection matrices; Performer
+ * notes, FAVOR+).  Writes W [H, m, d] (bf16 or fp32, row-major) for the key
+ * (seed, step): a new step gives an independent draw (redraw per call or per
+ * training step), the same key the same W, bit for bit.
+ *
+ * Definition (an oracle reproduces it from this text): Philox4x64-10 with key
+ * (seed, step) and counter (i, block, head, kind) gives 4 words; words (0, 1)
+ * and (2, 3) each give a Box-Muller pair (r cos t, r sin t), r = sqrt(-2 ln u1),
+ * t = 2 pi u2, u = ((word >> 11) + 0.5) * 2^-53: normals 4i .. 4i+3 of stream
+ * (head, block, kind).  For each head and block b < ceil(m/d): G[r][c] = normal
+ * r*d + c of kind 0; G = Q R with R's diagonal positive; row b*d + j of W (if
+ * below m) is |g_j| Q[:, j], g_j = normals j*d .. j*d + d-1 of kind 1.  Computed
+ * in fp64; the fp32 or bf16 output is the fp64 value rounded once to the nearest
+ * representable value (ties to even).
+ *
+ * d in {16, 32, 64} (else FAVOR_ERR_UNSUPPORTED); W 4-byte aligned, caller-owned.
+ */
+typedef enum { FAVOR_OUT_BF16 = 0, FAVOR_OUT_F32 = 1 } favor_out_t;
+favor_status_t favor_draw_features(unsigned long long seed, unsigned long long step, void* W, int out_dtype,
+                                   int H, int m, int d, hipStream_t stream);
+
+/*
  * Streaming decode -- the causal prefix sums carried from call to call
  * (Performer for vision, How It Works, Step 2: each token adds its key
  * features and value to running sums S, z and reads them with its query).

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import FavorError, check  # noqa: F401
 
 __all__ = ["feature_map", "attention", "attention_causal", "Workspace", "FavorError",
-           "workspace_bytes", "version", "State", "decode"]
+           "workspace_bytes", "version", "State", "decode", "draw_features", "PHI"]
 
 
 def version() -> int:
@@ -173,6 +173,21 @@ def attention_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch
         check(_lib.favor_attention_causal(*ptrs, B, H, n, d, m, chunk, s))
     else:
         raise TypeError("q must be bfloat16 or float32")
+    return out
+
+
+def draw_features(seed: int, step: int, H: int, m: int, d: int, dtype=torch.bfloat16,
+                  out: torch.Tensor | None = None, device="cuda", stream=None) -> torch.Tensor:
+    """Orthogonal random features W [H, m, d] drawn on the device for the key
+    (seed, step) (bfloat16 or float32): a new step is an independent redraw."""
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((H, m, d), dtype=dtype, device=device)
+    _need(out, "out", dtype, (H, m, d))
+    code = _lib.FAVOR_OUT_F32 if dtype == torch.float32 else _lib.FAVOR_OUT_BF16
+    check(_lib.favor_draw_features(int(seed) & (2**64 - 1), int(step) & (2**64 - 1), out.data_ptr(), code,
+                                   H, m, d, _stream_handle(stream)))
     return out
 
 

@@ -23,6 +23,9 @@ FAVOR_PHI_EXP = 0
 FAVOR_PHI_RELU = 1
 FAVOR_PHI_ELU1 = 2
 
+FAVOR_OUT_BF16 = 0
+FAVOR_OUT_F32 = 1
+
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
@@ -42,6 +45,7 @@ SIGNATURES = {
     "favor_attention_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "favor_workspace_bytes_phi": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "favor_attention_phi": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "favor_draw_features": (_i, [ctypes.c_ulonglong, ctypes.c_ulonglong, _vp, _i, _i, _i, _i, _vp]),
     "favor_state_bytes": (_sz, [_i, _i, _i, _i]),
     "favor_state_reset": (_i, [_vp, _i, _i, _i, _i, _vp]),
     "favor_state_from_keys": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -134,6 +138,10 @@ def favor_workspace_bytes_phi(B, H, n, d, m, causal, phi) -> int:
 
 def favor_attention_phi(q, k, v, W, out, B, H, n, d, m, causal, phi, ws, ws_bytes, stream) -> int:
     return lib().favor_attention_phi(q, k, v, W, out, B, H, n, d, m, causal, phi, ws, ws_bytes, stream)
+
+
+def favor_draw_features(seed, step, W, out_dtype, H, m, d, stream) -> int:
+    return lib().favor_draw_features(seed, step, W, out_dtype, H, m, d, stream)
 
 
 def favor_state_bytes(B, H, d, m) -> int:

@@ -454,3 +454,23 @@ favor_status_t favor_attention_phi(const void* q, const void* k, const void* v, 
 }
 
 }  // extern "C"
+
+extern "C" {
+
+favor_status_t favor_draw_features(unsigned long long seed, unsigned long long step, void* W, int out_dtype,
+                                   int H, int m, int d, hipStream_t stream) {
+  if (H < 1 || m < 1 || d < 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (H=%d m=%d d=%d)", H, m, d);
+  if (!W) return fail(FAVOR_ERR_INVALID_ARGUMENT, "W is null");
+  if (out_dtype != FAVOR_OUT_BF16 && out_dtype != FAVOR_OUT_F32)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "out_dtype must be FAVOR_OUT_BF16 or FAVOR_OUT_F32 (got %d)", out_dtype);
+  if (!favor::draw::draw_supported(d)) return fail(FAVOR_ERR_UNSUPPORTED, "d must be 16, 32 or 64 (got %d)", d);
+  if (!aligned(W, 4)) return fail(FAVOR_ERR_UNSUPPORTED, "W is not 4-byte aligned");
+  if (static_cast<long long>(H) * ((m + d - 1) / d) > (1LL << 30))
+    return fail(FAVOR_ERR_UNSUPPORTED, "too many blocks (H=%d m=%d)", H, m);
+  hipError_t e = favor::draw::launch_draw_features(seed, step, W, out_dtype == FAVOR_OUT_F32, H, m, d, stream);
+  if (e != hipSuccess) return hip_fail(e, "feature draw launch");
+  return ok();
+}
+
+}  // extern "C"

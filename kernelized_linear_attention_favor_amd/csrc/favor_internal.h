@@ -84,4 +84,11 @@ hipError_t launch_linear_bf16(const LinPlan& p, const uint16_t* q, const uint16_
                               const uint16_t* W, float* out, void* ws, hipStream_t s);
 }  // namespace lin
 
+// --------------------------------------------------- random feature draws
+namespace draw {
+bool draw_supported(int d);
+hipError_t launch_draw_features(uint64_t seed, uint64_t step, void* W, int out_f32, int H, int m, int d,
+                                hipStream_t s);
+}  // namespace draw
+
 }  // namespace favor

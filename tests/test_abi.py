@@ -148,3 +148,15 @@ def test_feature_map_kinds_host_only():
     assert "feature map" in L.last_error() or "aligned" in L.last_error()
     # an undersized workspace is refused before any launch
     assert L.favor_attention_phi(F, F, F, F, F, 1, 2, 64, 64, 64, 0, 1, F, 16, None) == L.FAVOR_ERR_OUT_OF_MEMORY
+
+
+def test_draw_features_host_only():
+    L = _lib()
+    F = FAKE
+    assert L.favor_draw_features(1, 0, None, 0, 8, 256, 64, None) == L.FAVOR_ERR_INVALID_ARGUMENT
+    assert L.favor_draw_features(1, 0, F, 2, 8, 256, 64, None) == L.FAVOR_ERR_INVALID_ARGUMENT
+    assert L.favor_draw_features(1, 0, F, 0, 0, 256, 64, None) == L.FAVOR_ERR_INVALID_ARGUMENT
+    assert L.favor_draw_features(1, 0, F, 0, 8, 0, 64, None) == L.FAVOR_ERR_INVALID_ARGUMENT
+    assert L.favor_draw_features(1, 0, F, 1, 8, 256, 48, None) == L.FAVOR_ERR_UNSUPPORTED
+    assert L.favor_draw_features(1, 0, F + 2, 0, 8, 256, 64, None) == L.FAVOR_ERR_UNSUPPORTED
+    assert "aligned" in L.last_error()
