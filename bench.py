@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+FP64_PEAK_TFLOPS = 78.6         # MI355X fp64 vector, published
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 CSRC = os.path.join(ROOT, "kernelized_linear_attention_favor_amd", "csrc")
 
@@ -284,6 +285,43 @@ def bench_phi(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s: floa
     return res
 
 
+# ---------------------------------------------------- random feature draws
+def bench_draw(favor, _lib, torch, cfg, steps: int, cpu_budget_s: float) -> dict:
+    """W [H, m, d] drawn on the device (a per-call or per-step redraw), timed
+    with HIP events around each launch; the oracle's draw of the same W beside."""
+    H, m, d = cfg.H, cfg.m, cfg.d
+    W = torch.empty((H, m, d), dtype=torch.bfloat16, device="cuda")
+    for i in range(3):
+        favor.draw_features(1, i, H, m, d, out=W)
+    torch.cuda.synchronize()
+    _lib.check(_lib.favor_profile_enable())
+    for i in range(steps):
+        favor.draw_features(1, 100 + i, H, m, d, out=W)
+    torch.cuda.synchronize()
+    c, t = _lib.favor_profile_collect()["k_draw_features"]
+    us = t / c * 1e3
+    nb = (m + d - 1) // d
+    # fp64 work per block: d*d*2 normals (Philox + Box-Muller, counted as 40 flops each)
+    # and modified Gram-Schmidt (2 d^3)
+    flops = H * nb * (2 * d * d * 40 + 2 * d ** 3)
+    out = {"workload": f"H={H} m={m} d={d}, bf16 out", "kernel_us": round(us, 2),
+           "fp64_gflop": round(flops / 1e9, 4),
+           "fp64_frac": round(flops / (us * 1e-6) / 1e12 / FP64_PEAK_TFLOPS, 5)}
+    if cpu_budget_s > 0:
+        import oracle  # cpu_baseline leg only
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.draw_features(1, n, H, m, d)
+            n += 1
+            if time.perf_counter() - t0 >= cpu_budget_s:
+                break
+        wall = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(wall / n * 1e6, 1), "unit": "us per draw", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} draws of W [{H},{m},{d}] by the fp64 oracle in {wall:.1f} s"}
+    return out
+
+
 # ------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -295,6 +333,7 @@ def main() -> int:
     ap.add_argument("--noncausal-only", action="store_true", help="time only the non-causal call")
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     ap.add_argument("--no-phi", action="store_true", help="skip the ReLU / elu+1 feature-map measurement")
+    ap.add_argument("--no-draw", action="store_true", help="skip the on-device feature draw measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="before timing, run a plain elementwise copy (negation) of MB MiB fp32 three "
                          "times; its HBM counters calibrate the per-kernel traffic figures")
@@ -447,6 +486,12 @@ def main() -> int:
                         cpu_budget_s=0.0 if args.no_cpu_baseline else 1.0)
         print(f"[bench] feature maps: {json.dumps(phi)}", file=sys.stderr, flush=True)
 
+    draw = None
+    if not args.no_draw:
+        print("[bench] feature draw", file=sys.stderr, flush=True)
+        draw = bench_draw(favor, _lib, torch, cfg, steps=20, cpu_budget_s=0.0 if args.no_cpu_baseline else 1.0)
+        print(f"[bench] feature draw: {json.dumps(draw)}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -477,6 +522,7 @@ def main() -> int:
         "kernels": kernels,
         "decode": dec,
         "feature_maps": phi,
+        "feature_draw": draw,
         "sources": digest,
     }
     print(json.dumps(out))

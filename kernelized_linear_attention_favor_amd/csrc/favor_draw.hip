@@ -8,8 +8,9 @@
 // of a stream gives normals 4i .. 4i+3 by two Box-Muller pairs (words 0-1, then
 // 2-3; cos then sin), each word mapped to (0, 1) by its top 53 bits.
 //
-// Per head and block b of d rows (one workgroup, thread j = column j):
-//   G[r][c] = normal r*d + c of stream kind 0  ->  LDS  ->  column j in registers;
+// Per head and block b of d rows (one workgroup; column j held by 4 threads,
+// a quarter of its rows each, their partial sums combined by lane shuffles):
+//   G[r][c] = normal r*d + c of stream kind 0  ->  LDS  ->  columns in registers;
 //   modified Gram-Schmidt in fp64 (R's diagonal comes out positive, the QR that
 //   makes Q unique): q_k is published through LDS, every later column removes
 //   its component;
@@ -52,21 +53,29 @@ __device__ __forceinline__ double unit(uint64_t w) {
   return (static_cast<double>(w >> 11) + 0.5) * 0x1p-53;
 }
 
-// Normals 4i .. 4i+3 of stream (head, block, kind) into dst[0..3].
+// Normals 4i .. 4i+3 of stream (head, block, kind) into dst[0..3].  The angle
+// 2 pi u goes through sincospi(2u): the same cosine and sine, without reducing
+// a multiple of pi.
 __device__ __forceinline__ void normals4(uint64_t seed, uint64_t step, int head, int block, int kind,
                                          uint64_t i, double* dst) {
   uint64_t c0 = i, c1 = static_cast<uint64_t>(block), c2 = static_cast<uint64_t>(head),
            c3 = static_cast<uint64_t>(kind);
   philox4x64_10(c0, c1, c2, c3, seed, step);
-  const double two_pi = 2.0 * 3.14159265358979323846;
+  double sn, cs;
   double r = sqrt(-2.0 * log(unit(c0)));
-  double t = two_pi * unit(c1);
-  dst[0] = r * cos(t);
-  dst[1] = r * sin(t);
+  sincospi(2.0 * unit(c1), &sn, &cs);
+  dst[0] = r * cs;
+  dst[1] = r * sn;
   r = sqrt(-2.0 * log(unit(c2)));
-  t = two_pi * unit(c3);
-  dst[2] = r * cos(t);
-  dst[3] = r * sin(t);
+  sincospi(2.0 * unit(c3), &sn, &cs);
+  dst[2] = r * cs;
+  dst[3] = r * sn;
+}
+
+// Sum over the 4 lanes 4j .. 4j+3 (the threads of one column), returned to all four.
+__device__ __forceinline__ double quad_sum(double x) {
+  x += __shfl_xor(x, 1);
+  return x + __shfl_xor(x, 2);
 }
 
 // fp64 -> fp32 rounded to odd: truncate toward zero and, if anything was
@@ -81,61 +90,65 @@ __device__ __forceinline__ float round_to_odd_f32(double x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void k_draw_features(uint64_t seed, uint64_t step, void* __restrict__ W,
-                                                      int out_f32, int m, int nblocks) {
+__global__ __launch_bounds__(256) void k_draw_features(uint64_t seed, uint64_t step, void* __restrict__ W,
+                                                       int out_f32, int m, int nblocks) {
+  constexpr int RPT = D / 4;   // rows of a column per thread
   __shared__ double buf[D * D];
   __shared__ double qk[2][D];
-  const int j = threadIdx.x;
+  const int t = threadIdx.x, j = t >> 2, p = t & 3;   // column j, row quarter p
+  const bool col = j < D;
   const int h = blockIdx.x / nblocks, b = blockIdx.x % nblocks;
   const int rows = min(D, m - b * D);
 
-  for (int i = j; i < D * D / 4; i += 64) normals4(seed, step, h, b, 0, static_cast<uint64_t>(i), &buf[4 * i]);
+  for (int i = t; i < D * D / 4; i += 256) normals4(seed, step, h, b, 0, static_cast<uint64_t>(i), &buf[4 * i]);
   __syncthreads();
-  double a[D];
+  double a[RPT];
 #pragma unroll
-  for (int r = 0; r < D; ++r) a[r] = j < D ? buf[r * D + j] : 0.0;
+  for (int r = 0; r < RPT; ++r) a[r] = col ? buf[(RPT * p + r) * D + j] : 0.0;
   __syncthreads();
-  for (int i = j; i < D * D / 4; i += 64) normals4(seed, step, h, b, 1, static_cast<uint64_t>(i), &buf[4 * i]);
+  for (int i = t; i < D * D / 4; i += 256) normals4(seed, step, h, b, 1, static_cast<uint64_t>(i), &buf[4 * i]);
   __syncthreads();
   double s = 0.0;
-  if (j < D) {
+  if (col) {
 #pragma unroll
-    for (int c = 0; c < D; ++c) s = fma(buf[j * D + c], buf[j * D + c], s);
-    s = sqrt(s);
+    for (int c = 0; c < RPT; ++c) s = fma(buf[j * D + RPT * p + c], buf[j * D + RPT * p + c], s);
   }
+  s = sqrt(quad_sum(s));
 
   for (int k = 0; k < D; ++k) {
-    if (j == k) {
-      double nn = 0.0;
+    double nn = 0.0;
 #pragma unroll
-      for (int r = 0; r < D; ++r) nn = fma(a[r], a[r], nn);
+    for (int r = 0; r < RPT; ++r) nn = fma(a[r], a[r], nn);
+    nn = quad_sum(nn);   // all lanes take part in the shuffles
+    if (j == k) {
       const double rkk = sqrt(nn);
 #pragma unroll
-      for (int r = 0; r < D; ++r) {
+      for (int r = 0; r < RPT; ++r) {
         a[r] /= rkk;
-        qk[k & 1][r] = a[r];
+        qk[k & 1][RPT * p + r] = a[r];
       }
     }
     __syncthreads();   // q_k published; q_{k-1}'s readers are done with it
-    if (j > k && j < D) {
-      double dot = 0.0;
+    double dot = 0.0;
 #pragma unroll
-      for (int r = 0; r < D; ++r) dot = fma(qk[k & 1][r], a[r], dot);
+    for (int r = 0; r < RPT; ++r) dot = fma(qk[k & 1][RPT * p + r], a[r], dot);
+    dot = quad_sum(dot);
+    if (col && j > k) {
 #pragma unroll
-      for (int r = 0; r < D; ++r) a[r] = fma(-dot, qk[k & 1][r], a[r]);
+      for (int r = 0; r < RPT; ++r) a[r] = fma(-dot, qk[k & 1][RPT * p + r], a[r]);
     }
   }
 
   if (j < rows) {
     const size_t row = static_cast<size_t>(h) * m + b * D + j;
     if (out_f32) {
-      float* o = static_cast<float*>(W) + row * D;
+      float* o = static_cast<float*>(W) + row * D + RPT * p;
 #pragma unroll
-      for (int c = 0; c < D; ++c) o[c] = static_cast<float>(s * a[c]);
+      for (int c = 0; c < RPT; ++c) o[c] = static_cast<float>(s * a[c]);
     } else {
-      uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(W) + row * D);
+      uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(W) + row * D + RPT * p);
 #pragma unroll
-      for (int c = 0; c < D; c += 2)
+      for (int c = 0; c < RPT; c += 2)
         o[c / 2] = pack_bf16(round_to_odd_f32(s * a[c]), round_to_odd_f32(s * a[c + 1]));
     }
   }
@@ -151,17 +164,17 @@ hipError_t launch_draw_features(uint64_t seed, uint64_t step, void* W, int out_f
   switch (d) {
     case 16: {
       auto k = k_draw_features<16>;
-      FAVOR_LAUNCH("k_draw_features", k, dim3(H * nb), dim3(64), 0, s, seed, step, W, out_f32, m, nb);
+      FAVOR_LAUNCH("k_draw_features", k, dim3(H * nb), dim3(256), 0, s, seed, step, W, out_f32, m, nb);
       break;
     }
     case 32: {
       auto k = k_draw_features<32>;
-      FAVOR_LAUNCH("k_draw_features", k, dim3(H * nb), dim3(64), 0, s, seed, step, W, out_f32, m, nb);
+      FAVOR_LAUNCH("k_draw_features", k, dim3(H * nb), dim3(256), 0, s, seed, step, W, out_f32, m, nb);
       break;
     }
     case 64: {
       auto k = k_draw_features<64>;
-      FAVOR_LAUNCH("k_draw_features", k, dim3(H * nb), dim3(64), 0, s, seed, step, W, out_f32, m, nb);
+      FAVOR_LAUNCH("k_draw_features", k, dim3(H * nb), dim3(256), 0, s, seed, step, W, out_f32, m, nb);
       break;
     }
     default: return hipErrorInvalidValue;
