@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "feature_map", "kv_state", "attention", "attention_causal", "decode", "attention_quadratic",
     "attention_quadratic_rows", "softmax_attention", "max_rel_err", "PHI_KINDS",
-    "philox4x64_10", "draw_normals", "draw_features",
+    "philox4x64_10", "draw_normals", "draw_features", "attention_backward", "attention_backward_rows",
 ]
 
 PHI_KINDS = ("exp", "relu", "elu1")
@@ -348,3 +348,93 @@ def draw_features(seed: int, step: int, H: int, m: int, d: int) -> np.ndarray:
             for i in range(rows):
                 W[h, b * d + i] = np.linalg.norm(g[i]) * Q[:, i]
     return W
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: dQ, dK, dV of y = phi(Q) S / phi(Q) z (non-causal) or of its
+# prefix-sum form (causal), for an upstream gradient dY.
+#
+# The pages mention training and gradients but print no formulas; these are
+# derived from the forward definitions above by the chain rule.  With
+# a_i = phi(q_i), b_j = phi(k_j), den_i = a_i . z_i and y_i = a_i^T S_i / den_i
+# (S_i, z_i: sums over the keys query i sees):
+#   da_i = (S_i dy_i - z_i (dy_i . y_i)) / den_i
+#   R_j  = sum over queries i that see key j of a_i dy_i^T / den_i     (m x d)
+#   rho_j = sum over the same i of a_i (dy_i . y_i) / den_i            (m)
+#   db_j = R_j v_j - rho_j,    dv_j = R_j^T b_j
+# and through phi_f(x) = exp(w_f . x - |x|^2/2) / sqrt(m), whose derivative is
+# phi_f(x) (w_f - x):  dx = W^T (phi(x) * dphi) - x (phi(x) . dphi).
+# ---------------------------------------------------------------------------
+def attention_backward(Q, K, V, W, dY, causal: bool = False):
+    """(dQ, dK, dV) for upstream gradient dY, FAVOR+ features, fp64.
+
+    Causal sums run over j <= i (the inclusive reading).  Plain loops over
+    tokens in the causal case; small n only.
+    """
+    Q, K, V, dY = _f64(Q), _f64(K), _f64(V), _f64(dY)
+    Wh = _heads_W(W, Q)
+    A = feature_map(Q, W)                                  # [..., n, m]
+    Bk = feature_map(K, W)
+    n = Q.shape[-2]
+    if causal:
+        mask = np.tril(np.ones((n, n)))
+    else:
+        mask = np.ones((n, n))
+    P = (A @ np.swapaxes(Bk, -1, -2)) * mask              # P_ij = a_i . b_j over visible keys
+    den = np.sum(P, axis=-1)                               # [..., n]
+    Y = (P @ V) / den[..., None]
+    delta = np.sum(dY * Y, axis=-1)                        # dy_i . y_i
+    # dP_ij = dy_i . (v_j - y_i) / den_i on visible pairs
+    dP = ((dY @ np.swapaxes(V, -1, -2)) - delta[..., None]) / den[..., None] * mask
+    dA = dP @ Bk                                           # [..., n, m]
+    dB = np.swapaxes(dP, -1, -2) @ A
+    dV = np.swapaxes(P / den[..., None], -1, -2) @ dY
+
+    def through_phi(X, F, dF):
+        g = F * dF                                         # phi * dphi, [..., n, m]
+        if Wh.ndim == 2:
+            WtG = g @ Wh
+        else:
+            WtG = g @ Wh                                   # [..., H, n, m] @ [H, m, d]
+        return WtG - X * np.sum(g, axis=-1, keepdims=True)
+
+    return through_phi(Q, A, dA), through_phi(K, Bk, dB), dV
+
+
+def attention_backward_rows(Q, K, V, W, dY, qrows, krows, causal: bool):
+    """Rows of (dQ, dK, dV) for one (batch, head) slice (Q, K, V, dY [n, d],
+    W [m, d]): dQ at query rows `qrows`, dK and dV at key rows `krows`, each
+    from the same definitions as attention_backward with the sums over tokens
+    taken directly (O(n m d) per row), so it serves as a sampled check at any n.
+    """
+    Q, K, V, dY = _f64(Q), _f64(K), _f64(V), _f64(dY)
+    W = _f64(W)
+    n = Q.shape[0]
+    A = feature_map(Q, W)                                  # [n, m]
+    Bk = feature_map(K, W)
+    if causal:
+        S = np.cumsum(Bk[:, :, None] * V[:, None, :], axis=0)    # S_i over j <= i, [n, m, d]
+        z = np.cumsum(Bk, axis=0)
+    else:
+        S = np.broadcast_to(Bk.T @ V, (n,) + (Bk.shape[1], V.shape[1]))
+        z = np.broadcast_to(np.sum(Bk, axis=0), Bk.shape)
+    den = np.einsum("im,im->i", A, z)
+    Y = np.einsum("im,imd->id", A, S) / den[:, None]
+    delta = np.sum(dY * Y, axis=-1)
+    dQ = np.empty((len(qrows), Q.shape[1]))
+    for t, i in enumerate(qrows):
+        da = (S[i] @ dY[i] - z[i] * delta[i]) / den[i]
+        g = A[i] * da
+        dQ[t] = W.T @ g - Q[i] * np.sum(g)
+    dK = np.empty((len(krows), K.shape[1]))
+    dV = np.empty((len(krows), V.shape[1]))
+    for t, j in enumerate(krows):
+        seen = np.arange(j, n) if causal else np.arange(n)
+        coef = A[seen] / den[seen, None]                   # a_i / den_i over the queries that see key j
+        R = coef.T @ dY[seen]                              # [m, d]
+        rho = coef.T @ delta[seen]
+        db = R @ V[j] - rho
+        g = Bk[j] * db
+        dK[t] = W.T @ g - K[j] * np.sum(g)
+        dV[t] = R.T @ Bk[j]
+    return dQ, dK, dV
