@@ -176,6 +176,26 @@ favor_status_t favor_draw_features(unsigned long long seed, unsigned long long s
                                    int H, int m, int d, hipStream_t stream);
 
 /*
+ * Backward pass (training): gradients dq, dk, dv of a scalar loss L for its
+ * upstream gradient dy = dL/dy, y = favor_attention(q, k, v, W, causal = 0).
+ * The pages mention training and gradients but print no formulas; these follow
+ * from the forward (Performer notes, Kernel Attention View, Normalization and
+ * FAVOR+) by the chain rule, with dphi_f(x)/dx = phi_f(x) (w_f - x).  W is a
+ * fixed random draw and gets no gradient.
+ *
+ * Inputs: q, k, v bf16 [B,H,n,d], W bf16 [H,m,d], y (the forward output) and
+ * dy fp32 [B,H,n,d].  Outputs dq, dk, dv fp32 [B,H,n,d] (caller-owned, fully
+ * written).  d = 64, m in {64,128,256}; every pointer 16-byte aligned.  ws /
+ * ws_bytes as for favor_attention_ws (ws = NULL: scratch allocated stream-
+ * ordered on `stream`).  causal = 1 returns FAVOR_ERR_UNSUPPORTED (not built).
+ * Bit-for-bit reproducible for a fixed shape.
+ */
+size_t favor_backward_workspace_bytes(int B, int H, int n, int d, int m, int causal);
+favor_status_t favor_attention_backward(const void* q, const void* k, const void* v, const void* W, const float* y,
+                                        const float* dy, float* dq, float* dk, float* dv, int B, int H, int n, int d,
+                                        int m, int causal, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Streaming decode -- the causal prefix sums carried from call to call
  * (Performer for vision, How It Works, Step 2: each token adds its key
  * features and value to running sums S, z and reads them with its query).

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import FavorError, check  # noqa: F401
 
 __all__ = ["feature_map", "attention", "attention_causal", "Workspace", "FavorError",
-           "workspace_bytes", "version", "State", "decode", "draw_features", "PHI"]
+           "workspace_bytes", "version", "State", "decode", "draw_features", "PHI", "attention_backward"]
 
 
 def version() -> int:
@@ -173,6 +173,29 @@ def attention_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch
         check(_lib.favor_attention_causal(*ptrs, B, H, n, d, m, chunk, s))
     else:
         raise TypeError("q must be bfloat16 or float32")
+    return out
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor, y: torch.Tensor,
+                       dy: torch.Tensor, causal: bool = False, out=None, workspace: torch.Tensor | None = None,
+                       stream=None):
+    """Gradients (dq, dk, dv), float32 [B, H, n, d], of FAVOR+ attention for the
+    upstream gradient dy, given the forward output y (bf16 q, k, v, W)."""
+    B, H, n, d, m = _shapes(q, W)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, (B, H, n, d))
+    _need(W, "W", torch.bfloat16, (H, m, d))
+    _need(y, "y", torch.float32, (B, H, n, d))
+    _need(dy, "dy", torch.float32, (B, H, n, d))
+    if out is None:
+        out = tuple(torch.empty((B, H, n, d), dtype=torch.float32, device=q.device) for _ in range(3))
+    for t, name in zip(out, ("dq", "dk", "dv")):
+        _need(t, name, torch.float32, (B, H, n, d))
+    ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if workspace is not None \
+        else (None, 0)
+    check(_lib.favor_attention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), y.data_ptr(),
+                                        dy.data_ptr(), out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                                        B, H, n, d, m, int(bool(causal)), ws, wsb, _stream_handle(stream)))
     return out
 
 

@@ -46,6 +46,9 @@ SIGNATURES = {
     "favor_workspace_bytes_phi": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "favor_attention_phi": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "favor_draw_features": (_i, [ctypes.c_ulonglong, ctypes.c_ulonglong, _vp, _i, _i, _i, _i, _vp]),
+    "favor_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "favor_attention_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                      _vp, _sz, _vp]),
     "favor_state_bytes": (_sz, [_i, _i, _i, _i]),
     "favor_state_reset": (_i, [_vp, _i, _i, _i, _i, _vp]),
     "favor_state_from_keys": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -142,6 +145,15 @@ def favor_attention_phi(q, k, v, W, out, B, H, n, d, m, causal, phi, ws, ws_byte
 
 def favor_draw_features(seed, step, W, out_dtype, H, m, d, stream) -> int:
     return lib().favor_draw_features(seed, step, W, out_dtype, H, m, d, stream)
+
+
+def favor_backward_workspace_bytes(B, H, n, d, m, causal) -> int:
+    return lib().favor_backward_workspace_bytes(B, H, n, d, m, causal)
+
+
+def favor_attention_backward(q, k, v, W, y, dy, dq, dk, dv, B, H, n, d, m, causal, ws, ws_bytes, stream) -> int:
+    return lib().favor_attention_backward(q, k, v, W, y, dy, dq, dk, dv, B, H, n, d, m, causal, ws, ws_bytes,
+                                          stream)
 
 
 def favor_state_bytes(B, H, d, m) -> int:

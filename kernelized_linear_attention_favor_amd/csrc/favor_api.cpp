@@ -474,3 +474,48 @@ favor_status_t favor_draw_features(unsigned long long seed, unsigned long long s
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t favor_backward_workspace_bytes(int B, int H, int n, int d, int m, int causal) {
+  if (B < 1 || H < 1 || n < 1 || causal != 0 || !favor::bf16_supported(d, m)) return 0;
+  return favor::bw::bw_plan(B, H, n, m, causal).off_end;
+}
+
+favor_status_t favor_attention_backward(const void* q, const void* k, const void* v, const void* W, const float* y,
+                                        const float* dy, float* dq, float* dk, float* dv, int B, int H, int n, int d,
+                                        int m, int causal, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (causal != 0 && causal != 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  favor_status_t st = check_bf16(q, k, v, W, dq, B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  const void* more[5] = {y, dy, dk, dv, dq};
+  const char* names[5] = {"y", "dy", "dk", "dv", "dq"};
+  for (int i = 0; i < 5; ++i) {
+    if (!more[i]) return fail(FAVOR_ERR_INVALID_ARGUMENT, "%s is null", names[i]);
+    if (!aligned(more[i], 16)) return fail(FAVOR_ERR_UNSUPPORTED, "%s is not 16-byte aligned", names[i]);
+  }
+  if (causal) return fail(FAVOR_ERR_UNSUPPORTED, "the causal backward pass is not built");
+  const favor::bw::BwPlan plan = favor::bw::bw_plan(B, H, n, m, causal);
+  StreamScratch own(stream);
+  if (!ws) {
+    hipError_t e = own.alloc(plan.off_end);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(FAVOR_ERR_OUT_OF_MEMORY, "scratch allocation of %zu bytes failed: %s", plan.off_end,
+                  hipGetErrorString(e));
+    }
+    ws = own.p;
+  } else if (ws_bytes < plan.off_end) {
+    return fail(FAVOR_ERR_OUT_OF_MEMORY, "workspace has %zu bytes, needs %zu", ws_bytes, plan.off_end);
+  } else if (!aligned(ws, 256)) {
+    return fail(FAVOR_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  }
+  hipError_t e = favor::bw::launch_backward_bf16(
+      plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(W), y, dy, dq, dk, dv, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+}  // extern "C"

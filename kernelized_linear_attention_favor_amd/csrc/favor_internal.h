@@ -91,4 +91,17 @@ hipError_t launch_draw_features(uint64_t seed, uint64_t step, void* W, int out_f
                                 hipStream_t s);
 }  // namespace draw
 
+// ------------------------------------------------------------ backward pass
+namespace bw {
+struct BwPlan {
+  int B, H, n, m, causal;
+  int splits, span;   // key / query ranges per (b,h) (multiple of 64 tokens)
+  size_t off_cpart, off_part, off_pvec, off_stiles, off_rtiles, off_z, off_rho, off_cfin, off_aux, off_end;
+};
+BwPlan bw_plan(int B, int H, int n, int m, int causal);
+hipError_t launch_backward_bf16(const BwPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* W, const float* y, const float* dy, float* dq, float* dk, float* dv,
+                                void* ws, hipStream_t s);
+}  // namespace bw
+
 }  // namespace favor

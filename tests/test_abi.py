@@ -160,3 +160,19 @@ def test_draw_features_host_only():
     assert L.favor_draw_features(1, 0, F, 1, 8, 256, 48, None) == L.FAVOR_ERR_UNSUPPORTED
     assert L.favor_draw_features(1, 0, F + 2, 0, 8, 256, 64, None) == L.FAVOR_ERR_UNSUPPORTED
     assert "aligned" in L.last_error()
+
+
+def test_backward_host_only():
+    L = _lib()
+    assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 256, 0) > 0
+    assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 100, 0) == 0
+    assert L.favor_backward_workspace_bytes(4, 8, 16384, 32, 64, 0) == 0
+    F = FAKE
+    ok = [F] * 9 + [1, 2, 64, 64, 64]
+    assert L.favor_attention_backward(*ok, 2, None, 0, None) == L.FAVOR_ERR_INVALID_ARGUMENT
+    bad_y = [F] * 4 + [None] + [F] * 4 + [1, 2, 64, 64, 64]
+    assert L.favor_attention_backward(*bad_y, 0, None, 0, None) == L.FAVOR_ERR_INVALID_ARGUMENT
+    odd = [F] * 5 + [F + 4] + [F] * 3 + [1, 2, 64, 64, 64]
+    assert L.favor_attention_backward(*odd, 0, None, 0, None) == L.FAVOR_ERR_UNSUPPORTED
+    assert L.favor_attention_backward(*([F] * 9 + [1, 2, 64, 64, 96]), 0, None, 0, None) == L.FAVOR_ERR_UNSUPPORTED
+    assert L.favor_attention_backward(*([F] * 9 + [1, 2, 64, 64, 64]), 0, F, 16, None) == L.FAVOR_ERR_OUT_OF_MEMORY

@@ -1,0 +1,131 @@
+"""GPU parity of the backward pass (dq, dk, dv) against the fp64 oracle.
+
+bf16 inputs, fp32 gradients; bar per gradient: max over (b, h) of
+max|g - g_ref| / max|g_ref| <= 2e-3 (the bf16 bar).  A single token is the
+degenerate case: y = v_0 whatever q and k are, so dq = dk = 0 exactly and dv =
+dy; there the bound is absolute.  The parity cases hand the backward the
+oracle's own forward output y, so that they measure the backward alone; one
+case runs the GPU forward first.
+"""
+import numpy as np
+import pytest
+
+import favor_inputs as fi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import kernelized_linear_attention_favor_amd as favor  # noqa: E402
+
+TOL = 2e-3
+DEV = torch.device("cuda:0")
+
+
+def gerr(g, w):
+    return oracle.max_rel_err(g, w)
+
+
+def bf(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=DEV, dtype=torch.bfloat16)
+
+
+def f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=DEV)
+
+
+def make(B, H, n, m, seed, scale=1.0):
+    x = fi.make_inputs(fi.Config("bw", B, H, n, 64, m, "bf16", False, 64, "iid", seed), qk_scale=scale)
+    rng = np.random.default_rng(seed + 1)
+    dy = rng.standard_normal(x["q"].shape).astype(np.float32)
+    return x, dy
+
+
+def gpu_backward(x, y, dy, **kw):
+    out = favor.attention_backward(bf(x["q"]), bf(x["k"]), bf(x["v"]), bf(x["W"]), f32(y), f32(dy), **kw)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+@pytest.mark.parametrize("m", [64, 128, 256])
+def test_backward_single_token(m):
+    x, dy = make(2, 2, 1, m, 299)
+    y = x["v"].astype(np.float64)
+    dq, dk, dv = gpu_backward(x, y, dy)
+    # dq and dk are exact cancellations (S dy - z delta, R v - rho): what is left is
+    # operand rounding (~2^-16) times |W| |v| |dy|, O(1) here; the bar is 2e-3 of a
+    # gradient scale of 0.5, a floor for these O(1) inputs
+    assert np.max(np.abs(dq)) < 1e-3 and np.max(np.abs(dk)) < 1e-3
+    assert np.max(np.abs(dv - dy)) < 1e-4 * np.max(np.abs(dy))   # hi + lo operands: ~2^-16 relative
+
+
+@pytest.mark.parametrize("m", [64, 128, 256])
+@pytest.mark.parametrize("n", [2, 31, 65, 1000, 2049])
+def test_backward_matches_oracle(n, m):
+    x, dy = make(1, 2, n, m, 300 + n)
+    y = oracle.attention(x["q"], x["k"], x["v"], x["W"])
+    got = gpu_backward(x, y, dy)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy)
+    for g, w, name in zip(got, want, ("dq", "dk", "dv")):
+        assert np.all(np.isfinite(g)), name
+        assert gerr(g, w) < TOL, (name, gerr(g, w))
+
+
+def test_backward_C2_shape_and_large_inputs():
+    for scale, seed in ((1.0, 2), (2.0, 3)):
+        x, dy = make(1, 8, 1024, 256, seed, scale)
+        y = oracle.attention(x["q"], x["k"], x["v"], x["W"])
+        got = gpu_backward(x, y, dy)
+        want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy)
+        for g, w in zip(got, want):
+            assert gerr(g, w) < TOL
+
+
+def test_backward_C3_shape_sampled():
+    """B=4, H=8, n=16384, m=256: the benchmark's shape; rows sampled per (b, h)."""
+    cfg = fi.config("C3")
+    x = fi.make_inputs(cfg)
+    dy = np.random.default_rng(8).standard_normal(x["q"].shape).astype(np.float32)
+    t = {k: bf(v) for k, v in x.items()}
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"])
+    dq, dk, dv = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    dq, dk, dv = (a.cpu().numpy() for a in (dq, dk, dv))
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    rng = np.random.default_rng(9)
+    for b, h in ((0, 0), (2, 3), (3, 7)):
+        rows = np.sort(np.concatenate([[0, 16383], rng.choice(16384, 6, replace=False)]))
+        rq, rk, rv = oracle.attention_backward_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["W"][h],
+                                                    dy[b, h], rows, rows, causal=False)
+        for got, want in ((dq[b, h][rows], rq), (dk[b, h][rows], rk), (dv[b, h][rows], rv)):
+            # normalised by the slice's largest gradient, as the metric does; the forward's own
+            # error (y from the GPU) is inside this bar too
+            scale = max(np.max(np.abs(want)), 1e-30)
+            assert np.max(np.abs(got - want)) / scale < 5 * TOL
+
+
+def test_backward_end_to_end_and_determinism():
+    x, dy = make(2, 4, 3000, 256, 11)
+    t = {k: bf(v) for k, v in x.items()}
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"])
+    a = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy))
+    nb = favor._lib.favor_backward_workspace_bytes(2, 4, 3000, 64, 256, 0)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    b = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy), workspace=ws)
+    torch.cuda.synchronize()
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy)
+    for g, w in zip(a, want):
+        assert gerr(g.cpu().numpy(), w) < TOL
+
+
+def test_backward_causal_not_built():
+    x, dy = make(1, 1, 64, 64, 12)
+    y = oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])
+    with pytest.raises(favor.FavorError):
+        gpu_backward(x, y, dy, causal=True)
