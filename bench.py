@@ -322,6 +322,57 @@ def bench_draw(favor, _lib, torch, cfg, steps: int, cpu_budget_s: float) -> dict
     return out
 
 
+# ------------------------------------------------------------- backward pass
+def bench_backward(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s: float) -> dict:
+    """dq, dk, dv for the workload's non-causal call: per-kernel HIP-event means
+    over `steps` backward calls (the forward output computed once, outside),
+    tokens/s and HBM fraction; the oracle's gradients on sampled rows beside."""
+    B, H, n, d, m = cfg.B, cfg.H, cfg.n, cfg.d, cfg.m
+    t = sets[0]
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"])
+    dy = torch.randn((B, H, n, d), generator=torch.Generator(device="cpu").manual_seed(5)).to(dev)
+    nb = _lib.favor_backward_workspace_bytes(B, H, n, d, m, 0)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    outs = tuple(torch.empty((B, H, n, d), dtype=torch.float32, device=dev) for _ in range(3))
+    for _ in range(3):
+        favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, dy, out=outs, workspace=ws)
+    torch.cuda.synchronize()
+    _lib.check(_lib.favor_profile_enable())
+    for _ in range(steps):
+        favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, dy, out=outs, workspace=ws)
+    torch.cuda.synchronize()
+    prof = _lib.favor_profile_collect()
+    kernels = {k: round(tt / c * 1e3, 2) for k, (c, tt) in prof.items()}
+    # launches per call: k_bw_merge runs twice
+    per_call = {k: (v * 2 if k == "k_bw_merge" else v) for k, v in kernels.items()}
+    us = sum(per_call.values())
+    # algorithmic bytes: q, k, v (bf16), y and dy (fp32) read once, dq, dk, dv (fp32) written once
+    call_bytes = 3 * 2.0 * B * H * n * d + 2 * 4.0 * B * H * n * d + 3 * 4.0 * B * H * n * d + 2.0 * H * m * d
+    assert all(bool(torch.isfinite(o).all()) for o in outs), "non-finite gradients"
+    out = {"workload": f"non-causal backward B={B} H={H} n={n} d={d} m={m}", "kernel_us": round(us, 2),
+           "tokens_per_s": round(B * n / (us * 1e-6), 1), "bytes_per_call": call_bytes,
+           "hbm_frac": round(call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "kernels_us": kernels}
+    if cpu_budget_s > 0:
+        import numpy as np
+        import oracle  # cpu_baseline leg only
+        x = {k: t[k][0, 0].float().cpu().numpy() for k in ("q", "k", "v")}
+        Wh = t["W"][0].float().cpu().numpy()
+        g = dy[0, 0].cpu().numpy()
+        rows, t0, r0 = 0, time.perf_counter(), 0
+        while True:
+            sel = np.arange(r0, r0 + 4) % n
+            oracle.attention_backward_rows(x["q"], x["k"], x["v"], Wh, g, sel, sel, causal=False)
+            rows += 4
+            r0 += 4
+            if time.perf_counter() - t0 >= cpu_budget_s:
+                break
+        wall = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(rows / H / wall, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"dq, dk, dv of {rows} rows of one (b,h) slice of n={n} through the "
+                                         f"fp64 oracle's sampled-row backward in {wall:.1f} s, one process"}
+    return out
+
+
 # ------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -334,6 +385,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     ap.add_argument("--no-phi", action="store_true", help="skip the ReLU / elu+1 feature-map measurement")
     ap.add_argument("--no-draw", action="store_true", help="skip the on-device feature draw measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="before timing, run a plain elementwise copy (negation) of MB MiB fp32 three "
                          "times; its HBM counters calibrate the per-kernel traffic figures")
@@ -492,6 +544,13 @@ def main() -> int:
         draw = bench_draw(favor, _lib, torch, cfg, steps=20, cpu_budget_s=0.0 if args.no_cpu_baseline else 1.0)
         print(f"[bench] feature draw: {json.dumps(draw)}", file=sys.stderr, flush=True)
 
+    bwd = None
+    if not args.no_backward:
+        print("[bench] backward pass", file=sys.stderr, flush=True)
+        bwd = bench_backward(favor, _lib, torch, cfg, sets, dev, steps=10,
+                             cpu_budget_s=0.0 if args.no_cpu_baseline else 2.0)
+        print(f"[bench] backward: {json.dumps(bwd)}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -523,6 +582,7 @@ def main() -> int:
         "decode": dec,
         "feature_maps": phi,
         "feature_draw": draw,
+        "backward": bwd,
         "sources": digest,
     }
     print(json.dumps(out))
