@@ -323,33 +323,33 @@ def bench_draw(favor, _lib, torch, cfg, steps: int, cpu_budget_s: float) -> dict
 
 
 # ------------------------------------------------------------- backward pass
-def bench_backward(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s: float) -> dict:
-    """dq, dk, dv for the workload's non-causal call: per-kernel HIP-event means
-    over `steps` backward calls (the forward output computed once, outside),
-    tokens/s and HBM fraction; the oracle's gradients on sampled rows beside."""
+def bench_backward(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s: float, causal: bool) -> dict:
+    """dq, dk, dv for the workload's call (non-causal or causal): per-kernel
+    HIP-event means over `steps` backward calls (the forward output computed
+    once, outside), tokens/s and HBM fraction; the oracle's gradients on sampled
+    rows beside."""
     B, H, n, d, m = cfg.B, cfg.H, cfg.n, cfg.d, cfg.m
     t = sets[0]
-    y = favor.attention(t["q"], t["k"], t["v"], t["W"])
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"], causal=causal)
     dy = torch.randn((B, H, n, d), generator=torch.Generator(device="cpu").manual_seed(5)).to(dev)
-    nb = _lib.favor_backward_workspace_bytes(B, H, n, d, m, 0)
+    nb = _lib.favor_backward_workspace_bytes(B, H, n, d, m, int(causal))
     ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
     outs = tuple(torch.empty((B, H, n, d), dtype=torch.float32, device=dev) for _ in range(3))
     for _ in range(3):
-        favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, dy, out=outs, workspace=ws)
+        favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, dy, causal=causal, out=outs, workspace=ws)
     torch.cuda.synchronize()
     _lib.check(_lib.favor_profile_enable())
     for _ in range(steps):
-        favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, dy, out=outs, workspace=ws)
+        favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, dy, causal=causal, out=outs, workspace=ws)
     torch.cuda.synchronize()
     prof = _lib.favor_profile_collect()
-    kernels = {k: round(tt / c * 1e3, 2) for k, (c, tt) in prof.items()}
-    # launches per call: k_bw_merge runs twice
-    per_call = {k: (v * 2 if k == "k_bw_merge" else v) for k, v in kernels.items()}
-    us = sum(per_call.values())
+    kernels = {k: round(tt / c * 1e3, 2) for k, (c, tt) in prof.items()}   # mean per launch
+    us = sum(tt for _, tt in prof.values()) * 1e3 / steps                    # all launches of one call
     # algorithmic bytes: q, k, v (bf16), y and dy (fp32) read once, dq, dk, dv (fp32) written once
     call_bytes = 3 * 2.0 * B * H * n * d + 2 * 4.0 * B * H * n * d + 3 * 4.0 * B * H * n * d + 2.0 * H * m * d
     assert all(bool(torch.isfinite(o).all()) for o in outs), "non-finite gradients"
-    out = {"workload": f"non-causal backward B={B} H={H} n={n} d={d} m={m}", "kernel_us": round(us, 2),
+    kind = "causal" if causal else "non-causal"
+    out = {"workload": f"{kind} backward B={B} H={H} n={n} d={d} m={m}", "kernel_us": round(us, 2),
            "tokens_per_s": round(B * n / (us * 1e-6), 1), "bytes_per_call": call_bytes,
            "hbm_frac": round(call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "kernels_us": kernels}
     if cpu_budget_s > 0:
@@ -358,18 +358,20 @@ def bench_backward(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s:
         x = {k: t[k][0, 0].float().cpu().numpy() for k in ("q", "k", "v")}
         Wh = t["W"][0].float().cpu().numpy()
         g = dy[0, 0].cpu().numpy()
+        # the causal form builds every prefix state once per call: hand it more rows per call
+        per = 64 if causal else 4
         rows, t0, r0 = 0, time.perf_counter(), 0
         while True:
-            sel = np.arange(r0, r0 + 4) % n
-            oracle.attention_backward_rows(x["q"], x["k"], x["v"], Wh, g, sel, sel, causal=False)
-            rows += 4
-            r0 += 4
+            sel = (r0 + np.arange(per) * max(1, n // per)) % n
+            oracle.attention_backward_rows(x["q"], x["k"], x["v"], Wh, g, sel, sel, causal=causal)
+            rows += per
+            r0 += 1
             if time.perf_counter() - t0 >= cpu_budget_s:
                 break
         wall = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": round(rows / H / wall, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                                "sample": f"dq, dk, dv of {rows} rows of one (b,h) slice of n={n} through the "
-                                         f"fp64 oracle's sampled-row backward in {wall:.1f} s, one process"}
+                                         f"fp64 oracle's sampled-row {kind} backward in {wall:.1f} s, one process"}
     return out
 
 
@@ -544,12 +546,15 @@ def main() -> int:
         draw = bench_draw(favor, _lib, torch, cfg, steps=20, cpu_budget_s=0.0 if args.no_cpu_baseline else 1.0)
         print(f"[bench] feature draw: {json.dumps(draw)}", file=sys.stderr, flush=True)
 
-    bwd = None
+    bwd = bwd_c = None
     if not args.no_backward:
         print("[bench] backward pass", file=sys.stderr, flush=True)
         bwd = bench_backward(favor, _lib, torch, cfg, sets, dev, steps=10,
-                             cpu_budget_s=0.0 if args.no_cpu_baseline else 2.0)
+                             cpu_budget_s=0.0 if args.no_cpu_baseline else 2.0, causal=False)
         print(f"[bench] backward: {json.dumps(bwd)}", file=sys.stderr, flush=True)
+        bwd_c = bench_backward(favor, _lib, torch, cfg, sets, dev, steps=10,
+                               cpu_budget_s=0.0 if args.no_cpu_baseline else 4.0, causal=True)
+        print(f"[bench] causal backward: {json.dumps(bwd_c)}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -583,6 +588,7 @@ def main() -> int:
         "feature_maps": phi,
         "feature_draw": draw,
         "backward": bwd,
+        "backward_causal": bwd_c,
         "sources": digest,
     }
     print(json.dumps(out))

@@ -177,7 +177,7 @@ favor_status_t favor_draw_features(unsigned long long seed, unsigned long long s
 
 /*
  * Backward pass (training): gradients dq, dk, dv of a scalar loss L for its
- * upstream gradient dy = dL/dy, y = favor_attention(q, k, v, W, causal = 0).
+ * upstream gradient dy = dL/dy, y = favor_attention(q, k, v, W, causal).
  * The pages mention training and gradients but print no formulas; these follow
  * from the forward (Performer notes, Kernel Attention View, Normalization and
  * FAVOR+) by the chain rule, with dphi_f(x)/dx = phi_f(x) (w_f - x).  W is a
@@ -187,8 +187,9 @@ favor_status_t favor_draw_features(unsigned long long seed, unsigned long long s
  * dy fp32 [B,H,n,d].  Outputs dq, dk, dv fp32 [B,H,n,d] (caller-owned, fully
  * written).  d = 64, m in {64,128,256}; every pointer 16-byte aligned.  ws /
  * ws_bytes as for favor_attention_ws (ws = NULL: scratch allocated stream-
- * ordered on `stream`).  causal = 1 returns FAVOR_ERR_UNSUPPORTED (not built).
- * Bit-for-bit reproducible for a fixed shape.
+ * ordered on `stream`).  causal = 1: query i's sums run over keys j <= i (the
+ * prefix sums of the causal forward), so key j's gradient collects queries
+ * i >= j.  Bit-for-bit reproducible for a fixed shape.
  */
 size_t favor_backward_workspace_bytes(int B, int H, int n, int d, int m, int causal);
 favor_status_t favor_attention_backward(const void* q, const void* k, const void* v, const void* W, const float* y,

@@ -478,7 +478,7 @@ favor_status_t favor_draw_features(unsigned long long seed, unsigned long long s
 extern "C" {
 
 size_t favor_backward_workspace_bytes(int B, int H, int n, int d, int m, int causal) {
-  if (B < 1 || H < 1 || n < 1 || causal != 0 || !favor::bf16_supported(d, m)) return 0;
+  if (B < 1 || H < 1 || n < 1 || (causal != 0 && causal != 1) || !favor::bf16_supported(d, m)) return 0;
   return favor::bw::bw_plan(B, H, n, m, causal).off_end;
 }
 
@@ -495,7 +495,6 @@ favor_status_t favor_attention_backward(const void* q, const void* k, const void
     if (!more[i]) return fail(FAVOR_ERR_INVALID_ARGUMENT, "%s is null", names[i]);
     if (!aligned(more[i], 16)) return fail(FAVOR_ERR_UNSUPPORTED, "%s is not 16-byte aligned", names[i]);
   }
-  if (causal) return fail(FAVOR_ERR_UNSUPPORTED, "the causal backward pass is not built");
   const favor::bw::BwPlan plan = favor::bw::bw_plan(B, H, n, m, causal);
   StreamScratch own(stream);
   if (!ws) {

@@ -72,6 +72,22 @@ __device__ __forceinline__ void split_row8(const float* p, u32x4& hi, u32x4& lo)
   split8(x, 0, hi, lo);
 }
 
+// 8 consecutive fp32 values as three bf16 words each (hi + mid + lo carries all
+// 24 bits): for the dot products dy.v that are set against delta = dy.y, where
+// the difference may cancel to zero (a query that sees one key: y = v).
+__device__ __forceinline__ void split3_row8(const float* p, u32x4& hi, u32x4& mid, u32x4& lo) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  float r[8];
+  split8(x, 0, hi, mid);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[2 * e] = x[2 * e] - bf16_lo_as_f32(hi[e]) - bf16_lo_as_f32(mid[e]);
+    r[2 * e + 1] = x[2 * e + 1] - bf16_hi_as_f32(hi[e]) - bf16_hi_as_f32(mid[e]);
+  }
+  lo = u32x4{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]), pack_bf16(r[4], r[5]), pack_bf16(r[6], r[7])};
+}
+
 // ---------------------------------------------------------------------------
 // k_bw_keys<M, PASS>: one key range of one (b, h); M/32 waves, wave w owns
 // features [32w, 32w+32).  Per 64 keys: K (and V) tiles and |k|^2 in LDS; per
@@ -225,6 +241,17 @@ __global__ __launch_bounds__(256) void k_bw_merge(const float* __restrict__ part
       cfin[static_cast<size_t>(bh) * M + r] = m;
     }
   }
+}
+
+// k_bw_cmax: the largest key exponent per (b, h, feature) over the ranges.
+__global__ __launch_bounds__(256) void k_bw_cmax(const float* __restrict__ cpart, float* __restrict__ cfin, int total,
+                                                 int M, int splits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int bh = i / M, f = i % M;
+  float m = kNegInf;
+  for (int sp = 0; sp < splits; ++sp) m = fmaxf(m, cpart[(static_cast<size_t>(bh) * splits + sp) * M + f]);
+  cfin[i] = m;
 }
 
 // Stage a (b, h)'s tiled bf16 hi / lo array, W (tiled) and two m-vectors in LDS.
@@ -562,6 +589,569 @@ __global__ __launch_bounds__(512) void k_bw_key(const uint16_t* __restrict__ K, 
   }
 }
 
+// ===========================================================================
+// Causal backward: the sums run over j <= i (S, z: prefix sums of the keys)
+// and i >= j (R, rho: suffix sums of the queries).  Both kernels walk one
+// segment of one (b, h) in chunks of 32 tokens; M/32 waves, wave w owns
+// features [32w, 32w+32).  Each wave forms its features' share of every
+// per-token quantity; the shares are summed in wave order in LDS (two barriers
+// per chunk).  The state is kept transposed where it is an A operand
+// (S^T[c][f], R^T[c][f]: lane = feature, register = value column), so the
+// value columns of dy and v are read in the MFMA register order:
+//   k-block kb of 16 columns, lane half h: columns 16kb + 4h .. +3 and 16kb + 8 + 4h .. +3.
+// ===========================================================================
+__device__ __forceinline__ void perm_f32x8(const float* row, int kb, int h, u32x4& hi, u32x4& lo) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(row + 16 * kb + 4 * h);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(row + 16 * kb + 8 + 4 * h);
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  split8(x, 0, hi, lo);
+}
+__device__ __forceinline__ u32x4 perm_bf16x8(const uint16_t* row, int kb, int h) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(row + 16 * kb + 4 * h);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(row + 16 * kb + 8 + 4 * h);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+// bf16 (1, 0) per register pair of a k-block: 1 where key drow <= query, for the
+// B operand of the running sum over the keys of the chunk.
+__device__ __forceinline__ u32x4 tril_ones(int kb, int q, int lane) {
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r0 = drow(8 * kb + 2 * p, lane), r1 = drow(8 * kb + 2 * p + 1, lane);
+    w[p] = (r0 <= q ? bf16k::kBf16One : 0u) | ((r1 <= q ? bf16k::kBf16One : 0u) << 16);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// ---------------------------------------------------------------------------
+// k_bw_query_causal: dq and (M_i, D_i, delta_i) per query.  Per chunk, wave w:
+//   a_if = 2^(g_if - M_wi) (FT, M_wi the wave's row maximum);
+//   T_if - z_if delta_i = (S_f.dy_i - z_f delta_i over keys before the chunk,
+//   S^T in registers) + sum over keys j <= i of the chunk b_jf (v_j.dy_i - delta_i);
+//   D_w = sum_f a z,  Ghat = a (T - z delta),  u_w = sum_f Ghat,  U_w = Ghat W;
+// then S^T, z take the chunk's keys.  Combine: scale_w = 2^(M_wi - M_i),
+// dq_i = (sum_w scale_w U_w - q_i sum_w scale_w u_w) / sum_w scale_w D_w.
+// ---------------------------------------------------------------------------
+template <int M>
+__global__ __launch_bounds__(2 * M) void k_bw_query_causal(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ W, const float* __restrict__ Y, const float* __restrict__ dY,
+    const float* __restrict__ cfin, const float* __restrict__ part_S, const float* __restrict__ part_z,
+    float* __restrict__ dQ, float* __restrict__ aux, int H, int n, int segs, int span) {
+  constexpr int NW = M / 32, NT = 2 * M;
+  __shared__ __attribute__((aligned(16))) uint16_t wl[M * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[64 * 64];
+  __shared__ __attribute__((aligned(16))) float ul[NW][32][kD];
+  __shared__ float sl_u[NW][32], sl_d[NW][32], sl_m[NW][32], dl[32];
+  __shared__ __attribute__((aligned(16))) float zl[NW][32];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5;
+  const int bh = blockIdx.x / segs, sg = blockIdx.x % segs, hh = bh % H;
+  const int t0 = sg * span, t1 = min(n, t0 + span);
+  const int fb = 32 * wave, f = fb + (lane & 31);
+  const uint16_t* Wh = W + static_cast<size_t>(hh) * M * kD;
+  for (int c = t; c < M * 8; c += NT)
+    *reinterpret_cast<u32x4*>(wl + tile_at(c >> 3, c & 7)) = *reinterpret_cast<const u32x4*>(Wh + 8 * c);
+  u32x4 wop[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    wop[ks] = *reinterpret_cast<const u32x4*>(Wh + static_cast<size_t>(f) * kD + 16 * ks + 8 * h);
+  const float C = cfin[static_cast<size_t>(bh) * M + f];
+  // S^T (rows = value columns, lane = feature) and z of the keys before the segment
+  f32x16 St[2];
+  {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) St[ct][i] = 0.f;
+    float z = 0.f;
+    for (int s = 0; s < sg; ++s) {
+      const float* PS = part_S + (static_cast<size_t>(bh) * segs + s) * M * kD + static_cast<size_t>(f) * kD;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) St[ct][i] += PS[32 * ct + drow(i, lane)];
+      z += part_z[(static_cast<size_t>(bh) * segs + s) * M + f];
+    }
+    if (lane < 32) zl[wave][lane] = z;
+  }
+  __syncthreads();
+
+  const size_t rowbase = static_cast<size_t>(bh) * n;
+  for (int c0 = t0; c0 < t1; c0 += 32) {
+    const int row = c0 + (lane & 31), qi = lane & 31;
+    const bool ok = row < t1;
+    // the chunk's values (rows 0..31 of the tile) for the S update
+    for (int c = t; c < 256; c += NT) {
+      const int r = c >> 3, ch = c & 7;
+      *reinterpret_cast<u32x4*>(vt + swz(r, ch)) =
+          c0 + r < t1 ? *reinterpret_cast<const u32x4*>(V + (rowbase + c0 + r) * kD + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 xq[4], xk[4], xv[4], dph[4], dpl[4];
+    f32x16 pq = {}, pkt = {}, mvd = {};
+    float dlp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cc = 16 * ks + 8 * h;
+      u32x4 dnh = {0u, 0u, 0u, 0u}, dnm = dnh, dnl = dnh;
+      if (ok) {
+        xq[ks] = *reinterpret_cast<const u32x4*>(Q + (rowbase + row) * kD + cc);
+        xk[ks] = *reinterpret_cast<const u32x4*>(K + (rowbase + row) * kD + cc);
+        xv[ks] = *reinterpret_cast<const u32x4*>(V + (rowbase + row) * kD + cc);
+        split3_row8(dY + (rowbase + row) * kD + cc, dnh, dnm, dnl);
+        perm_f32x8(dY + (rowbase + row) * kD, ks, h, dph[ks], dpl[ks]);
+        const float* dp = dY + (rowbase + row) * kD + cc;
+        const float* yp = Y + (rowbase + row) * kD + cc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dlp = fmaf(dp[e], yp[e], dlp);
+      } else {
+        xq[ks] = xk[ks] = xv[ks] = dph[ks] = dpl[ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+      // projections: queries (FT, lane = token), keys (TF, lane = feature); V dY^T
+      // (rows = keys, columns = queries (lane)) with dy to all its 24 bits
+      pq = mfma_bf16(as_bf16x8(rows_operand(wl, fb, lane, ks)), as_bf16x8(xq[ks]), pq);
+      pkt = mfma_bf16(as_bf16x8(xk[ks]), as_bf16x8(wop[ks]), pkt);
+      mvd = mfma_bf16(as_bf16x8(xv[ks]), as_bf16x8(dnh), mvd);
+      mvd = mfma_bf16(as_bf16x8(xv[ks]), as_bf16x8(dnm), mvd);
+      mvd = mfma_bf16(as_bf16x8(xv[ks]), as_bf16x8(dnl), mvd);
+    }
+    const float delta = pair_sum(dlp);
+    // |k|^2 of the chunk's keys (lane = key) -> LDS, for the TF key features
+    float kp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo_as_f32(xk[ks][e]), hi = bf16_hi_as_f32(xk[ks][e]);
+        kp = fmaf(lo, lo, kp);
+        kp = fmaf(hi, hi, kp);
+      }
+    kp = pair_sum(kp);
+    if (lane < 32) dl[lane] = kp;   // every wave writes the same values
+    __syncthreads();                // V tile and |k|^2 visible
+    float b[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = drow(i, lane);
+      b[i] = c0 + r < t1 ? fast_exp2(kLog2e * fmaf(-0.5f, dl[r], pkt[i]) - C) : 0.f;
+    }
+    // masked N = V dY^T - delta (keys after the query dropped) as hi / lo B operands:
+    // v_j.dy_i - delta_i = dy_i.(v_j - y_i), formed before the product with b
+    float mm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mm[i] = drow(i, lane) <= qi ? mvd[i] - delta : 0.f;
+    // T (FT: lane = query): carry (S^T x dy) + chunk (b^T x N); z over the chunk's keys
+    f32x16 tacc = {}, zacc = {};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4 sh, slo;
+      split8(St[kb >> 1], kb & 1, sh, slo);
+      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dph[kb]), tacc);
+      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dpl[kb]), tacc);
+      tacc = mfma_bf16(as_bf16x8(slo), as_bf16x8(dph[kb]), tacc);
+    }
+    u32x4 bth[2], btl[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      split8(b, kb, bth[kb], btl[kb]);
+      u32x4 mh, ml;
+      split8(mm, kb, mh, ml);
+      tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(mh), tacc);
+      tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ml), tacc);
+      tacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(mh), tacc);
+      const u32x4 ones = tril_ones(kb, qi, lane);
+      zacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ones), zacc);
+      zacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(ones), zacc);
+    }
+    // a (FT), the wave's row maximum, and the wave's shares
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 cc = *reinterpret_cast<const f32x4*>(&cfin[static_cast<size_t>(bh) * M + fb + 8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pq[4 * j + e] = fmaf(kLog2e, pq[4 * j + e], cc[e]);
+        mx = fmaxf(mx, pq[4 * j + e]);
+      }
+    }
+    const float Mw = pair_max(mx);
+    float G[16], Dp = 0.f, Gs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 zc = *reinterpret_cast<const f32x4*>(&zl[wave][8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        const float a = fast_exp2(pq[i] - Mw);
+        Dp = fmaf(a, zc[e] + zacc[i], Dp);
+        G[i] = a * fmaf(-zc[e], delta, tacc[i]);
+        Gs += G[i];
+      }
+    }
+    f32x16 acc[2] = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 gh, gl;
+      split8(G, kb, gh, gl);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const u32x4 wb = cols_operand(wl, fb, kb, dt, lane);
+        acc[dt] = mfma_bf16(as_bf16x8(gh), as_bf16x8(wb), acc[dt]);
+        acc[dt] = mfma_bf16(as_bf16x8(gl), as_bf16x8(wb), acc[dt]);
+      }
+    }
+    const float Dw = pair_sum(Dp), Gw = pair_sum(Gs);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + (lane & 31)] = acc[dt][i];
+    if (lane < 32) {
+      sl_u[wave][lane] = Gw;
+      sl_d[wave][lane] = Dw;
+      sl_m[wave][lane] = Mw;
+    }
+    // the chunk's keys join S^T and z
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const u32x4 va = v_operand(vt, 16 * kb, ct, lane);
+        St[ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(bth[kb]), St[ct]);
+        St[ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(btl[kb]), St[ct]);
+      }
+    float zs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) zs += b[i];
+    zs = pair_sum(zs);
+    __syncthreads();   // shares visible; zl of this chunk read by every wave
+    if (lane < 32) zl[wave][lane] += zs;
+    // combine: thread -> one query and CPQ columns
+    {
+      constexpr int CPQ = 32 * kD / NT;
+      const int q = t / (kD / CPQ), cb = (t % (kD / CPQ)) * CPQ, r = c0 + q;
+      float Mq = sl_m[0][q];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) Mq = fmaxf(Mq, sl_m[w][q]);
+      float sc[NW], D = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        sc[w] = fast_exp2(sl_m[w][q] - Mq);
+        D = fmaf(sc[w], sl_d[w][q], D);
+        u = fmaf(sc[w], sl_u[w][q], u);
+      }
+      if (r < t1) {
+        const float rD = 1.f / D;
+#pragma unroll
+        for (int e = 0; e < CPQ; ++e) {
+          float U = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) U = fmaf(sc[w], ul[w][q][cb + e], U);
+          const float qv = __uint_as_float(static_cast<uint32_t>(Q[(rowbase + r) * kD + cb + e]) << 16);
+          dQ[(rowbase + r) * kD + cb + e] = (U - qv * u) * rD;
+        }
+        if (cb == 0) {
+          // delta of query r: from the lane that holds it in wave 0 (written below)
+          aux[(rowbase + r) * 4 + 0] = Mq;
+          aux[(rowbase + r) * 4 + 1] = D;
+        }
+      }
+    }
+    if (wave == 0 && lane < 32 && ok) aux[(rowbase + row) * 4 + 2] = delta;
+    __syncthreads();   // shares, V tile and |k|^2 free for the next chunk
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_bw_key_causal: dk and dv, walking the segment's chunks from the last.
+// R (lane = value column) and R^T (lane = feature) and rho hold the sums over
+// queries after the chunk (the segments after this one, then the later chunks).
+// Per chunk, wave w, coef_if = 2^(g_if - M_i) / D_i:
+//   dv_j = b_j.R + sum_{i >= j in chunk} (coef_i.b_j) dy_i
+//   db_jf = R_f.v_j - rho_f + sum_{i >= j in chunk} coef_if (dy_i.v_j - delta_i)
+//   H = b db,  dk_j = W^T H_j - k_j sum_f H_jf
+// then R, R^T, rho take the chunk's queries.
+// ---------------------------------------------------------------------------
+template <int M>
+__global__ __launch_bounds__(2 * M) void k_bw_key_causal(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ W, const float* __restrict__ dY, const float* __restrict__ cfin,
+    const float* __restrict__ aux, const float* __restrict__ part_R, const float* __restrict__ part_rho,
+    float* __restrict__ dK, float* __restrict__ dV, int H, int n, int segs, int span) {
+  constexpr int NW = M / 32, NT = 2 * M;
+  __shared__ __attribute__((aligned(16))) uint16_t wl[M * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t dth[64 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t dtl[64 * 64];
+  __shared__ __attribute__((aligned(16))) float ul[NW][32][kD];
+  __shared__ float sl_h[NW][32];
+  __shared__ __attribute__((aligned(16))) f32x4 ax[32];
+  __shared__ __attribute__((aligned(16))) float rl[NW][32];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5;
+  const int bh = blockIdx.x / segs, sg = blockIdx.x % segs, hh = bh % H;
+  const int t0 = sg * span, t1 = min(n, t0 + span);
+  const int fb = 32 * wave, f = fb + (lane & 31);
+  const uint16_t* Wh = W + static_cast<size_t>(hh) * M * kD;
+  for (int c = t; c < M * 8; c += NT)
+    *reinterpret_cast<u32x4*>(wl + tile_at(c >> 3, c & 7)) = *reinterpret_cast<const u32x4*>(Wh + 8 * c);
+  u32x4 wop[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    wop[ks] = *reinterpret_cast<const u32x4*>(Wh + static_cast<size_t>(f) * kD + 16 * ks + 8 * h);
+  const float C = cfin[static_cast<size_t>(bh) * M + f];
+  // R (D[f][c]: lane = column), R^T (D[c][f]: lane = feature), rho: segments after this one
+  f32x16 R[2], Rt[2];
+  {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) R[x][i] = Rt[x][i] = 0.f;
+    float rho = 0.f;
+    for (int s = segs - 1; s > sg; --s) {
+      const float* PR = part_R + (static_cast<size_t>(bh) * segs + s) * M * kD;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          R[x][i] += PR[static_cast<size_t>(fb + drow(i, lane)) * kD + 32 * x + (lane & 31)];
+          Rt[x][i] += PR[static_cast<size_t>(f) * kD + 32 * x + drow(i, lane)];
+        }
+      rho += part_rho[(static_cast<size_t>(bh) * segs + s) * M + f];
+    }
+    if (lane < 32) rl[wave][lane] = rho;
+  }
+  __syncthreads();
+
+  const size_t rowbase = static_cast<size_t>(bh) * n;
+  const int nch = (t1 - t0 + 31) / 32;
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int c0 = t0 + 32 * ci;
+    const int row = c0 + (lane & 31), tj = lane & 31;
+    const bool ok = row < t1;
+    // the chunk's dY as bf16 hi / lo tiles (rows 0..31) and (M_i, D_i, delta_i)
+    for (int c = t; c < 256; c += NT) {
+      const int r = c >> 3, ch = c & 7;
+      u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+      if (c0 + r < t1) split_row8(dY + (rowbase + c0 + r) * kD + 8 * ch, hi, lo);
+      *reinterpret_cast<u32x4*>(dth + swz(r, ch)) = hi;
+      *reinterpret_cast<u32x4*>(dtl + swz(r, ch)) = lo;
+    }
+    for (int r = t; r < 32; r += NT)
+      ax[r] = c0 + r < t1 ? *reinterpret_cast<const f32x4*>(aux + (rowbase + c0 + r) * 4) : f32x4{0.f, 1.f, 0.f, 0.f};
+    __syncthreads();   // dY tiles and aux visible
+    // per k-step: projections of the chunk's queries (FT and TF) and keys (FT),
+    // dY V^T (rows = queries, columns = keys (lane)) with dy to all its 24 bits,
+    // and R.v_j (FT: lane = key) from R^T with v's columns in register order
+    f32x16 pqf = {}, pqt = {}, pkf = {}, rvd = {}, ndv = {};
+    float kp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cc = 16 * ks + 8 * h;
+      u32x4 xq = {0u, 0u, 0u, 0u}, xk = xq, xvn = xq, xvp = xq, dnh = xq, dnm = xq, dnl = xq;
+      if (ok) {
+        xq = *reinterpret_cast<const u32x4*>(Q + (rowbase + row) * kD + cc);
+        xk = *reinterpret_cast<const u32x4*>(K + (rowbase + row) * kD + cc);
+        xvn = *reinterpret_cast<const u32x4*>(V + (rowbase + row) * kD + cc);
+        xvp = perm_bf16x8(V + (rowbase + row) * kD, ks, h);
+        split3_row8(dY + (rowbase + row) * kD + cc, dnh, dnm, dnl);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo_as_f32(xk[e]), hi = bf16_hi_as_f32(xk[e]);
+        kp = fmaf(lo, lo, kp);
+        kp = fmaf(hi, hi, kp);
+      }
+      const u32x4 wa = rows_operand(wl, fb, lane, ks);
+      pqf = mfma_bf16(as_bf16x8(wa), as_bf16x8(xq), pqf);
+      pqt = mfma_bf16(as_bf16x8(xq), as_bf16x8(wop[ks]), pqt);
+      pkf = mfma_bf16(as_bf16x8(wa), as_bf16x8(xk), pkf);
+      ndv = mfma_bf16(as_bf16x8(dnh), as_bf16x8(xvn), ndv);
+      ndv = mfma_bf16(as_bf16x8(dnm), as_bf16x8(xvn), ndv);
+      ndv = mfma_bf16(as_bf16x8(dnl), as_bf16x8(xvn), ndv);
+      u32x4 rh, rlo;
+      split8(Rt[ks >> 1], ks & 1, rh, rlo);
+      rvd = mfma_bf16(as_bf16x8(rh), as_bf16x8(xvp), rvd);
+      rvd = mfma_bf16(as_bf16x8(rlo), as_bf16x8(xvp), rvd);
+    }
+    const float kk = pair_sum(kp);
+    float cff[16], cft[16], bk[16];
+    const float mq = ax[tj][0], dq_ = ax[tj][1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 cc = *reinterpret_cast<const f32x4*>(&cfin[static_cast<size_t>(bh) * M + fb + 8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        cff[i] = ok ? fast_exp2(fmaf(kLog2e, pqf[i], cc[e]) - mq) / dq_ : 0.f;   // lane = query
+        bk[i] = ok ? fast_exp2(kLog2e * fmaf(-0.5f, kk, pkf[i]) - cc[e]) : 0.f;   // lane = key
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = drow(i, lane);
+      const f32x4 a = ax[r];
+      cft[i] = c0 + r < t1 ? fast_exp2(fmaf(kLog2e, pqt[i], C) - a[0]) / a[1] : 0.f;   // lane = feature, reg = query
+    }
+    u32x4 bh_[2], bl_[2], cfh[2], cfl[2], cth[2], ctl[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      split8(bk, kb, bh_[kb], bl_[kb]);
+      split8(cff, kb, cfh[kb], cfl[kb]);
+      split8(cft, kb, cth[kb], ctl[kb]);
+    }
+    // P'^T[i][j] = coef_i . b_j (lane = key j, register = query i), kept for i >= j
+    f32x16 pp = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      pp = mfma_bf16(as_bf16x8(cfh[kb]), as_bf16x8(bh_[kb]), pp);
+      pp = mfma_bf16(as_bf16x8(cfh[kb]), as_bf16x8(bl_[kb]), pp);
+      pp = mfma_bf16(as_bf16x8(cfl[kb]), as_bf16x8(bh_[kb]), pp);
+    }
+    float pm[16], nm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = drow(i, lane);   // query row of the register
+      pm[i] = r >= tj ? pp[i] : 0.f;
+      nm[i] = r >= tj ? ndv[i] - ax[r][2] : 0.f;
+    }
+    // dv: carry b R + chunk P' dY
+    f32x16 adv[2] = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 ph, pl;
+      split8(pm, kb, ph, pl);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        u32x4 rh, rlo;
+        split8(R[dt], kb, rh, rlo);
+        adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rh), adv[dt]);
+        adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rlo), adv[dt]);
+        adv[dt] = mfma_bf16(as_bf16x8(bl_[kb]), as_bf16x8(rh), adv[dt]);
+        const u32x4 yh = v_operand(dth, 16 * kb, dt, lane), yl = v_operand(dtl, 16 * kb, dt, lane);
+        adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(yh), adv[dt]);
+        adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(yl), adv[dt]);
+        adv[dt] = mfma_bf16(as_bf16x8(pl), as_bf16x8(yh), adv[dt]);
+      }
+    }
+    // db (FT: lane = key): R.v - rho + coef^T N
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 nh, nl;
+      split8(nm, kb, nh, nl);
+      rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nh), rvd);
+      rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nl), rvd);
+      rvd = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(nh), rvd);
+    }
+    float Hh[16], Hs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 rr = *reinterpret_cast<const f32x4*>(&rl[wave][8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Hh[4 * j + e] = bk[4 * j + e] * (rvd[4 * j + e] - rr[e]);
+        Hs += Hh[4 * j + e];
+      }
+    }
+    f32x16 adk[2] = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 hh_, hl_;
+      split8(Hh, kb, hh_, hl_);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const u32x4 wb = cols_operand(wl, fb, kb, dt, lane);
+        adk[dt] = mfma_bf16(as_bf16x8(hh_), as_bf16x8(wb), adk[dt]);
+        adk[dt] = mfma_bf16(as_bf16x8(hl_), as_bf16x8(wb), adk[dt]);
+      }
+    }
+    const float Hw = pair_sum(Hs);
+    // the chunk's queries join R, R^T and rho (after their use above)
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rs = fmaf(cft[i], ax[drow(i, lane)][2], rs);
+    rs = pair_sum(rs);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const u32x4 yh = v_operand(dth, 16 * kb, dt, lane), yl = v_operand(dtl, 16 * kb, dt, lane);
+        R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(yh), R[dt]);
+        R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(yl), R[dt]);
+        R[dt] = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(yh), R[dt]);
+        Rt[dt] = mfma_bf16(as_bf16x8(yh), as_bf16x8(cth[kb]), Rt[dt]);
+        Rt[dt] = mfma_bf16(as_bf16x8(yh), as_bf16x8(ctl[kb]), Rt[dt]);
+        Rt[dt] = mfma_bf16(as_bf16x8(yl), as_bf16x8(cth[kb]), Rt[dt]);
+      }
+    // dv shares, then dk shares, through LDS
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + (lane & 31)] = adv[dt][i];
+    if (lane < 32) sl_h[wave][lane] = Hw;
+    __syncthreads();
+    if (lane < 32) rl[wave][lane] += rs;
+    constexpr int CPQ = 32 * kD / NT;
+    const int q = t / (kD / CPQ), cb = (t % (kD / CPQ)) * CPQ, r = c0 + q;
+    if (r < t1) {
+#pragma unroll
+      for (int e = 0; e < CPQ; ++e) {
+        float U = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) U += ul[w][q][cb + e];
+        dV[(rowbase + r) * kD + cb + e] = U;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + (lane & 31)] = adk[dt][i];
+    __syncthreads();
+    if (r < t1) {
+      float hs = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) hs += sl_h[w][q];
+#pragma unroll
+      for (int e = 0; e < CPQ; ++e) {
+        float U = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) U += ul[w][q][cb + e];
+        const float kv = __uint_as_float(static_cast<uint32_t>(K[(rowbase + r) * kD + cb + e]) << 16);
+        dK[(rowbase + r) * kD + cb + e] = U - kv * hs;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int M>
+hipError_t launch_causal_m(const BwPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* W, const float* y, const float* dy, float* dq, float* dk, float* dv,
+                           void* ws, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  float* cpart = reinterpret_cast<float*>(base + p.off_cpart);
+  float* pS = reinterpret_cast<float*>(base + p.off_part);
+  float* pz = reinterpret_cast<float*>(base + p.off_pvec);
+  float* pR = reinterpret_cast<float*>(base + p.off_part2);
+  float* prho = reinterpret_cast<float*>(base + p.off_pvec2);
+  float* cfin = reinterpret_cast<float*>(base + p.off_cfin);
+  float* aux = reinterpret_cast<float*>(base + p.off_aux);
+  const int BH = p.B * p.H;
+  const dim3 gs(BH * p.splits), bs(2 * M);
+  auto kmax = k_bw_keys<M, 0>;
+  FAVOR_LAUNCH("k_bw_kmax", kmax, gs, bs, 0, s, k, v, W, cpart, pS, pz, p.H, p.n, p.splits, p.span);
+  auto kst = k_bw_keys<M, 1>;
+  FAVOR_LAUNCH("k_bw_kstate", kst, gs, bs, 0, s, k, v, W, cpart, pS, pz, p.H, p.n, p.splits, p.span);
+  FAVOR_LAUNCH("k_bw_cmax", k_bw_cmax, dim3((BH * p.m + 255) / 256), dim3(256), 0, s, cpart, cfin, BH * p.m, p.m,
+               p.splits);
+  auto kq = k_bw_query_causal<M>;
+  FAVOR_LAUNCH("k_bw_query_causal", kq, gs, bs, 0, s, q, k, v, W, y, dy, cfin, pS, pz, dq, aux, p.H, p.n, p.splits,
+               p.span);
+  auto kr = k_bw_rstate<M>;
+  FAVOR_LAUNCH("k_bw_rstate", kr, gs, bs, 0, s, q, dy, W, cfin, aux, pR, prho, p.H, p.n, p.splits, p.span);
+  auto kc = k_bw_key_causal<M>;
+  FAVOR_LAUNCH("k_bw_key_causal", kc, gs, bs, 0, s, q, k, v, W, dy, cfin, aux, pR, prho, dk, dv, p.H, p.n,
+               p.splits, p.span);
+  return hipGetLastError();
+}
+
 template <int M>
 hipError_t launch_m(const BwPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* W,
                     const float* y, const float* dy, float* dq, float* dk, float* dv, void* ws, hipStream_t s) {
@@ -626,10 +1216,13 @@ BwPlan bw_plan(int B, int H, int n, int m, int causal) {
   p.off_cpart = take(static_cast<size_t>(BH) * p.splits * m * 4);
   p.off_part = take(static_cast<size_t>(BH) * p.splits * m * kD * 4);
   p.off_pvec = take(static_cast<size_t>(BH) * p.splits * m * 4);
-  p.off_stiles = take(static_cast<size_t>(BH) * m * kD * 2 * 2);
-  p.off_rtiles = take(static_cast<size_t>(BH) * m * kD * 2 * 2);
-  p.off_z = take(static_cast<size_t>(BH) * m * 4);
-  p.off_rho = take(static_cast<size_t>(BH) * m * 4);
+  p.off_part2 = causal ? take(static_cast<size_t>(BH) * p.splits * m * kD * 4) : 0;
+  p.off_pvec2 = causal ? take(static_cast<size_t>(BH) * p.splits * m * 4) : 0;
+  // the merged states (non-causal only: the causal kernels read the partials)
+  p.off_stiles = causal ? 0 : take(static_cast<size_t>(BH) * m * kD * 2 * 2);
+  p.off_rtiles = causal ? 0 : take(static_cast<size_t>(BH) * m * kD * 2 * 2);
+  p.off_z = causal ? 0 : take(static_cast<size_t>(BH) * m * 4);
+  p.off_rho = causal ? 0 : take(static_cast<size_t>(BH) * m * 4);
   p.off_cfin = take(static_cast<size_t>(BH) * m * 4);
   p.off_aux = take(static_cast<size_t>(BH) * n * 16);
   p.off_end = off;
@@ -639,7 +1232,14 @@ BwPlan bw_plan(int B, int H, int n, int m, int causal) {
 hipError_t launch_backward_bf16(const BwPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* W, const float* y, const float* dy, float* dq, float* dk, float* dv,
                                 void* ws, hipStream_t s) {
-  if (p.causal) return hipErrorInvalidValue;
+  if (p.causal) {
+    switch (p.m) {
+      case 64: return launch_causal_m<64>(p, q, k, v, W, y, dy, dq, dk, dv, ws, s);
+      case 128: return launch_causal_m<128>(p, q, k, v, W, y, dy, dq, dk, dv, ws, s);
+      case 256: return launch_causal_m<256>(p, q, k, v, W, y, dy, dq, dk, dv, ws, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.m) {
     case 64: return launch_m<64>(p, q, k, v, W, y, dy, dq, dk, dv, ws, s);
     case 128: return launch_m<128>(p, q, k, v, W, y, dy, dq, dk, dv, ws, s);

@@ -96,7 +96,8 @@ namespace bw {
 struct BwPlan {
   int B, H, n, m, causal;
   int splits, span;   // key / query ranges per (b,h) (multiple of 64 tokens)
-  size_t off_cpart, off_part, off_pvec, off_stiles, off_rtiles, off_z, off_rho, off_cfin, off_aux, off_end;
+  size_t off_cpart, off_part, off_pvec, off_part2, off_pvec2, off_stiles, off_rtiles, off_z, off_rho, off_cfin,
+      off_aux, off_end;
 };
 BwPlan bw_plan(int B, int H, int n, int m, int causal);
 hipError_t launch_backward_bf16(const BwPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,

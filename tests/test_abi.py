@@ -167,6 +167,9 @@ def test_backward_host_only():
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 256, 0) > 0
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 100, 0) == 0
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 32, 64, 0) == 0
+    # the causal pass keeps both partial states (no merged tiles)
+    assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 256, 1) > 0
+    assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 256, 2) == 0
     F = FAKE
     ok = [F] * 9 + [1, 2, 64, 64, 64]
     assert L.favor_attention_backward(*ok, 2, None, 0, None) == L.FAVOR_ERR_INVALID_ARGUMENT
@@ -176,3 +179,4 @@ def test_backward_host_only():
     assert L.favor_attention_backward(*odd, 0, None, 0, None) == L.FAVOR_ERR_UNSUPPORTED
     assert L.favor_attention_backward(*([F] * 9 + [1, 2, 64, 64, 96]), 0, None, 0, None) == L.FAVOR_ERR_UNSUPPORTED
     assert L.favor_attention_backward(*([F] * 9 + [1, 2, 64, 64, 64]), 0, F, 16, None) == L.FAVOR_ERR_OUT_OF_MEMORY
+    assert L.favor_attention_backward(*([F] * 9 + [1, 2, 64, 64, 64]), 1, F, 16, None) == L.FAVOR_ERR_OUT_OF_MEMORY

@@ -1,9 +1,14 @@
-"""GPU parity of the backward pass (dq, dk, dv) against the fp64 oracle.
+"""GPU parity of the backward pass (dq, dk, dv) against the fp64 oracle,
+non-causal and causal.
 
 bf16 inputs, fp32 gradients; bar per gradient: max over (b, h) of
 max|g - g_ref| / max|g_ref| <= 2e-3 (the bf16 bar).  A single token is the
 degenerate case: y = v_0 whatever q and k are, so dq = dk = 0 exactly and dv =
-dy; there the bound is absolute.  The parity cases hand the backward the
+dy; there the bound is absolute (and so for the causal first query, which sees
+key 0 alone).  The causal kernels walk ranges of keys and queries in 32-token
+chunks, carrying the prefix (suffix) state of the ranges before (after): the
+shapes below give one range, many short ranges, and long ranges with a ragged
+last chunk.  The parity cases hand the backward the
 oracle's own forward output y, so that they measure the backward alone; one
 case runs the GPU forward first.
 """
@@ -50,11 +55,16 @@ def gpu_backward(x, y, dy, **kw):
     return [t.cpu().numpy() for t in out]
 
 
+def fwd(x, causal):
+    return (oracle.attention_causal if causal else oracle.attention)(x["q"], x["k"], x["v"], x["W"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("m", [64, 128, 256])
-def test_backward_single_token(m):
+def test_backward_single_token(m, causal):
     x, dy = make(2, 2, 1, m, 299)
     y = x["v"].astype(np.float64)
-    dq, dk, dv = gpu_backward(x, y, dy)
+    dq, dk, dv = gpu_backward(x, y, dy, causal=causal)
     # dq and dk are exact cancellations (S dy - z delta, R v - rho): what is left is
     # operand rounding (~2^-16) times |W| |v| |dy|, O(1) here; the bar is 2e-3 of a
     # gradient scale of 0.5, a floor for these O(1) inputs
@@ -62,36 +72,49 @@ def test_backward_single_token(m):
     assert np.max(np.abs(dv - dy)) < 1e-4 * np.max(np.abs(dy))   # hi + lo operands: ~2^-16 relative
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("m", [64, 128, 256])
 @pytest.mark.parametrize("n", [2, 31, 65, 1000, 2049])
-def test_backward_matches_oracle(n, m):
+def test_backward_matches_oracle(n, m, causal):
     x, dy = make(1, 2, n, m, 300 + n)
-    y = oracle.attention(x["q"], x["k"], x["v"], x["W"])
-    got = gpu_backward(x, y, dy)
-    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy)
+    got = gpu_backward(x, fwd(x, causal), dy, causal=causal)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy, causal=causal)
     for g, w, name in zip(got, want, ("dq", "dk", "dv")):
         assert np.all(np.isfinite(g)), name
         assert gerr(g, w) < TOL, (name, gerr(g, w))
 
 
-def test_backward_C2_shape_and_large_inputs():
+@pytest.mark.parametrize("B,H,n,m", [(4, 8, 1000, 128), (2, 4, 3000, 64), (8, 8, 777, 256)])
+def test_backward_causal_long_ranges(B, H, n, m):
+    # many (b, h): few ranges per head, each several chunks long, the last one ragged
+    x, dy = make(B, H, n, m, 310 + n)
+    got = gpu_backward(x, fwd(x, True), dy, causal=True)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy, causal=True)
+    for g, w, name in zip(got, want, ("dq", "dk", "dv")):
+        assert gerr(g, w) < TOL, (name, gerr(g, w))
+    # query 0 sees key 0 alone (y_0 = v_0): its dq cancels
+    assert np.max(np.abs(got[0][:, :, 0])) < 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_C2_shape_and_large_inputs(causal):
     for scale, seed in ((1.0, 2), (2.0, 3)):
         x, dy = make(1, 8, 1024, 256, seed, scale)
-        y = oracle.attention(x["q"], x["k"], x["v"], x["W"])
-        got = gpu_backward(x, y, dy)
-        want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy)
+        got = gpu_backward(x, fwd(x, causal), dy, causal=causal)
+        want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy, causal=causal)
         for g, w in zip(got, want):
             assert gerr(g, w) < TOL
 
 
-def test_backward_C3_shape_sampled():
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_C3_shape_sampled(causal):
     """B=4, H=8, n=16384, m=256: the benchmark's shape; rows sampled per (b, h)."""
     cfg = fi.config("C3")
     x = fi.make_inputs(cfg)
     dy = np.random.default_rng(8).standard_normal(x["q"].shape).astype(np.float32)
     t = {k: bf(v) for k, v in x.items()}
-    y = favor.attention(t["q"], t["k"], t["v"], t["W"])
-    dq, dk, dv = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy))
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"], causal=causal)
+    dq, dk, dv = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy), causal=causal)
     torch.cuda.synchronize()
     y = y.cpu().numpy()
     dq, dk, dv = (a.cpu().numpy() for a in (dq, dk, dv))
@@ -100,7 +123,7 @@ def test_backward_C3_shape_sampled():
     for b, h in ((0, 0), (2, 3), (3, 7)):
         rows = np.sort(np.concatenate([[0, 16383], rng.choice(16384, 6, replace=False)]))
         rq, rk, rv = oracle.attention_backward_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["W"][h],
-                                                    dy[b, h], rows, rows, causal=False)
+                                                    dy[b, h], rows, rows, causal=causal)
         for got, want in ((dq[b, h][rows], rq), (dk[b, h][rows], rk), (dv[b, h][rows], rv)):
             # normalised by the slice's largest gradient, as the metric does; the forward's own
             # error (y from the GPU) is inside this bar too
@@ -108,24 +131,27 @@ def test_backward_C3_shape_sampled():
             assert np.max(np.abs(got - want)) / scale < 5 * TOL
 
 
-def test_backward_end_to_end_and_determinism():
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_end_to_end_and_determinism(causal):
     x, dy = make(2, 4, 3000, 256, 11)
     t = {k: bf(v) for k, v in x.items()}
-    y = favor.attention(t["q"], t["k"], t["v"], t["W"])
-    a = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy))
-    nb = favor._lib.favor_backward_workspace_bytes(2, 4, 3000, 64, 256, 0)
+    y = favor.attention(t["q"], t["k"], t["v"], t["W"], causal=causal)
+    a = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy), causal=causal)
+    nb = favor._lib.favor_backward_workspace_bytes(2, 4, 3000, 64, 256, int(causal))
     ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
-    b = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy), workspace=ws)
+    b = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy), causal=causal, workspace=ws)
+    c = favor.attention_backward(t["q"], t["k"], t["v"], t["W"], y, f32(dy), causal=causal, workspace=ws)
     torch.cuda.synchronize()
-    for u, w in zip(a, b):
-        assert torch.equal(u, w)
-    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy)
+    for u, w, z in zip(a, b, c):
+        assert torch.equal(u, w) and torch.equal(u, z)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy, causal=causal)
     for g, w in zip(a, want):
         assert gerr(g.cpu().numpy(), w) < TOL
 
 
-def test_backward_causal_not_built():
-    x, dy = make(1, 1, 64, 64, 12)
-    y = oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])
+def test_backward_workspace_too_small_raises():
+    x, dy = make(1, 2, 300, 64, 12)
+    nb = favor._lib.favor_backward_workspace_bytes(1, 2, 300, 64, 64, 1)
+    ws = torch.zeros(nb - 256, dtype=torch.uint8, device=DEV)
     with pytest.raises(favor.FavorError):
-        gpu_backward(x, y, dy, causal=True)
+        gpu_backward(x, fwd(x, True), dy, causal=True, workspace=ws)
