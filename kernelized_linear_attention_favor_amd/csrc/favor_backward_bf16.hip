@@ -72,22 +72,6 @@ __device__ __forceinline__ void split_row8(const float* p, u32x4& hi, u32x4& lo)
   split8(x, 0, hi, lo);
 }
 
-// 8 consecutive fp32 values as three bf16 words each (hi + mid + lo carries all
-// 24 bits): for the dot products dy.v that are set against delta = dy.y, where
-// the difference may cancel to zero (a query that sees one key: y = v).
-__device__ __forceinline__ void split3_row8(const float* p, u32x4& hi, u32x4& mid, u32x4& lo) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  float r[8];
-  split8(x, 0, hi, mid);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[2 * e] = x[2 * e] - bf16_lo_as_f32(hi[e]) - bf16_lo_as_f32(mid[e]);
-    r[2 * e + 1] = x[2 * e + 1] - bf16_hi_as_f32(hi[e]) - bf16_hi_as_f32(mid[e]);
-  }
-  lo = u32x4{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]), pack_bf16(r[4], r[5]), pack_bf16(r[6], r[7])};
-}
-
 // ---------------------------------------------------------------------------
 // k_bw_keys<M, PASS>: one key range of one (b, h); M/32 waves, wave w owns
 // features [32w, 32w+32).  Per 64 keys: K (and V) tiles and |k|^2 in LDS; per
@@ -594,23 +578,12 @@ __global__ __launch_bounds__(512) void k_bw_key(const uint16_t* __restrict__ K, 
 // and i >= j (R, rho: suffix sums of the queries).  Both kernels walk one
 // segment of one (b, h) in chunks of 32 tokens; M/32 waves, wave w owns
 // features [32w, 32w+32).  Each wave forms its features' share of every
-// per-token quantity; the shares are summed in wave order in LDS (two barriers
-// per chunk).  The state is kept transposed where it is an A operand
-// (S^T[c][f], R^T[c][f]: lane = feature, register = value column), so the
-// value columns of dy and v are read in the MFMA register order:
-//   k-block kb of 16 columns, lane half h: columns 16kb + 4h .. +3 and 16kb + 8 + 4h .. +3.
+// per-token quantity; the shares are summed in wave order in LDS.  The state is
+// kept transposed where it is an A operand (S^T[c][f], R^T[c][f]: lane =
+// feature, register = value column), so the value columns of dy and v are read
+// in the MFMA register order: k-block kb of 16 columns, lane half h: columns
+// 16kb + 4h .. +3 and 16kb + 8 + 4h .. +3.
 // ===========================================================================
-__device__ __forceinline__ void perm_f32x8(const float* row, int kb, int h, u32x4& hi, u32x4& lo) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(row + 16 * kb + 4 * h);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(row + 16 * kb + 8 + 4 * h);
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  split8(x, 0, hi, lo);
-}
-__device__ __forceinline__ u32x4 perm_bf16x8(const uint16_t* row, int kb, int h) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(row + 16 * kb + 4 * h);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(row + 16 * kb + 8 + 4 * h);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
 // bf16 (1, 0) per register pair of a k-block: 1 where key drow <= query, for the
 // B operand of the running sum over the keys of the chunk.
 __device__ __forceinline__ u32x4 tril_ones(int kb, int q, int lane) {
@@ -623,6 +596,126 @@ __device__ __forceinline__ u32x4 tril_ones(int kb, int q, int lane) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// One 32-token chunk of a (b, h) in LDS, staged once per workgroup: q, k, v and
+// dy (as three bf16 words hi, mid, lo) in swizzled row-major [32][64] bf16 tiles,
+// |k|^2 per key, and per token (M_i, 1 / D_i, delta_i) (key side) or delta_i in
+// element 2 (query side, delta = dy.y formed here).  Rows past the end are zero.
+struct ChunkBuf {
+  uint16_t q[32 * 64], k[32 * 64], v[32 * 64], dh[32 * 64], dm[32 * 64], dl[32 * 64];
+  f32x4 ax[32];
+  float kk[32];
+};
+
+// The chunk's global reads, held in registers between chunks so that they are in
+// flight while the previous chunk computes.  16-byte pieces: 768 of q, k, v
+// (32 rows x 8 per matrix), 512 of dy (32 rows x 16), as many of y (query side).
+template <int NT, bool QSIDE>
+struct ChunkRegs {
+  static constexpr int NB = (768 + NT - 1) / NT, ND = (512 + NT - 1) / NT;
+  u32x4 b[NB];
+  f32x4 dy[ND];
+  f32x4 y[QSIDE ? ND : 1];
+  f32x4 ax;
+};
+
+template <int NT, bool QSIDE>
+__device__ __forceinline__ void chunk_load(ChunkRegs<NT, QSIDE>& R, const uint16_t* Q, const uint16_t* K,
+                                           const uint16_t* V, const float* dY, const float* Y, const float* aux,
+                                           size_t rowbase, int c0, int t1, int t) {
+#pragma unroll
+  for (int i = 0; i < R.NB; ++i) {
+    const int c = t + NT * i;
+    if (c < 768) {   // uniform per wave (NT and 256 are multiples of 64)
+      const int mat = c >> 8, r = (c >> 3) & 31, ch = c & 7;
+      const uint16_t* src = mat == 0 ? Q : (mat == 1 ? K : V);
+      R.b[i] = c0 + r < t1 ? *reinterpret_cast<const u32x4*>(src + (rowbase + c0 + r) * kD + 8 * ch)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R.ND; ++i) {
+    const int c = t + NT * i;
+    if (c < 512) {
+      const int r = c >> 4, c4 = (c & 15) * 4;
+      const bool ok = c0 + r < t1;
+      R.dy[i] = ok ? *reinterpret_cast<const f32x4*>(dY + (rowbase + c0 + r) * kD + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (QSIDE)
+        R.y[i] = ok ? *reinterpret_cast<const f32x4*>(Y + (rowbase + c0 + r) * kD + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if constexpr (!QSIDE) {
+    if (t < 32) R.ax = c0 + t < t1 ? *reinterpret_cast<const f32x4*>(aux + (rowbase + c0 + t) * 4) : f32x4{0.f, 1.f, 0.f, 0.f};
+  }
+}
+
+template <int NT, bool QSIDE>
+__device__ __forceinline__ void chunk_store(const ChunkRegs<NT, QSIDE>& R, ChunkBuf& B, int t) {
+#pragma unroll
+  for (int i = 0; i < R.NB; ++i) {
+    const int c = t + NT * i;
+    if (c < 768) {
+      const int mat = c >> 8, r = (c >> 3) & 31, ch = c & 7;
+      uint16_t* dst = mat == 0 ? B.q : (mat == 1 ? B.k : B.v);
+      *reinterpret_cast<u32x4*>(dst + swz(r, ch)) = R.b[i];
+      if (mat == 1) {   // |k|^2: the 8 lanes of one row
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = bf16_lo_as_f32(R.b[i][e]), hi = bf16_hi_as_f32(R.b[i][e]);
+          s = fmaf(lo, lo, s);
+          s = fmaf(hi, hi, s);
+        }
+        s = sum8(s);
+        if ((t & 7) == 0) B.kk[r] = s;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R.ND; ++i) {
+    const int c = t + NT * i;
+    if (c < 512) {
+      const int r = c >> 4, c4 = (c & 15) * 4;
+      const f32x4 x = R.dy[i];
+      uint32_t h0, m0, h1, m1;
+      split_bf16(x[0], x[1], h0, m0);
+      split_bf16(x[2], x[3], h1, m1);
+      const uint32_t l0 = pack_bf16(x[0] - bf16_lo_as_f32(h0) - bf16_lo_as_f32(m0),
+                                    x[1] - bf16_hi_as_f32(h0) - bf16_hi_as_f32(m0));
+      const uint32_t l1 = pack_bf16(x[2] - bf16_lo_as_f32(h1) - bf16_lo_as_f32(m1),
+                                    x[3] - bf16_hi_as_f32(h1) - bf16_hi_as_f32(m1));
+      const int off = swz(r, c4 >> 3) + (c4 & 7);
+      *reinterpret_cast<u32x2*>(B.dh + off) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(B.dm + off) = u32x2{m0, m1};
+      *reinterpret_cast<u32x2*>(B.dl + off) = u32x2{l0, l1};
+      if constexpr (QSIDE) {   // delta: the 16 lanes of one row
+        const f32x4 y = R.y[i];
+        float d = x[0] * y[0];
+        d = fmaf(x[1], y[1], d);
+        d = fmaf(x[2], y[2], d);
+        d = fmaf(x[3], y[3], d);
+        d = sum8(d);
+        d += __shfl_xor(d, 8);
+        if ((t & 15) == 0) B.ax[r] = f32x4{0.f, 0.f, d, 0.f};
+      }
+    }
+  }
+  if constexpr (!QSIDE) {   // (M_i, 1 / D_i, delta_i)
+    if (t < 32) B.ax[t] = f32x4{R.ax[0], 1.f / R.ax[1], R.ax[2], 0.f};
+  }
+}
+
+// Operands of token row `row` of a chunk tile: 8 columns 16ks + 8h .. (natural
+// order) or the register order of a k-block (columns 16kb + 4h .. +3 and
+// 16kb + 8 + 4h .. +3).
+__device__ __forceinline__ u32x4 tile_row8(const uint16_t* tile, int row, int ks, int h) {
+  return *reinterpret_cast<const u32x4*>(tile + swz(row, 2 * ks + h));
+}
+__device__ __forceinline__ u32x4 tile_perm8(const uint16_t* tile, int row, int kb, int h) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(tile + swz(row, 2 * kb) + 4 * h);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(tile + swz(row, 2 * kb + 1) + 4 * h);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // ---------------------------------------------------------------------------
 // k_bw_query_causal: dq and (M_i, D_i, delta_i) per query.  Per chunk, wave w:
 //   a_if = 2^(g_if - M_wi) (FT, M_wi the wave's row maximum);
@@ -631,6 +724,7 @@ __device__ __forceinline__ u32x4 tril_ones(int kb, int q, int lane) {
 //   D_w = sum_f a z,  Ghat = a (T - z delta),  u_w = sum_f Ghat,  U_w = Ghat W;
 // then S^T, z take the chunk's keys.  Combine: scale_w = 2^(M_wi - M_i),
 // dq_i = (sum_w scale_w U_w - q_i sum_w scale_w u_w) / sum_w scale_w D_w.
+// Chunks are staged in LDS (two buffers) with the next chunk's reads in flight.
 // ---------------------------------------------------------------------------
 template <int M>
 __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
@@ -640,23 +734,24 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
     float* __restrict__ dQ, float* __restrict__ aux, int H, int n, int segs, int span) {
   constexpr int NW = M / 32, NT = 2 * M;
   __shared__ __attribute__((aligned(16))) uint16_t wl[M * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[64 * 64];
+  __shared__ __attribute__((aligned(16))) ChunkBuf buf[2];
   __shared__ __attribute__((aligned(16))) float ul[NW][32][kD];
-  __shared__ float sl_u[NW][32], sl_d[NW][32], sl_m[NW][32], dl[32];
+  __shared__ float sl_u[NW][32], sl_d[NW][32], sl_m[NW][32];
   __shared__ __attribute__((aligned(16))) float zl[NW][32];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5;
+  __shared__ __attribute__((aligned(16))) float cl[M];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5, ql = lane & 31;
   const int bh = blockIdx.x / segs, sg = blockIdx.x % segs, hh = bh % H;
   const int t0 = sg * span, t1 = min(n, t0 + span);
-  const int fb = 32 * wave, f = fb + (lane & 31);
+  const int fb = 32 * wave, f = fb + ql;
+  const size_t rowbase = static_cast<size_t>(bh) * n;
+  ChunkRegs<NT, true> pre;
+  chunk_load<NT, true>(pre, Q, K, V, dY, Y, nullptr, rowbase, t0, t1, t);
   const uint16_t* Wh = W + static_cast<size_t>(hh) * M * kD;
   for (int c = t; c < M * 8; c += NT)
     *reinterpret_cast<u32x4*>(wl + tile_at(c >> 3, c & 7)) = *reinterpret_cast<const u32x4*>(Wh + 8 * c);
-  u32x4 wop[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    wop[ks] = *reinterpret_cast<const u32x4*>(Wh + static_cast<size_t>(f) * kD + 16 * ks + 8 * h);
+  for (int i = t; i < M; i += NT) cl[i] = cfin[static_cast<size_t>(bh) * M + i];
   const float C = cfin[static_cast<size_t>(bh) * M + f];
-  // S^T (rows = value columns, lane = feature) and z of the keys before the segment
+  // S^T (rows = value columns, lane = feature) and z of the keys before the range
   f32x16 St[2];
   {
 #pragma unroll
@@ -674,99 +769,89 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
     }
     if (lane < 32) zl[wave][lane] = z;
   }
+  chunk_store<NT, true>(pre, buf[0], t);
+  if (t0 + 32 < t1) chunk_load<NT, true>(pre, Q, K, V, dY, Y, nullptr, rowbase, t0 + 32, t1, t);
   __syncthreads();
 
-  const size_t rowbase = static_cast<size_t>(bh) * n;
-  for (int c0 = t0; c0 < t1; c0 += 32) {
-    const int row = c0 + (lane & 31), qi = lane & 31;
-    const bool ok = row < t1;
-    // the chunk's values (rows 0..31 of the tile) for the S update
-    for (int c = t; c < 256; c += NT) {
-      const int r = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4*>(vt + swz(r, ch)) =
-          c0 + r < t1 ? *reinterpret_cast<const u32x4*>(V + (rowbase + c0 + r) * kD + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+  int it = 0;
+  for (int c0 = t0; c0 < t1; c0 += 32, ++it) {
+    const ChunkBuf& B = buf[it & 1];
+    if (c0 + 32 < t1) {
+      chunk_store<NT, true>(pre, buf[(it + 1) & 1], t);
+      if (c0 + 64 < t1) chunk_load<NT, true>(pre, Q, K, V, dY, Y, nullptr, rowbase, c0 + 64, t1, t);
     }
-    u32x4 xq[4], xk[4], xv[4], dph[4], dpl[4];
-    f32x16 pq = {}, pkt = {}, mvd = {};
-    float dlp = 0.f;
+    // the phases below are kept apart (sched_barrier) so that each one's operands
+    // are read from LDS when used and die after it
+    // 1. key features b (TF: lane = feature, register = key), as bf16 hi / lo
+    u32x4 bth[2], btl[2];
+    float zs = 0.f;
+    {
+      f32x16 pkt = {};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int cc = 16 * ks + 8 * h;
-      u32x4 dnh = {0u, 0u, 0u, 0u}, dnm = dnh, dnl = dnh;
-      if (ok) {
-        xq[ks] = *reinterpret_cast<const u32x4*>(Q + (rowbase + row) * kD + cc);
-        xk[ks] = *reinterpret_cast<const u32x4*>(K + (rowbase + row) * kD + cc);
-        xv[ks] = *reinterpret_cast<const u32x4*>(V + (rowbase + row) * kD + cc);
-        split3_row8(dY + (rowbase + row) * kD + cc, dnh, dnm, dnl);
-        perm_f32x8(dY + (rowbase + row) * kD, ks, h, dph[ks], dpl[ks]);
-        const float* dp = dY + (rowbase + row) * kD + cc;
-        const float* yp = Y + (rowbase + row) * kD + cc;
+      for (int ks = 0; ks < 4; ++ks)
+        pkt = mfma_bf16(as_bf16x8(tile_row8(B.k, ql, ks, h)), as_bf16x8(rows_operand(wl, fb, lane, ks)), pkt);
+      float b[16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dlp = fmaf(dp[e], yp[e], dlp);
-      } else {
-        xq[ks] = xk[ks] = xv[ks] = dph[ks] = dpl[ks] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 16; ++i) {
+        const int r = drow(i, lane);
+        const float x = fast_exp2(kLog2e * fmaf(-0.5f, B.kk[r], pkt[i]) - C);
+        b[i] = c0 + r < t1 ? x : 0.f;
+        zs += b[i];
       }
-      // projections: queries (FT, lane = token), keys (TF, lane = feature); V dY^T
-      // (rows = keys, columns = queries (lane)) with dy to all its 24 bits
-      pq = mfma_bf16(as_bf16x8(rows_operand(wl, fb, lane, ks)), as_bf16x8(xq[ks]), pq);
-      pkt = mfma_bf16(as_bf16x8(xk[ks]), as_bf16x8(wop[ks]), pkt);
-      mvd = mfma_bf16(as_bf16x8(xv[ks]), as_bf16x8(dnh), mvd);
-      mvd = mfma_bf16(as_bf16x8(xv[ks]), as_bf16x8(dnm), mvd);
-      mvd = mfma_bf16(as_bf16x8(xv[ks]), as_bf16x8(dnl), mvd);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) split8(b, kb, bth[kb], btl[kb]);
     }
-    const float delta = pair_sum(dlp);
-    // |k|^2 of the chunk's keys (lane = key) -> LDS, for the TF key features
-    float kp = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_lo_as_f32(xk[ks][e]), hi = bf16_hi_as_f32(xk[ks][e]);
-        kp = fmaf(lo, lo, kp);
-        kp = fmaf(hi, hi, kp);
-      }
-    kp = pair_sum(kp);
-    if (lane < 32) dl[lane] = kp;   // every wave writes the same values
-    __syncthreads();                // V tile and |k|^2 visible
-    float b[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = drow(i, lane);
-      b[i] = c0 + r < t1 ? fast_exp2(kLog2e * fmaf(-0.5f, dl[r], pkt[i]) - C) : 0.f;
-    }
-    // masked N = V dY^T - delta (keys after the query dropped) as hi / lo B operands:
-    // v_j.dy_i - delta_i = dy_i.(v_j - y_i), formed before the product with b
-    float mm[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mm[i] = drow(i, lane) <= qi ? mvd[i] - delta : 0.f;
-    // T (FT: lane = query): carry (S^T x dy) + chunk (b^T x N); z over the chunk's keys
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. the chunk's part of T - z delta and of z (FT: lane = query): b^T N with
+    // N = V dY^T - delta masked to keys j <= i (v_j.dy_i - delta_i = dy_i.(v_j - y_i),
+    // formed before the product with b; dy to all its 24 bits)
+    const float delta = B.ax[ql][2];
     f32x16 tacc = {}, zacc = {};
+    {
+      f32x16 mvd = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 xv = tile_row8(B.v, ql, ks, h);
+        mvd = mfma_bf16(as_bf16x8(xv), as_bf16x8(tile_row8(B.dh, ql, ks, h)), mvd);
+        mvd = mfma_bf16(as_bf16x8(xv), as_bf16x8(tile_row8(B.dm, ql, ks, h)), mvd);
+        mvd = mfma_bf16(as_bf16x8(xv), as_bf16x8(tile_row8(B.dl, ql, ks, h)), mvd);
+      }
+      float mm[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mm[i] = drow(i, lane) <= ql ? mvd[i] - delta : 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4 mh, ml;
+        split8(mm, kb, mh, ml);
+        tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(mh), tacc);
+        tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ml), tacc);
+        tacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(mh), tacc);
+        const u32x4 ones = tril_ones(kb, ql, lane);
+        zacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ones), zacc);
+        zacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(ones), zacc);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. the carry: S^T x dy (dy hi / mid in register order)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       u32x4 sh, slo;
       split8(St[kb >> 1], kb & 1, sh, slo);
-      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dph[kb]), tacc);
-      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dpl[kb]), tacc);
-      tacc = mfma_bf16(as_bf16x8(slo), as_bf16x8(dph[kb]), tacc);
+      const u32x4 dph = tile_perm8(B.dh, ql, kb, h), dpl = tile_perm8(B.dm, ql, kb, h);
+      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dph), tacc);
+      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dpl), tacc);
+      tacc = mfma_bf16(as_bf16x8(slo), as_bf16x8(dph), tacc);
     }
-    u32x4 bth[2], btl[2];
+    __builtin_amdgcn_sched_barrier(0);
+    // 4. a (FT), the wave's row maximum, and the wave's shares
+    f32x16 pq = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      split8(b, kb, bth[kb], btl[kb]);
-      u32x4 mh, ml;
-      split8(mm, kb, mh, ml);
-      tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(mh), tacc);
-      tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ml), tacc);
-      tacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(mh), tacc);
-      const u32x4 ones = tril_ones(kb, qi, lane);
-      zacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ones), zacc);
-      zacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(ones), zacc);
-    }
-    // a (FT), the wave's row maximum, and the wave's shares
+    for (int ks = 0; ks < 4; ++ks)
+      pq = mfma_bf16(as_bf16x8(rows_operand(wl, fb, lane, ks)), as_bf16x8(tile_row8(B.q, ql, ks, h)), pq);
     float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 cc = *reinterpret_cast<const f32x4*>(&cfin[static_cast<size_t>(bh) * M + fb + 8 * j + 4 * h]);
+      const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[fb + 8 * j + 4 * h]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pq[4 * j + e] = fmaf(kLog2e, pq[4 * j + e], cc[e]);
@@ -803,27 +888,25 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + (lane & 31)] = acc[dt][i];
+      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = acc[dt][i];
     if (lane < 32) {
       sl_u[wave][lane] = Gw;
       sl_d[wave][lane] = Dw;
       sl_m[wave][lane] = Mw;
     }
-    // the chunk's keys join S^T and z
+    __builtin_amdgcn_sched_barrier(0);
+    // 5. the chunk's keys join S^T and z
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const u32x4 va = v_operand(vt, 16 * kb, ct, lane);
+        const u32x4 va = v_operand(B.v, 16 * kb, ct, lane);
         St[ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(bth[kb]), St[ct]);
         St[ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(btl[kb]), St[ct]);
       }
-    float zs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) zs += b[i];
     zs = pair_sum(zs);
-    __syncthreads();   // shares visible; zl of this chunk read by every wave
     if (lane < 32) zl[wave][lane] += zs;
+    __syncthreads();   // shares visible
     // combine: thread -> one query and CPQ columns
     {
       constexpr int CPQ = 32 * kD / NT;
@@ -841,34 +924,38 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
       if (r < t1) {
         const float rD = 1.f / D;
 #pragma unroll
-        for (int e = 0; e < CPQ; ++e) {
-          float U = 0.f;
+        for (int e4 = 0; e4 < CPQ; e4 += 4) {
+          f32x4 U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int w = 0; w < NW; ++w) U = fmaf(sc[w], ul[w][q][cb + e], U);
-          const float qv = __uint_as_float(static_cast<uint32_t>(Q[(rowbase + r) * kD + cb + e]) << 16);
-          dQ[(rowbase + r) * kD + cb + e] = (U - qv * u) * rD;
+          for (int w = 0; w < NW; ++w) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&ul[w][q][cb + e4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) U[e] = fmaf(sc[w], x[e], U[e]);
+          }
+          const u32x2 qw = *reinterpret_cast<const u32x2*>(B.q + swz(q, (cb + e4) >> 3) + ((cb + e4) & 7));
+          const float qv[4] = {bf16_lo_as_f32(qw[0]), bf16_hi_as_f32(qw[0]), bf16_lo_as_f32(qw[1]),
+                               bf16_hi_as_f32(qw[1])};
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (U[e] - qv[e] * u) * rD;
+          *reinterpret_cast<f32x4*>(dQ + (rowbase + r) * kD + cb + e4) = o;
         }
-        if (cb == 0) {
-          // delta of query r: from the lane that holds it in wave 0 (written below)
-          aux[(rowbase + r) * 4 + 0] = Mq;
-          aux[(rowbase + r) * 4 + 1] = D;
-        }
+        if (cb == 0) *reinterpret_cast<f32x4*>(aux + (rowbase + r) * 4) = f32x4{Mq, D, B.ax[q][2], 0.f};
       }
     }
-    if (wave == 0 && lane < 32 && ok) aux[(rowbase + row) * 4 + 2] = delta;
-    __syncthreads();   // shares, V tile and |k|^2 free for the next chunk
+    __syncthreads();   // shares and this chunk's buffer free
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_bw_key_causal: dk and dv, walking the segment's chunks from the last.
+// k_bw_key_causal: dk and dv, walking the range's chunks from the last.
 // R (lane = value column) and R^T (lane = feature) and rho hold the sums over
-// queries after the chunk (the segments after this one, then the later chunks).
+// queries after the chunk (the ranges after this one, then the later chunks).
 // Per chunk, wave w, coef_if = 2^(g_if - M_i) / D_i:
 //   dv_j = b_j.R + sum_{i >= j in chunk} (coef_i.b_j) dy_i
 //   db_jf = R_f.v_j - rho_f + sum_{i >= j in chunk} coef_if (dy_i.v_j - delta_i)
 //   H = b db,  dk_j = W^T H_j - k_j sum_f H_jf
-// then R, R^T, rho take the chunk's queries.
+// then R, R^T, rho take the chunk's queries.  Staging as for the query side.
 // ---------------------------------------------------------------------------
 template <int M>
 __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
@@ -878,25 +965,25 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
     float* __restrict__ dK, float* __restrict__ dV, int H, int n, int segs, int span) {
   constexpr int NW = M / 32, NT = 2 * M;
   __shared__ __attribute__((aligned(16))) uint16_t wl[M * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t dth[64 * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t dtl[64 * 64];
+  __shared__ __attribute__((aligned(16))) ChunkBuf buf[2];
   __shared__ __attribute__((aligned(16))) float ul[NW][32][kD];
   __shared__ float sl_h[NW][32];
-  __shared__ __attribute__((aligned(16))) f32x4 ax[32];
   __shared__ __attribute__((aligned(16))) float rl[NW][32];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5;
+  __shared__ __attribute__((aligned(16))) float cl[M];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5, ql = lane & 31;
   const int bh = blockIdx.x / segs, sg = blockIdx.x % segs, hh = bh % H;
   const int t0 = sg * span, t1 = min(n, t0 + span);
-  const int fb = 32 * wave, f = fb + (lane & 31);
+  const int fb = 32 * wave, f = fb + ql;
+  const size_t rowbase = static_cast<size_t>(bh) * n;
+  const int nch = (t1 - t0 + 31) / 32;
+  ChunkRegs<NT, false> pre;
+  chunk_load<NT, false>(pre, Q, K, V, dY, nullptr, aux, rowbase, t0 + 32 * (nch - 1), t1, t);
   const uint16_t* Wh = W + static_cast<size_t>(hh) * M * kD;
   for (int c = t; c < M * 8; c += NT)
     *reinterpret_cast<u32x4*>(wl + tile_at(c >> 3, c & 7)) = *reinterpret_cast<const u32x4*>(Wh + 8 * c);
-  u32x4 wop[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    wop[ks] = *reinterpret_cast<const u32x4*>(Wh + static_cast<size_t>(f) * kD + 16 * ks + 8 * h);
+  for (int i = t; i < M; i += NT) cl[i] = cfin[static_cast<size_t>(bh) * M + i];
   const float C = cfin[static_cast<size_t>(bh) * M + f];
-  // R (D[f][c]: lane = column), R^T (D[c][f]: lane = feature), rho: segments after this one
+  // R (D[f][c]: lane = column), R^T (D[c][f]: lane = feature), rho: ranges after this one
   f32x16 R[2], Rt[2];
   {
 #pragma unroll
@@ -910,134 +997,139 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
       for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          R[x][i] += PR[static_cast<size_t>(fb + drow(i, lane)) * kD + 32 * x + (lane & 31)];
+          R[x][i] += PR[static_cast<size_t>(fb + drow(i, lane)) * kD + 32 * x + ql];
           Rt[x][i] += PR[static_cast<size_t>(f) * kD + 32 * x + drow(i, lane)];
         }
       rho += part_rho[(static_cast<size_t>(bh) * segs + s) * M + f];
     }
     if (lane < 32) rl[wave][lane] = rho;
   }
+  chunk_store<NT, false>(pre, buf[0], t);
+  if (nch > 1) chunk_load<NT, false>(pre, Q, K, V, dY, nullptr, aux, rowbase, t0 + 32 * (nch - 2), t1, t);
   __syncthreads();
 
-  const size_t rowbase = static_cast<size_t>(bh) * n;
-  const int nch = (t1 - t0 + 31) / 32;
-  for (int ci = nch - 1; ci >= 0; --ci) {
+  int it = 0;
+  for (int ci = nch - 1; ci >= 0; --ci, ++it) {
     const int c0 = t0 + 32 * ci;
-    const int row = c0 + (lane & 31), tj = lane & 31;
-    const bool ok = row < t1;
-    // the chunk's dY as bf16 hi / lo tiles (rows 0..31) and (M_i, D_i, delta_i)
-    for (int c = t; c < 256; c += NT) {
-      const int r = c >> 3, ch = c & 7;
-      u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-      if (c0 + r < t1) split_row8(dY + (rowbase + c0 + r) * kD + 8 * ch, hi, lo);
-      *reinterpret_cast<u32x4*>(dth + swz(r, ch)) = hi;
-      *reinterpret_cast<u32x4*>(dtl + swz(r, ch)) = lo;
-    }
-    for (int r = t; r < 32; r += NT)
-      ax[r] = c0 + r < t1 ? *reinterpret_cast<const f32x4*>(aux + (rowbase + c0 + r) * 4) : f32x4{0.f, 1.f, 0.f, 0.f};
-    __syncthreads();   // dY tiles and aux visible
-    // per k-step: projections of the chunk's queries (FT and TF) and keys (FT),
-    // dY V^T (rows = queries, columns = keys (lane)) with dy to all its 24 bits,
-    // and R.v_j (FT: lane = key) from R^T with v's columns in register order
-    f32x16 pqf = {}, pqt = {}, pkf = {}, rvd = {}, ndv = {};
-    float kp = 0.f;
+    const ChunkBuf& B = buf[it & 1];
+    if (ci > 0) chunk_store<NT, false>(pre, buf[(it + 1) & 1], t);
+    const bool ok = c0 + ql < t1;
+    // the phases below are kept apart (sched_barrier) so that each one's operands
+    // are read from LDS when used and die after it
+    // 1. coef (FT: lane = query, and TF: lane = feature) and b (FT: lane = key);
+    // rho's new part
+    float bk[16], cff[16];
+    u32x4 cth[2], ctl[2];
+    float rs = 0.f;
+    {
+      f32x16 pqf = {}, pqt = {}, pkf = {};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int cc = 16 * ks + 8 * h;
-      u32x4 xq = {0u, 0u, 0u, 0u}, xk = xq, xvn = xq, xvp = xq, dnh = xq, dnm = xq, dnl = xq;
-      if (ok) {
-        xq = *reinterpret_cast<const u32x4*>(Q + (rowbase + row) * kD + cc);
-        xk = *reinterpret_cast<const u32x4*>(K + (rowbase + row) * kD + cc);
-        xvn = *reinterpret_cast<const u32x4*>(V + (rowbase + row) * kD + cc);
-        xvp = perm_bf16x8(V + (rowbase + row) * kD, ks, h);
-        split3_row8(dY + (rowbase + row) * kD + cc, dnh, dnm, dnl);
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 xq = tile_row8(B.q, ql, ks, h);
+        const u32x4 wa = rows_operand(wl, fb, lane, ks);
+        pqf = mfma_bf16(as_bf16x8(wa), as_bf16x8(xq), pqf);
+        pqt = mfma_bf16(as_bf16x8(xq), as_bf16x8(wa), pqt);
+        pkf = mfma_bf16(as_bf16x8(wa), as_bf16x8(tile_row8(B.k, ql, ks, h)), pkf);
+      }
+      const f32x4 aq = B.ax[ql];   // the lane's query
+      const float kk = B.kk[ql];   // the lane's key
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[fb + 8 * j + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          cff[i] = ok ? fast_exp2(fmaf(kLog2e, pqf[i], cc[e]) - aq[0]) * aq[1] : 0.f;
+          bk[i] = ok ? fast_exp2(kLog2e * fmaf(-0.5f, kk, pkf[i]) - cc[e]) : 0.f;
+        }
+      }
+      float cft[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = drow(i, lane);
+        const f32x4 a = B.ax[r];
+        const float x = fast_exp2(fmaf(kLog2e, pqt[i], C) - a[0]) * a[1];
+        cft[i] = c0 + r < t1 ? x : 0.f;   // register = query
+        rs = fmaf(cft[i], a[2], rs);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_lo_as_f32(xk[e]), hi = bf16_hi_as_f32(xk[e]);
-        kp = fmaf(lo, lo, kp);
-        kp = fmaf(hi, hi, kp);
+      for (int kb = 0; kb < 2; ++kb) split8(cft, kb, cth[kb], ctl[kb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. dv: carry b R + chunk P' dY (P'^T[i][j] = coef_i . b_j kept for i >= j),
+    // written as the wave's share; b stays on as its bf16 hi + lo
+    u32x4 bh_[2], bl_[2];
+    {
+      f32x16 pp = {};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        split8(bk, kb, bh_[kb], bl_[kb]);
+        u32x4 cfh, cfl;
+        split8(cff, kb, cfh, cfl);
+        pp = mfma_bf16(as_bf16x8(cfh), as_bf16x8(bh_[kb]), pp);
+        pp = mfma_bf16(as_bf16x8(cfh), as_bf16x8(bl_[kb]), pp);
+        pp = mfma_bf16(as_bf16x8(cfl), as_bf16x8(bh_[kb]), pp);
       }
-      const u32x4 wa = rows_operand(wl, fb, lane, ks);
-      pqf = mfma_bf16(as_bf16x8(wa), as_bf16x8(xq), pqf);
-      pqt = mfma_bf16(as_bf16x8(xq), as_bf16x8(wop[ks]), pqt);
-      pkf = mfma_bf16(as_bf16x8(wa), as_bf16x8(xk), pkf);
-      ndv = mfma_bf16(as_bf16x8(dnh), as_bf16x8(xvn), ndv);
-      ndv = mfma_bf16(as_bf16x8(dnm), as_bf16x8(xvn), ndv);
-      ndv = mfma_bf16(as_bf16x8(dnl), as_bf16x8(xvn), ndv);
-      u32x4 rh, rlo;
-      split8(Rt[ks >> 1], ks & 1, rh, rlo);
-      rvd = mfma_bf16(as_bf16x8(rh), as_bf16x8(xvp), rvd);
-      rvd = mfma_bf16(as_bf16x8(rlo), as_bf16x8(xvp), rvd);
-    }
-    const float kk = pair_sum(kp);
-    float cff[16], cft[16], bk[16];
-    const float mq = ax[tj][0], dq_ = ax[tj][1];
+      float pm[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 cc = *reinterpret_cast<const f32x4*>(&cfin[static_cast<size_t>(bh) * M + fb + 8 * j + 4 * h]);
+      for (int i = 0; i < 16; ++i) pm[i] = drow(i, lane) >= ql ? pp[i] : 0.f;
+      f32x16 adv[2] = {};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * j + e;
-        cff[i] = ok ? fast_exp2(fmaf(kLog2e, pqf[i], cc[e]) - mq) / dq_ : 0.f;   // lane = query
-        bk[i] = ok ? fast_exp2(kLog2e * fmaf(-0.5f, kk, pkf[i]) - cc[e]) : 0.f;   // lane = key
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4 ph, pl;
+        split8(pm, kb, ph, pl);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          u32x4 rh, rlo;
+          split8(R[dt], kb, rh, rlo);
+          adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rh), adv[dt]);
+          adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rlo), adv[dt]);
+          adv[dt] = mfma_bf16(as_bf16x8(bl_[kb]), as_bf16x8(rh), adv[dt]);
+          const u32x4 yh = v_operand(B.dh, 16 * kb, dt, lane), ym = v_operand(B.dm, 16 * kb, dt, lane);
+          adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(yh), adv[dt]);
+          adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(ym), adv[dt]);
+          adv[dt] = mfma_bf16(as_bf16x8(pl), as_bf16x8(yh), adv[dt]);
+        }
       }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = adv[dt][i];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. db (FT: lane = key): R.v - rho + coef^T N with R.v_j from R^T (v's columns
+    // in register order) and N = dY V^T - delta masked to i >= j (dy to all its 24
+    // bits); H = b db; the wave's dk share H W
+    f32x16 rvd = {};
+    {
+      f32x16 ndv = {};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = drow(i, lane);
-      const f32x4 a = ax[r];
-      cft[i] = c0 + r < t1 ? fast_exp2(fmaf(kLog2e, pqt[i], C) - a[0]) / a[1] : 0.f;   // lane = feature, reg = query
-    }
-    u32x4 bh_[2], bl_[2], cfh[2], cfl[2], cth[2], ctl[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      split8(bk, kb, bh_[kb], bl_[kb]);
-      split8(cff, kb, cfh[kb], cfl[kb]);
-      split8(cft, kb, cth[kb], ctl[kb]);
-    }
-    // P'^T[i][j] = coef_i . b_j (lane = key j, register = query i), kept for i >= j
-    f32x16 pp = {};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      pp = mfma_bf16(as_bf16x8(cfh[kb]), as_bf16x8(bh_[kb]), pp);
-      pp = mfma_bf16(as_bf16x8(cfh[kb]), as_bf16x8(bl_[kb]), pp);
-      pp = mfma_bf16(as_bf16x8(cfl[kb]), as_bf16x8(bh_[kb]), pp);
-    }
-    float pm[16], nm[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = drow(i, lane);   // query row of the register
-      pm[i] = r >= tj ? pp[i] : 0.f;
-      nm[i] = r >= tj ? ndv[i] - ax[r][2] : 0.f;
-    }
-    // dv: carry b R + chunk P' dY
-    f32x16 adv[2] = {};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 ph, pl;
-      split8(pm, kb, ph, pl);
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 xv = tile_row8(B.v, ql, ks, h);
+        ndv = mfma_bf16(as_bf16x8(tile_row8(B.dh, ql, ks, h)), as_bf16x8(xv), ndv);
+        ndv = mfma_bf16(as_bf16x8(tile_row8(B.dm, ql, ks, h)), as_bf16x8(xv), ndv);
+        ndv = mfma_bf16(as_bf16x8(tile_row8(B.dl, ql, ks, h)), as_bf16x8(xv), ndv);
         u32x4 rh, rlo;
-        split8(R[dt], kb, rh, rlo);
-        adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rh), adv[dt]);
-        adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rlo), adv[dt]);
-        adv[dt] = mfma_bf16(as_bf16x8(bl_[kb]), as_bf16x8(rh), adv[dt]);
-        const u32x4 yh = v_operand(dth, 16 * kb, dt, lane), yl = v_operand(dtl, 16 * kb, dt, lane);
-        adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(yh), adv[dt]);
-        adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(yl), adv[dt]);
-        adv[dt] = mfma_bf16(as_bf16x8(pl), as_bf16x8(yh), adv[dt]);
+        split8(Rt[ks >> 1], ks & 1, rh, rlo);
+        const u32x4 xvp = tile_perm8(B.v, ql, ks, h);
+        rvd = mfma_bf16(as_bf16x8(rh), as_bf16x8(xvp), rvd);
+        rvd = mfma_bf16(as_bf16x8(rlo), as_bf16x8(xvp), rvd);
       }
-    }
-    // db (FT: lane = key): R.v - rho + coef^T N
+      float nm[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 nh, nl;
-      split8(nm, kb, nh, nl);
-      rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nh), rvd);
-      rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nl), rvd);
-      rvd = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(nh), rvd);
+      for (int i = 0; i < 16; ++i) {
+        const int r = drow(i, lane);
+        const float x = ndv[i] - B.ax[r][2];
+        nm[i] = r >= ql ? x : 0.f;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4 nh, nl;
+        split8(nm, kb, nh, nl);
+        rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nh), rvd);
+        rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nl), rvd);
+        rvd = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(nh), rvd);
+      }
     }
     float Hh[16], Hs = 0.f;
 #pragma unroll
@@ -1045,8 +1137,11 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
       const f32x4 rr = *reinterpret_cast<const f32x4*>(&rl[wave][8 * j + 4 * h]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        Hh[4 * j + e] = bk[4 * j + e] * (rvd[4 * j + e] - rr[e]);
-        Hs += Hh[4 * j + e];
+        const int i = 4 * j + e;
+        const uint32_t wh = bh_[i >> 3][(i & 7) >> 1], wl_ = bl_[i >> 3][(i & 7) >> 1];
+        const float bv = (i & 1) ? bf16_hi_as_f32(wh) + bf16_hi_as_f32(wl_) : bf16_lo_as_f32(wh) + bf16_lo_as_f32(wl_);
+        Hh[i] = bv * (rvd[i] - rr[e]);
+        Hs += Hh[i];
       }
     }
     f32x16 adk[2] = {};
@@ -1061,63 +1156,63 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
         adk[dt] = mfma_bf16(as_bf16x8(hl_), as_bf16x8(wb), adk[dt]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     const float Hw = pair_sum(Hs);
-    // the chunk's queries join R, R^T and rho (after their use above)
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) rs = fmaf(cft[i], ax[drow(i, lane)][2], rs);
+    if (lane < 32) sl_h[wave][lane] = Hw;
+    // the reads of the chunk after next, in flight through the combines below
+    if (ci > 1) chunk_load<NT, false>(pre, Q, K, V, dY, nullptr, aux, rowbase, c0 - 64, t1, t);
+    // 4. the chunk's queries join R, R^T and rho (after their use above)
     rs = pair_sum(rs);
+    if (lane < 32) rl[wave][lane] += rs;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const u32x4 yh = v_operand(dth, 16 * kb, dt, lane), yl = v_operand(dtl, 16 * kb, dt, lane);
+        const u32x4 yh = v_operand(B.dh, 16 * kb, dt, lane), ym = v_operand(B.dm, 16 * kb, dt, lane);
         R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(yh), R[dt]);
-        R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(yl), R[dt]);
+        R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(ym), R[dt]);
         R[dt] = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(yh), R[dt]);
         Rt[dt] = mfma_bf16(as_bf16x8(yh), as_bf16x8(cth[kb]), Rt[dt]);
         Rt[dt] = mfma_bf16(as_bf16x8(yh), as_bf16x8(ctl[kb]), Rt[dt]);
-        Rt[dt] = mfma_bf16(as_bf16x8(yl), as_bf16x8(cth[kb]), Rt[dt]);
+        Rt[dt] = mfma_bf16(as_bf16x8(ym), as_bf16x8(cth[kb]), Rt[dt]);
       }
-    // dv shares, then dk shares, through LDS
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + (lane & 31)] = adv[dt][i];
-    if (lane < 32) sl_h[wave][lane] = Hw;
-    __syncthreads();
-    if (lane < 32) rl[wave][lane] += rs;
+    __syncthreads();   // dv shares visible
     constexpr int CPQ = 32 * kD / NT;
     const int q = t / (kD / CPQ), cb = (t % (kD / CPQ)) * CPQ, r = c0 + q;
     if (r < t1) {
 #pragma unroll
-      for (int e = 0; e < CPQ; ++e) {
-        float U = 0.f;
+      for (int e4 = 0; e4 < CPQ; e4 += 4) {
+        f32x4 U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < NW; ++w) U += ul[w][q][cb + e];
-        dV[(rowbase + r) * kD + cb + e] = U;
+        for (int w = 0; w < NW; ++w) U += *reinterpret_cast<const f32x4*>(&ul[w][q][cb + e4]);
+        *reinterpret_cast<f32x4*>(dV + (rowbase + r) * kD + cb + e4) = U;
       }
     }
-    __syncthreads();
+    __syncthreads();   // dv shares read
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + (lane & 31)] = adk[dt][i];
-    __syncthreads();
+      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = adk[dt][i];
+    __syncthreads();   // dk shares visible
     if (r < t1) {
       float hs = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) hs += sl_h[w][q];
 #pragma unroll
-      for (int e = 0; e < CPQ; ++e) {
-        float U = 0.f;
+      for (int e4 = 0; e4 < CPQ; e4 += 4) {
+        f32x4 U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < NW; ++w) U += ul[w][q][cb + e];
-        const float kv = __uint_as_float(static_cast<uint32_t>(K[(rowbase + r) * kD + cb + e]) << 16);
-        dK[(rowbase + r) * kD + cb + e] = U - kv * hs;
+        for (int w = 0; w < NW; ++w) U += *reinterpret_cast<const f32x4*>(&ul[w][q][cb + e4]);
+        const u32x2 kw = *reinterpret_cast<const u32x2*>(B.k + swz(q, (cb + e4) >> 3) + ((cb + e4) & 7));
+        const float kv[4] = {bf16_lo_as_f32(kw[0]), bf16_hi_as_f32(kw[0]), bf16_lo_as_f32(kw[1]),
+                             bf16_hi_as_f32(kw[1])};
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = U[e] - kv[e] * hs;
+        *reinterpret_cast<f32x4*>(dK + (rowbase + r) * kD + cb + e4) = o;
       }
     }
-    __syncthreads();
+    __syncthreads();   // dk shares and this chunk's buffer free
   }
 }
 
