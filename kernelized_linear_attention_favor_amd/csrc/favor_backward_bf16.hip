@@ -578,11 +578,11 @@ __global__ __launch_bounds__(512) void k_bw_key(const uint16_t* __restrict__ K, 
 // and i >= j (R, rho: suffix sums of the queries).  Both kernels walk one
 // segment of one (b, h) in chunks of 32 tokens; M/32 waves, wave w owns
 // features [32w, 32w+32).  Each wave forms its features' share of every
-// per-token quantity; the shares are summed in wave order in LDS.  The state is
-// kept transposed where it is an A operand (S^T[c][f], R^T[c][f]: lane =
-// feature, register = value column), so the value columns of dy and v are read
-// in the MFMA register order: k-block kb of 16 columns, lane half h: columns
-// 16kb + 4h .. +3 and 16kb + 8 + 4h .. +3.
+// per-token quantity; the shares are summed in wave order in LDS.  The query
+// side keeps S transposed (S^T[c][f]: lane = feature, register = value column),
+// the A operand of S.dy, so the value columns of dy are read in the MFMA
+// register order: k-block kb of 16 columns, lane half h: columns 16kb + 4h .. +3
+// and 16kb + 8 + 4h .. +3.
 // ===========================================================================
 // bf16 (1, 0) per register pair of a k-block: 1 where key drow <= query, for the
 // B operand of the running sum over the keys of the chunk.
@@ -949,13 +949,14 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
 
 // ---------------------------------------------------------------------------
 // k_bw_key_causal: dk and dv, walking the range's chunks from the last.
-// R (lane = value column) and R^T (lane = feature) and rho hold the sums over
-// queries after the chunk (the ranges after this one, then the later chunks).
+// R (lane = value column) and rho hold the sums over queries after the chunk
+// (the ranges after this one, then the later chunks); R.v reads R a feature per
+// lane after a pass through LDS.
 // Per chunk, wave w, coef_if = 2^(g_if - M_i) / D_i:
 //   dv_j = b_j.R + sum_{i >= j in chunk} (coef_i.b_j) dy_i
 //   db_jf = R_f.v_j - rho_f + sum_{i >= j in chunk} coef_if (dy_i.v_j - delta_i)
 //   H = b db,  dk_j = W^T H_j - k_j sum_f H_jf
-// then R, R^T, rho take the chunk's queries.  Staging as for the query side.
+// then R and rho take the chunk's queries.  Staging as for the query side.
 // ---------------------------------------------------------------------------
 template <int M>
 __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
@@ -983,23 +984,20 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
     *reinterpret_cast<u32x4*>(wl + tile_at(c >> 3, c & 7)) = *reinterpret_cast<const u32x4*>(Wh + 8 * c);
   for (int i = t; i < M; i += NT) cl[i] = cfin[static_cast<size_t>(bh) * M + i];
   const float C = cfin[static_cast<size_t>(bh) * M + f];
-  // R (D[f][c]: lane = column), R^T (D[c][f]: lane = feature), rho: ranges after this one
-  f32x16 R[2], Rt[2];
+  // R (D[f][c]: lane = column) and rho: ranges after this one
+  f32x16 R[2];
   {
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) R[x][i] = Rt[x][i] = 0.f;
+      for (int i = 0; i < 16; ++i) R[x][i] = 0.f;
     float rho = 0.f;
     for (int s = segs - 1; s > sg; --s) {
       const float* PR = part_R + (static_cast<size_t>(bh) * segs + s) * M * kD;
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          R[x][i] += PR[static_cast<size_t>(fb + drow(i, lane)) * kD + 32 * x + ql];
-          Rt[x][i] += PR[static_cast<size_t>(f) * kD + 32 * x + drow(i, lane)];
-        }
+        for (int i = 0; i < 16; ++i) R[x][i] += PR[static_cast<size_t>(fb + drow(i, lane)) * kD + 32 * x + ql];
       rho += part_rho[(static_cast<size_t>(bh) * segs + s) * M + f];
     }
     if (lane < 32) rl[wave][lane] = rho;
@@ -1016,6 +1014,27 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
     const bool ok = c0 + ql < t1;
     // the phases below are kept apart (sched_barrier) so that each one's operands
     // are read from LDS when used and die after it
+    // 0. R.v_j (FT: lane = key): R passes through the wave's own share rows (free
+    // until the dv share below) to be read back a feature per lane, the A operand
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = R[dt][i];
+    __builtin_amdgcn_wave_barrier();
+    f32x16 rvd = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x4 ra = *reinterpret_cast<const f32x4*>(&ul[wave][ql][16 * ks + 8 * h]);
+      const f32x4 rb = *reinterpret_cast<const f32x4*>(&ul[wave][ql][16 * ks + 8 * h + 4]);
+      const float x[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+      u32x4 rh, rlo;
+      split8(x, 0, rh, rlo);
+      const u32x4 xv = tile_row8(B.v, ql, ks, h);
+      rvd = mfma_bf16(as_bf16x8(rh), as_bf16x8(xv), rvd);
+      rvd = mfma_bf16(as_bf16x8(rlo), as_bf16x8(xv), rvd);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     // 1. coef (FT: lane = query, and TF: lane = feature) and b (FT: lane = key);
     // rho's new part
     float bk[16], cff[16];
@@ -1097,10 +1116,8 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
         for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = adv[dt][i];
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 3. db (FT: lane = key): R.v - rho + coef^T N with R.v_j from R^T (v's columns
-    // in register order) and N = dY V^T - delta masked to i >= j (dy to all its 24
-    // bits); H = b db; the wave's dk share H W
-    f32x16 rvd = {};
+    // 3. db (FT: lane = key): R.v - rho + coef^T N with N = dY V^T - delta masked to
+    // i >= j (dy to all its 24 bits); H = b db; the wave's dk share H W
     {
       f32x16 ndv = {};
 #pragma unroll
@@ -1109,11 +1126,6 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
         ndv = mfma_bf16(as_bf16x8(tile_row8(B.dh, ql, ks, h)), as_bf16x8(xv), ndv);
         ndv = mfma_bf16(as_bf16x8(tile_row8(B.dm, ql, ks, h)), as_bf16x8(xv), ndv);
         ndv = mfma_bf16(as_bf16x8(tile_row8(B.dl, ql, ks, h)), as_bf16x8(xv), ndv);
-        u32x4 rh, rlo;
-        split8(Rt[ks >> 1], ks & 1, rh, rlo);
-        const u32x4 xvp = tile_perm8(B.v, ql, ks, h);
-        rvd = mfma_bf16(as_bf16x8(rh), as_bf16x8(xvp), rvd);
-        rvd = mfma_bf16(as_bf16x8(rlo), as_bf16x8(xvp), rvd);
       }
       float nm[16];
 #pragma unroll
@@ -1161,7 +1173,7 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
     if (lane < 32) sl_h[wave][lane] = Hw;
     // the reads of the chunk after next, in flight through the combines below
     if (ci > 1) chunk_load<NT, false>(pre, Q, K, V, dY, nullptr, aux, rowbase, c0 - 64, t1, t);
-    // 4. the chunk's queries join R, R^T and rho (after their use above)
+    // 4. the chunk's queries join R and rho (after their use above)
     rs = pair_sum(rs);
     if (lane < 32) rl[wave][lane] += rs;
 #pragma unroll
@@ -1172,9 +1184,6 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
         R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(yh), R[dt]);
         R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(ym), R[dt]);
         R[dt] = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(yh), R[dt]);
-        Rt[dt] = mfma_bf16(as_bf16x8(yh), as_bf16x8(cth[kb]), Rt[dt]);
-        Rt[dt] = mfma_bf16(as_bf16x8(yh), as_bf16x8(ctl[kb]), Rt[dt]);
-        Rt[dt] = mfma_bf16(as_bf16x8(ym), as_bf16x8(cth[kb]), Rt[dt]);
       }
     __syncthreads();   // dv shares visible
     constexpr int CPQ = 32 * kD / NT;
