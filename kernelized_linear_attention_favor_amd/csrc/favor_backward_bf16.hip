@@ -1305,7 +1305,9 @@ BwPlan bw_plan(int B, int H, int n, int m, int causal) {
   p.m = m;
   p.causal = causal;
   const int BH = B * H;
-  int s = (256 + BH - 1) / BH;
+  // about two workgroups per CU for the key-range kernels of the non-causal pass
+  // (they fit twice); one segment walk per CU for the causal pass
+  int s = ((causal ? 256 : 512) + BH - 1) / BH;
   const int tiles = (n + 63) / 64;
   if (s > tiles) s = tiles;
   if (s < 1) s = 1;
