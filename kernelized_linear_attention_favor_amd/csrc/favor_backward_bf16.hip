@@ -598,13 +598,23 @@ __device__ __forceinline__ u32x4 tril_ones(int kb, int q, int lane) {
 
 // One 32-token chunk of a (b, h) in LDS, staged once per workgroup: q, k, v and
 // dy (as three bf16 words hi, mid, lo) in swizzled row-major [32][64] bf16 tiles,
-// |k|^2 per key, and per token (M_i, 1 / D_i, delta_i) (key side) or delta_i in
-// element 2 (query side, delta = dy.y formed here).  Rows past the end are zero.
+// |k|^2 per key, and per token delta_i (dy.y, formed here on the query side) and,
+// on the key side, M_i and 1 / D_i; each a separate array, so that the 4
+// consecutive tokens of an MFMA register group come in one vector read.  Rows
+// past the end are zero (1 / D_i: one).
 struct ChunkBuf {
   uint16_t q[32 * 64], k[32 * 64], v[32 * 64], dh[32 * 64], dm[32 * 64], dl[32 * 64];
-  f32x4 ax[32];
-  float kk[32];
+  float am[32], ar[32], ad[32], kk[32];
 };
+// Values of a per-token array for the 16 rows drow(i, lane) of a D tile.
+__device__ __forceinline__ void rows16(const float* a, int h, float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a + 8 * j + 4 * h);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * j + e] = v[e];
+  }
+}
 
 // The chunk's global reads, held in registers between chunks so that they are in
 // flight while the previous chunk computes.  16-byte pieces: 768 of q, k, v
@@ -695,12 +705,16 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<NT, QSIDE>& R, Chunk
         d = fmaf(x[3], y[3], d);
         d = sum8(d);
         d += __shfl_xor(d, 8);
-        if ((t & 15) == 0) B.ax[r] = f32x4{0.f, 0.f, d, 0.f};
+        if ((t & 15) == 0) B.ad[r] = d;
       }
     }
   }
   if constexpr (!QSIDE) {   // (M_i, 1 / D_i, delta_i)
-    if (t < 32) B.ax[t] = f32x4{R.ax[0], 1.f / R.ax[1], R.ax[2], 0.f};
+    if (t < 32) {
+      B.am[t] = R.ax[0];
+      B.ar[t] = 1.f / R.ax[1];
+      B.ad[t] = R.ax[2];
+    }
   }
 }
 
@@ -790,11 +804,12 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         pkt = mfma_bf16(as_bf16x8(tile_row8(B.k, ql, ks, h)), as_bf16x8(rows_operand(wl, fb, lane, ks)), pkt);
-      float b[16];
+      float b[16], kr[16];
+      rows16(B.kk, h, kr);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = drow(i, lane);
-        const float x = fast_exp2(kLog2e * fmaf(-0.5f, B.kk[r], pkt[i]) - C);
+        const float x = fast_exp2(kLog2e * fmaf(-0.5f, kr[i], pkt[i]) - C);
         b[i] = c0 + r < t1 ? x : 0.f;
         zs += b[i];
       }
@@ -805,7 +820,7 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
     // 2. the chunk's part of T - z delta and of z (FT: lane = query): b^T N with
     // N = V dY^T - delta masked to keys j <= i (v_j.dy_i - delta_i = dy_i.(v_j - y_i),
     // formed before the product with b; dy to all its 24 bits)
-    const float delta = B.ax[ql][2];
+    const float delta = B.ad[ql];
     f32x16 tacc = {}, zacc = {};
     {
       f32x16 mvd = {};
@@ -940,7 +955,7 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
           for (int e = 0; e < 4; ++e) o[e] = (U[e] - qv[e] * u) * rD;
           *reinterpret_cast<f32x4*>(dQ + (rowbase + r) * kD + cb + e4) = o;
         }
-        if (cb == 0) *reinterpret_cast<f32x4*>(aux + (rowbase + r) * 4) = f32x4{Mq, D, B.ax[q][2], 0.f};
+        if (cb == 0) *reinterpret_cast<f32x4*>(aux + (rowbase + r) * 4) = f32x4{Mq, D, B.ad[q], 0.f};
       }
     }
     __syncthreads();   // shares and this chunk's buffer free
@@ -1050,26 +1065,28 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
         pqt = mfma_bf16(as_bf16x8(xq), as_bf16x8(wa), pqt);
         pkf = mfma_bf16(as_bf16x8(wa), as_bf16x8(tile_row8(B.k, ql, ks, h)), pkf);
       }
-      const f32x4 aq = B.ax[ql];   // the lane's query
-      const float kk = B.kk[ql];   // the lane's key
+      const float aqm = B.am[ql], aqr = B.ar[ql];   // the lane's query
+      const float kk = B.kk[ql];                     // the lane's key
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[fb + 8 * j + 4 * h]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
-          cff[i] = ok ? fast_exp2(fmaf(kLog2e, pqf[i], cc[e]) - aq[0]) * aq[1] : 0.f;
+          cff[i] = ok ? fast_exp2(fmaf(kLog2e, pqf[i], cc[e]) - aqm) * aqr : 0.f;
           bk[i] = ok ? fast_exp2(kLog2e * fmaf(-0.5f, kk, pkf[i]) - cc[e]) : 0.f;
         }
       }
-      float cft[16];
+      float cft[16], rm[16], rr[16], rd[16];
+      rows16(B.am, h, rm);
+      rows16(B.ar, h, rr);
+      rows16(B.ad, h, rd);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = drow(i, lane);
-        const f32x4 a = B.ax[r];
-        const float x = fast_exp2(fmaf(kLog2e, pqt[i], C) - a[0]) * a[1];
+        const float x = fast_exp2(fmaf(kLog2e, pqt[i], C) - rm[i]) * rr[i];
         cft[i] = c0 + r < t1 ? x : 0.f;   // register = query
-        rs = fmaf(cft[i], a[2], rs);
+        rs = fmaf(cft[i], rd[i], rs);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) split8(cft, kb, cth[kb], ctl[kb]);
@@ -1127,12 +1144,12 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
         ndv = mfma_bf16(as_bf16x8(tile_row8(B.dm, ql, ks, h)), as_bf16x8(xv), ndv);
         ndv = mfma_bf16(as_bf16x8(tile_row8(B.dl, ql, ks, h)), as_bf16x8(xv), ndv);
       }
-      float nm[16];
+      float nm[16], rd[16];
+      rows16(B.ad, h, rd);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = drow(i, lane);
-        const float x = ndv[i] - B.ax[r][2];
-        nm[i] = r >= ql ? x : 0.f;
+        const float x = ndv[i] - rd[i];
+        nm[i] = drow(i, lane) >= ql ? x : 0.f;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {

@@ -107,6 +107,18 @@ def test_backward_C2_shape_and_large_inputs(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_backward_C5_low_rank(causal):
+    """The vision stand-in's low-rank q, k (m = 128, H = 12) at n = 1024."""
+    x = fi.make_inputs(fi.config("C5", B=1, n=1024))
+    dy = np.random.default_rng(13).standard_normal(x["q"].shape).astype(np.float32)
+    got = gpu_backward(x, fwd(x, causal), dy, causal=causal)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy, causal=causal)
+    for g, w, name in zip(got, want, ("dq", "dk", "dv")):
+        assert np.all(np.isfinite(g)), name
+        assert gerr(g, w) < TOL, (name, gerr(g, w))
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_backward_C3_shape_sampled(causal):
     """B=4, H=8, n=16384, m=256: the benchmark's shape; rows sampled per (b, h)."""
     cfg = fi.config("C3")
