@@ -17,8 +17,8 @@
 // feature for the whole head, so these are plain bounded sums in fp32; a
 // feature's key exponents may spread up to ~2^126 below its largest.
 //
-// Kernels (non-causal): k_bw_keys<MAX> (C_f partials), k_bw_keys<STATE> (S, z
-// partials), k_bw_merge (sum, written as bf16 hi + lo row-major tiles),
+// Kernels (non-causal): k_bw_keys (S, z partials with a running shift per
+// range), k_bw_merge (C_f; the sum, written as bf16 hi + lo row-major tiles),
 // k_bw_query (dq; M_i, D_i, delta_i per query), k_bw_rstate (R, rho partials),
 // k_bw_merge, k_bw_key (dk, dv).  bf16 MFMA with fp32 accumulation; fp32
 // operands enter as bf16 hi + lo pairs, the bf16 inputs exactly.
@@ -73,24 +73,27 @@ __device__ __forceinline__ void split_row8(const float* p, u32x4& hi, u32x4& lo)
 }
 
 // ---------------------------------------------------------------------------
-// k_bw_keys<M, PASS>: one key range of one (b, h); M/32 waves, wave w owns
-// features [32w, 32w+32).  Per 64 keys: K (and V) tiles and |k|^2 in LDS; per
-// 32 keys each wave projects to a TF tile (lane = feature, register = key).
-//   PASS 0: the largest e_jf of the range per feature -> cpart.
-//   PASS 1: b_jf = 2^(e_jf - C_f) (C_f = max over ranges of cpart); z += b,
-//           S += b^T V with b as bf16 hi + lo -> part_S, part_z.
+// k_bw_keys<M>: the key state of one key range of one (b, h); M/32 waves, wave w
+// owns features [32w, 32w+32).  Per 64 keys: K and V tiles and |k|^2 in LDS;
+// each wave projects the two 32-key halves to TF tiles (lane = feature,
+// register = key), e_jf = log2e (w_f.k_j - |k_j|^2/2).  The range keeps a
+// running maximum m_f of e_jf: when a half raises it, z and S so far are scaled
+// by 2^(m_old - m_new) (a factor per feature; S's registers, a feature each,
+// take theirs through the wave's LDS row).  Then b_jf = 2^(e_jf - m_f), z += b,
+// S += b^T V with b as bf16 hi + lo.  Out: part_S, part_z and m_f -> cpart, so
+// that a range's sums times 2^(m_f - C_f) are its share at any shift C_f >= m_f.
 // ---------------------------------------------------------------------------
-template <int M, int PASS>
-__global__ __launch_bounds__(2 * M) void k_bw_keys(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+template <int M>
+__global__ __launch_bounds__(2 * M) __attribute__((amdgpu_waves_per_eu(M == 256 ? 4 : 1))) void k_bw_keys(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                    const uint16_t* __restrict__ W, float* __restrict__ cpart,
                                                    float* __restrict__ part_S, float* __restrict__ part_z, int H,
                                                    int n, int splits, int span) {
-  constexpr int NT = 2 * M;
-  constexpr int NMAT = PASS == 0 ? 1 : 2;          // K only, or K and V
-  constexpr int CPT = 512 * NMAT / NT;
+  constexpr int NT = 2 * M, NW = M / 32;
+  constexpr int CPT = 1024 / NT;
   __shared__ __attribute__((aligned(16))) uint16_t kt[64 * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[PASS == 0 ? 8 : 64 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[64 * 64];
   __shared__ float kk[64];
+  __shared__ __attribute__((aligned(16))) float fac[NW][32];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5;
   const int bh = blockIdx.x / splits, sp = blockIdx.x % splits, hh = bh % H;
   const int j0 = sp * span, j1 = min(n, j0 + span);
@@ -99,11 +102,6 @@ __global__ __launch_bounds__(2 * M) void k_bw_keys(const uint16_t* __restrict__ 
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     wop[ks] = *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD + 16 * ks + 8 * h);
-  float C = 0.f;
-  if constexpr (PASS == 1) {
-    C = kNegInf;
-    for (int s = 0; s < splits; ++s) C = fmaxf(C, cpart[(static_cast<size_t>(bh) * splits + s) * M + f]);
-  }
 
   const size_t rowbase = static_cast<size_t>(bh) * n;
   u32x4 pre[CPT];
@@ -117,7 +115,7 @@ __global__ __launch_bounds__(2 * M) void k_bw_keys(const uint16_t* __restrict__ 
   };
 
   f32x16 acc[2] = {};
-  float zp = 0.f, mx = kNegInf;
+  float zp = 0.f, mrun = kNegInf;
   if (j0 < j1) fetch(j0);
   for (int tok0 = j0; tok0 < j1; tok0 += 64) {
     __syncthreads();
@@ -128,76 +126,92 @@ __global__ __launch_bounds__(2 * M) void k_bw_keys(const uint16_t* __restrict__ 
     }
     __syncthreads();
     if (t < 64) {
-      float s = 0.f;
+      float sq = 0.f;
 #pragma unroll
       for (int ch = 0; ch < 8; ++ch) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(kt + swz(t, ch));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float lo = bf16_lo_as_f32(x[e]), hi = bf16_hi_as_f32(x[e]);
-          s = fmaf(lo, lo, s);
-          s = fmaf(hi, hi, s);
+          sq = fmaf(lo, lo, sq);
+          sq = fmaf(hi, hi, sq);
         }
       }
-      kk[t] = s;
+      kk[t] = sq;
     }
     __syncthreads();
     if (tok0 + 64 < j1) fetch(tok0 + 64);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
+      // exponents of this 32-key half and their maximum per feature
       f32x16 pr = {};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4 xk = *reinterpret_cast<const u32x4*>(kt + swz(32 * st + (lane & 31), 2 * ks + h));
         pr = mfma_bf16(as_bf16x8(xk), as_bf16x8(wop[ks]), pr);
       }
-      float b[16];
+      float e[16], tm = kNegInf;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 32 * st + drow(i, lane);
-        const float e = kLog2e * fmaf(-0.5f, kk[r], pr[i]);
-        const bool ok = tok0 + r < j1;
-        if constexpr (PASS == 0) {
-          mx = ok ? fmaxf(mx, e) : mx;
-        } else {
-          b[i] = ok ? fast_exp2(e - C) : 0.f;
-          zp += b[i];
-        }
+        e[i] = tok0 + r < j1 ? kLog2e * fmaf(-0.5f, kk[r], pr[i]) : kNegInf;
+        tm = fmaxf(tm, e[i]);
       }
-      if constexpr (PASS == 1) {
+      tm = pair_max(tm);
+      // the running maximum and the rescale of the sums so far (a factor of one
+      // when the maximum stays; the first half scales the zero sums by zero)
+      const float mnew = fmaxf(mrun, tm);
+      const float sc = fast_exp2(mrun - mnew);
+      mrun = mnew;
+      zp *= sc;
+      if (lane < 32) fac[wave][lane] = sc;
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          u32x4 ahi, alo;
-          split8(b, kb, ahi, alo);
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(&fac[wave][8 * j + 4 * h]);
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const u32x4 vb = v_operand(vt, 32 * st + 16 * kb, dt, lane);
-            acc[dt] = mfma_bf16(as_bf16x8(ahi), as_bf16x8(vb), acc[dt]);
-            acc[dt] = mfma_bf16(as_bf16x8(alo), as_bf16x8(vb), acc[dt]);
-          }
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[dt][4 * j + q] *= v4[q];
+      }
+      __builtin_amdgcn_wave_barrier();
+      float bv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        bv[i] = fast_exp2(e[i] - mrun);   // 0 for keys past the end
+        zp += bv[i];
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4 ahi, alo;
+        split8(bv, kb, ahi, alo);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const u32x4 vb = v_operand(vt, 32 * st + 16 * kb, dt, lane);
+          acc[dt] = mfma_bf16(as_bf16x8(ahi), as_bf16x8(vb), acc[dt]);
+          acc[dt] = mfma_bf16(as_bf16x8(alo), as_bf16x8(vb), acc[dt]);
         }
       }
     }
   }
   const size_t slot = static_cast<size_t>(bh) * splits + sp;
-  if constexpr (PASS == 0) {
-    mx = pair_max(mx);
-    if (lane < 32) cpart[slot * M + f] = mx;
-  } else {
-    float* PS = part_S + slot * M * kD;
+  float* PS = part_S + slot * M * kD;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) PS[(fb + drow(i, lane)) * kD + 32 * dt + (lane & 31)] = acc[dt][i];
-    zp = pair_sum(zp);
-    if (lane < 32) part_z[slot * M + f] = zp;
+    for (int i = 0; i < 16; ++i) PS[(fb + drow(i, lane)) * kD + 32 * dt + (lane & 31)] = acc[dt][i];
+  zp = pair_sum(zp);
+  if (lane < 32) {
+    part_z[slot * M + f] = zp;
+    cpart[slot * M + f] = mrun;
   }
 }
 
 // ---------------------------------------------------------------------------
 // k_bw_merge: the ranges of one (b, h) summed in index order; the m x 64 sum as
-// bf16 hi + lo tiled arrays, the m-vector in fp32, and (if cpart) the largest
-// key exponent per feature over the ranges.  One workgroup per (b, h, 4 rows).
+// bf16 hi + lo tiled arrays and the m-vector in fp32.  With cpart (the ranges'
+// key shifts m_r): C_f = max_r m_r -> cfin, and range r enters at 2^(m_r - C_f).
+// One workgroup per (b, h, 4 rows).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bw_merge(const float* __restrict__ part, const float* __restrict__ pvec,
                                                   uint16_t* __restrict__ tiles, float* __restrict__ vec,
@@ -205,10 +219,21 @@ __global__ __launch_bounds__(256) void k_bw_merge(const float* __restrict__ part
                                                   int M, int splits) {
   const int q4 = M / 4;
   const int bh = blockIdx.x / q4, r = (blockIdx.x % q4) * 4 + (threadIdx.x >> 6), c = threadIdx.x & 63;
-  float a = 0.f;
+  // with cpart: each range's sums carry the shift m_r, and enter at 2^(m_r - C)
+  float C = 0.f;
+  if (cpart) {
+    C = kNegInf;
+    for (int sp = 0; sp < splits; ++sp) C = fmaxf(C, cpart[(static_cast<size_t>(bh) * splits + sp) * M + r]);
+  }
+  float a = 0.f, s = 0.f;
   const float* P = part + (static_cast<size_t>(bh) * splits * M + r) * kD + c;
+  const float* Z = pvec + static_cast<size_t>(bh) * splits * M + r;
 #pragma unroll 8
-  for (int sp = 0; sp < splits; ++sp) a += P[static_cast<size_t>(sp) * M * kD];
+  for (int sp = 0; sp < splits; ++sp) {
+    const float w = cpart ? fast_exp2(cpart[(static_cast<size_t>(bh) * splits + sp) * M + r] - C) : 1.f;
+    a = fmaf(P[static_cast<size_t>(sp) * M * kD], w, a);
+    s = fmaf(Z[static_cast<size_t>(sp) * M], w, s);
+  }
   const uint32_t pk = pack_bf16(a, 0.f);
   const uint16_t hi = static_cast<uint16_t>(pk & 0xffffu);
   const uint16_t lo = static_cast<uint16_t>(pack_bf16(a - bf16_lo_as_f32(pk), 0.f) & 0xffffu);
@@ -216,14 +241,8 @@ __global__ __launch_bounds__(256) void k_bw_merge(const float* __restrict__ part
   tiles[base] = hi;
   tiles[static_cast<size_t>(BH) * M * kD + base] = lo;
   if (c == 0) {
-    float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp) s += pvec[(static_cast<size_t>(bh) * splits + sp) * M + r];
     vec[static_cast<size_t>(bh) * M + r] = s;
-    if (cpart) {
-      float m = kNegInf;
-      for (int sp = 0; sp < splits; ++sp) m = fmaxf(m, cpart[(static_cast<size_t>(bh) * splits + sp) * M + r]);
-      cfin[static_cast<size_t>(bh) * M + r] = m;
-    }
+    if (cpart) cfin[static_cast<size_t>(bh) * M + r] = C;
   }
 }
 
@@ -744,8 +763,9 @@ template <int M>
 __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ W, const float* __restrict__ Y, const float* __restrict__ dY,
-    const float* __restrict__ cfin, const float* __restrict__ part_S, const float* __restrict__ part_z,
-    float* __restrict__ dQ, float* __restrict__ aux, int H, int n, int segs, int span) {
+    const float* __restrict__ cfin, const float* __restrict__ cpart, const float* __restrict__ part_S,
+    const float* __restrict__ part_z, float* __restrict__ dQ, float* __restrict__ aux, int H, int n, int segs,
+    int span) {
   constexpr int NW = M / 32, NT = 2 * M;
   __shared__ __attribute__((aligned(16))) uint16_t wl[M * kD];
   __shared__ __attribute__((aligned(16))) ChunkBuf buf[2];
@@ -773,13 +793,15 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
 #pragma unroll
       for (int i = 0; i < 16; ++i) St[ct][i] = 0.f;
     float z = 0.f;
-    for (int s = 0; s < sg; ++s) {
-      const float* PS = part_S + (static_cast<size_t>(bh) * segs + s) * M * kD + static_cast<size_t>(f) * kD;
+    for (int s = 0; s < sg; ++s) {   // each range's sums at its own shift m_s: times 2^(m_s - C)
+      const size_t slot = static_cast<size_t>(bh) * segs + s;
+      const float w = fast_exp2(cpart[slot * M + f] - C);
+      const float* PS = part_S + slot * M * kD + static_cast<size_t>(f) * kD;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) St[ct][i] += PS[32 * ct + drow(i, lane)];
-      z += part_z[(static_cast<size_t>(bh) * segs + s) * M + f];
+        for (int i = 0; i < 16; ++i) St[ct][i] = fmaf(PS[32 * ct + drow(i, lane)], w, St[ct][i]);
+      z = fmaf(part_z[slot * M + f], w, z);
     }
     if (lane < 32) zl[wave][lane] = z;
   }
@@ -1256,15 +1278,13 @@ hipError_t launch_causal_m(const BwPlan& p, const uint16_t* q, const uint16_t* k
   float* aux = reinterpret_cast<float*>(base + p.off_aux);
   const int BH = p.B * p.H;
   const dim3 gs(BH * p.splits), bs(2 * M);
-  auto kmax = k_bw_keys<M, 0>;
-  FAVOR_LAUNCH("k_bw_kmax", kmax, gs, bs, 0, s, k, v, W, cpart, pS, pz, p.H, p.n, p.splits, p.span);
-  auto kst = k_bw_keys<M, 1>;
+  auto kst = k_bw_keys<M>;
   FAVOR_LAUNCH("k_bw_kstate", kst, gs, bs, 0, s, k, v, W, cpart, pS, pz, p.H, p.n, p.splits, p.span);
   FAVOR_LAUNCH("k_bw_cmax", k_bw_cmax, dim3((BH * p.m + 255) / 256), dim3(256), 0, s, cpart, cfin, BH * p.m, p.m,
                p.splits);
   auto kq = k_bw_query_causal<M>;
-  FAVOR_LAUNCH("k_bw_query_causal", kq, gs, bs, 0, s, q, k, v, W, y, dy, cfin, pS, pz, dq, aux, p.H, p.n, p.splits,
-               p.span);
+  FAVOR_LAUNCH("k_bw_query_causal", kq, gs, bs, 0, s, q, k, v, W, y, dy, cfin, cpart, pS, pz, dq, aux, p.H, p.n,
+               p.splits, p.span);
   auto kr = k_bw_rstate<M>;
   FAVOR_LAUNCH("k_bw_rstate", kr, gs, bs, 0, s, q, dy, W, cfin, aux, pR, prho, p.H, p.n, p.splits, p.span);
   auto kc = k_bw_key_causal<M>;
@@ -1288,9 +1308,7 @@ hipError_t launch_m(const BwPlan& p, const uint16_t* q, const uint16_t* k, const
   float* aux = reinterpret_cast<float*>(base + p.off_aux);
   const int BH = p.B * p.H;
   const dim3 gs(BH * p.splits), bs(2 * M);
-  auto kmax = k_bw_keys<M, 0>;
-  FAVOR_LAUNCH("k_bw_kmax", kmax, gs, bs, 0, s, k, v, W, cpart, pS, pz, p.H, p.n, p.splits, p.span);
-  auto kst = k_bw_keys<M, 1>;
+  auto kst = k_bw_keys<M>;
   FAVOR_LAUNCH("k_bw_kstate", kst, gs, bs, 0, s, k, v, W, cpart, pS, pz, p.H, p.n, p.splits, p.span);
   FAVOR_LAUNCH("k_bw_merge", k_bw_merge, dim3(BH * (M / 4)), dim3(256), 0, s, pS, pz, stl, zg, cpart, cfin, BH, M,
                p.splits);
