@@ -403,7 +403,7 @@ __global__ __launch_bounds__(512) void k_bw_query(const uint16_t* __restrict__ Q
 // ---------------------------------------------------------------------------
 // k_bw_rstate: R = sum_i (a_i / D_i) dy_i^T and rho = sum_i (a_i / D_i) delta_i
 // over one query range; M/32 waves, wave w owns features [32w, 32w+32).  Per 64
-// queries: Q, dY (as bf16 hi and lo tiles) and (M_i, D_i, delta_i) in LDS; per 32
+// queries: Q, dY (as bf16 hi and lo tiles) and (M_i, 1 / D_i, delta_i) in LDS; per 32
 // queries a TF projection gives a_if / D_i, which enters as bf16 hi + lo.
 // ---------------------------------------------------------------------------
 template <int M>
@@ -445,8 +445,11 @@ __global__ __launch_bounds__(2 * M) void k_bw_rstate(const uint16_t* __restrict_
       *reinterpret_cast<u32x4*>(dh + swz(r, ch)) = hi;
       *reinterpret_cast<u32x4*>(dlo + swz(r, ch)) = lo;
     }
-    for (int r = t; r < 64; r += NT)
-      ax[r] = tok0 + r < j1 ? *reinterpret_cast<const f32x4*>(aux + (rowbase + tok0 + r) * 4) : f32x4{0.f, 1.f, 0.f, 0.f};
+    for (int r = t; r < 64; r += NT) {   // (M_i, 1 / D_i, delta_i)
+      const f32x4 a = tok0 + r < j1 ? *reinterpret_cast<const f32x4*>(aux + (rowbase + tok0 + r) * 4)
+                                    : f32x4{0.f, 1.f, 0.f, 0.f};
+      ax[r] = f32x4{a[0], 1.f / a[1], a[2], 0.f};
+    }
     __syncthreads();
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -460,8 +463,9 @@ __global__ __launch_bounds__(2 * M) void k_bw_rstate(const uint16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 32 * st + drow(i, lane);
-        const f32x4 a = ax[r];   // M_i, D_i, delta_i
-        cf[i] = tok0 + r < j1 ? fast_exp2(fmaf(kLog2e, pr[i], C) - a[0]) / a[1] : 0.f;
+        const f32x4 a = ax[r];   // M_i, 1 / D_i, delta_i
+        const float x = fast_exp2(fmaf(kLog2e, pr[i], C) - a[0]) * a[1];
+        cf[i] = tok0 + r < j1 ? x : 0.f;
         rp = fmaf(cf[i], a[2], rp);
       }
 #pragma unroll
