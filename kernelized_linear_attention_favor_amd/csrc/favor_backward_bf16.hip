@@ -280,9 +280,10 @@ __device__ __forceinline__ void stage_common(uint16_t (&th)[2][M * kD], uint16_t
 
 // ---------------------------------------------------------------------------
 // k_bw_query: dq, and M_i, D_i, delta_i per query (aux [BH][n][4]).  8 waves;
-// each wave takes 32-query tiles of its (b, h) and walks the feature tiles
-// twice: once for the row maximum M_i, once for a (FT: lane = query), D_i,
-// T = S dy (three MFMAs per k-step against S hi / lo), G and the product G W.
+// each wave takes 32-query tiles of its (b, h) and walks the feature tiles once
+// for a (FT: lane = query), D_i, T = S dy (three MFMAs per k-step against S hi /
+// lo), G and the product G W, with the first feature tile's row maximum as the
+// shift M_i (a second walk with the exact maximum when some a_if exceeds 2^64).
 // ---------------------------------------------------------------------------
 template <int M>
 __global__ __launch_bounds__(512) void k_bw_query(const uint16_t* __restrict__ Q, const float* __restrict__ Y,
@@ -323,58 +324,77 @@ __global__ __launch_bounds__(512) void k_bw_query(const uint16_t* __restrict__ Q
       }
     }
     const float delta = pair_sum(dl);
-    // pass 1: the row maximum of g
-    float mx = kNegInf;
-    for (int ft = 0; ft < M / 32; ++ft) {
-      f32x16 pr = {};
+    // the row maximum of g over all features, from the projections
+    auto row_max = [&](int nft) {
+      float mx = kNegInf;
+#pragma unroll 1
+      for (int ft = 0; ft < nft; ++ft) {
+        f32x16 pr = {};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        pr = mfma_bf16(as_bf16x8(rows_operand(wl, 32 * ft, lane, ks)), as_bf16x8(xq[ks]), pr);
+        for (int ks = 0; ks < 4; ++ks)
+          pr = mfma_bf16(as_bf16x8(rows_operand(wl, 32 * ft, lane, ks)), as_bf16x8(xq[ks]), pr);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[32 * ft + 8 * j + 4 * h]);
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[32 * ft + 8 * j + 4 * h]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaf(kLog2e, pr[4 * j + e], cc[e]));
-      }
-    }
-    const float Mi = pair_max(mx);
-    // pass 2
-    f32x16 acc[2] = {};
-    float Dp = 0.f, Gs = 0.f;
-    for (int ft = 0; ft < M / 32; ++ft) {
-      f32x16 pr = {}, tacc = {};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        pr = mfma_bf16(as_bf16x8(rows_operand(wl, 32 * ft, lane, ks)), as_bf16x8(xq[ks]), pr);
-        const u32x4 ah = rows_operand(sl[0], 32 * ft, lane, ks), al = rows_operand(sl[1], 32 * ft, lane, ks);
-        tacc = mfma_bf16(as_bf16x8(ah), as_bf16x8(dyh[ks]), tacc);
-        tacc = mfma_bf16(as_bf16x8(ah), as_bf16x8(dyl[ks]), tacc);
-        tacc = mfma_bf16(as_bf16x8(al), as_bf16x8(dyh[ks]), tacc);
-      }
-      float G[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[32 * ft + 8 * j + 4 * h]);
-        const f32x4 zz = *reinterpret_cast<const f32x4*>(&zl[32 * ft + 8 * j + 4 * h]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = fast_exp2(fmaf(kLog2e, pr[4 * j + e], cc[e]) - Mi);
-          Dp = fmaf(a, zz[e], Dp);
-          G[4 * j + e] = a * fmaf(-zz[e], delta, tacc[4 * j + e]);
-          Gs += G[4 * j + e];
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaf(kLog2e, pr[4 * j + e], cc[e]));
         }
       }
+      return pair_max(mx);
+    };
+    f32x16 acc[2];
+    float Dp, Gs, tmax;
+    auto accumulate = [&](float Ms) {
+      acc[0] = acc[1] = f32x16{};
+      Dp = Gs = 0.f;
+      tmax = kNegInf;
+#pragma unroll 1
+      for (int ft = 0; ft < M / 32; ++ft) {
+        f32x16 pr = {}, tacc = {};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        u32x4 gh, gl;
-        split8(G, kb, gh, gl);
+        for (int ks = 0; ks < 4; ++ks) {
+          pr = mfma_bf16(as_bf16x8(rows_operand(wl, 32 * ft, lane, ks)), as_bf16x8(xq[ks]), pr);
+          const u32x4 ah = rows_operand(sl[0], 32 * ft, lane, ks), al = rows_operand(sl[1], 32 * ft, lane, ks);
+          tacc = mfma_bf16(as_bf16x8(ah), as_bf16x8(dyh[ks]), tacc);
+          tacc = mfma_bf16(as_bf16x8(ah), as_bf16x8(dyl[ks]), tacc);
+          tacc = mfma_bf16(as_bf16x8(al), as_bf16x8(dyh[ks]), tacc);
+        }
+        float G[16];
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const u32x4 wb = cols_operand(wl, 32 * ft, kb, dt, lane);
-          acc[dt] = mfma_bf16(as_bf16x8(gh), as_bf16x8(wb), acc[dt]);
-          acc[dt] = mfma_bf16(as_bf16x8(gl), as_bf16x8(wb), acc[dt]);
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[32 * ft + 8 * j + 4 * h]);
+          const f32x4 zz = *reinterpret_cast<const f32x4*>(&zl[32 * ft + 8 * j + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ge = fmaf(kLog2e, pr[4 * j + e], cc[e]) - Ms;
+            tmax = fmaxf(tmax, ge);
+            const float a = fast_exp2(ge);
+            Dp = fmaf(a, zz[e], Dp);
+            G[4 * j + e] = a * fmaf(-zz[e], delta, tacc[4 * j + e]);
+            Gs += G[4 * j + e];
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          u32x4 gh, gl;
+          split8(G, kb, gh, gl);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const u32x4 wb = cols_operand(wl, 32 * ft, kb, dt, lane);
+            acc[dt] = mfma_bf16(as_bf16x8(gh), as_bf16x8(wb), acc[dt]);
+            acc[dt] = mfma_bf16(as_bf16x8(gl), as_bf16x8(wb), acc[dt]);
+          }
         }
       }
+    };
+    // The shift M_i is the first feature tile's row maximum: any per-row constant
+    // cancels, and the a_if above 1 that it leaves are bounded by 2^64 (checked);
+    // beyond that the exact maximum is taken and the tile redone.
+    float Mi = row_max(1);
+    accumulate(Mi);
+    if (__ballot(tmax > 64.f) != 0) {
+      Mi = row_max(M / 32);
+      accumulate(Mi);
     }
     const float Di = pair_sum(Dp), Gsum = pair_sum(Gs);
     if (lane < 32) {

@@ -107,6 +107,28 @@ def test_backward_C2_shape_and_large_inputs(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_backward_far_features(causal):
+    """Features far above the first 32: W's first 32 rows are zero and the others long, so
+    some query's exponents lie ~90 (log2) above its first feature tile's largest. The
+    non-causal query pass shifts by that tile's maximum and redoes the tile with the exact
+    maximum when a weight would exceed 2^64; the keys' exponents spread ~53 below their
+    largest."""
+    x, dy = make(1, 2, 200, 64, 77)
+    rng = np.random.default_rng(5)
+    W = x["W"].astype(np.float64)
+    W[:, :32] = 0.0
+    W[:, 32:] *= 8.0 / np.sqrt(64)
+    x["W"] = fi.round_bf16(W.astype(np.float32))
+    x["q"] = fi.round_bf16((rng.standard_normal(x["q"].shape) * 1.5).astype(np.float32))
+    x["k"] = fi.round_bf16((rng.standard_normal(x["k"].shape) * 0.5).astype(np.float32))
+    got = gpu_backward(x, fwd(x, causal), dy, causal=causal)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy, causal=causal)
+    for g, w, name in zip(got, want, ("dq", "dk", "dv")):
+        assert np.all(np.isfinite(g)), name
+        assert gerr(g, w) < TOL, (name, gerr(g, w))
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_backward_C5_low_rank(causal):
     """The vision stand-in's low-rank q, k (m = 128, H = 12) at n = 1024."""
     x = fi.make_inputs(fi.config("C5", B=1, n=1024))
