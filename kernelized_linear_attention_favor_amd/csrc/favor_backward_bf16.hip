@@ -423,8 +423,9 @@ __global__ __launch_bounds__(512) void k_bw_query(const uint16_t* __restrict__ Q
 // ---------------------------------------------------------------------------
 // k_bw_rstate: R = sum_i (a_i / D_i) dy_i^T and rho = sum_i (a_i / D_i) delta_i
 // over one query range; M/32 waves, wave w owns features [32w, 32w+32).  Per 64
-// queries: Q, dY (as bf16 hi and lo tiles) and (M_i, 1 / D_i, delta_i) in LDS; per 32
-// queries a TF projection gives a_if / D_i, which enters as bf16 hi + lo.
+// queries (read one tile ahead into registers): Q, dY (as bf16 hi and lo tiles)
+// and (M_i, 1 / D_i, delta_i) in LDS; per 32 queries a TF projection gives
+// a_if / D_i, which enters as bf16 hi + lo.
 // ---------------------------------------------------------------------------
 template <int M>
 __global__ __launch_bounds__(2 * M) void k_bw_rstate(const uint16_t* __restrict__ Q, const float* __restrict__ dY,
@@ -448,29 +449,44 @@ __global__ __launch_bounds__(2 * M) void k_bw_rstate(const uint16_t* __restrict_
   const float C = cfin[static_cast<size_t>(bh) * M + f];
   const size_t rowbase = static_cast<size_t>(bh) * n;
 
+  // a 64-query tile's reads, held in registers while the previous tile computes:
+  // Q (64 rows x 8 chunks), dY (64 rows x 8 groups of 8 floats), (M, D, delta)
+  constexpr int QN = 512 / NT;
+  u32x4 pq[QN];
+  f32x4 pdy[2 * QN], pa = {0.f, 1.f, 0.f, 0.f};
+  auto fetch = [&](int tok0) {
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+      const int c = t + NT * i, r = c >> 3, ch = c & 7;
+      const bool ok = tok0 + r < j1;
+      const size_t row = rowbase + tok0 + r;
+      pq[i] = ok ? *reinterpret_cast<const u32x4*>(Q + row * kD + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+      pdy[2 * i] = ok ? *reinterpret_cast<const f32x4*>(dY + row * kD + 8 * ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+      pdy[2 * i + 1] = ok ? *reinterpret_cast<const f32x4*>(dY + row * kD + 8 * ch + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (t < 64)
+      pa = tok0 + t < j1 ? *reinterpret_cast<const f32x4*>(aux + (rowbase + tok0 + t) * 4) : f32x4{0.f, 1.f, 0.f, 0.f};
+  };
+
   f32x16 acc[2] = {};
   float rp = 0.f;
+  if (j0 < j1) fetch(j0);
   for (int tok0 = j0; tok0 < j1; tok0 += 64) {
-    __syncthreads();
-    for (int c = t; c < 512; c += NT) {   // Q: 64 rows x 8 chunks
-      const int r = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4*>(qt + swz(r, ch)) =
-          tok0 + r < j1 ? *reinterpret_cast<const u32x4*>(Q + (rowbase + tok0 + r) * kD + 8 * ch)
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
-    for (int c = t; c < 512; c += NT) {   // dY: 64 rows x 8 groups of 8 floats -> hi, lo chunks
-      const int r = c >> 3, ch = c & 7;
-      u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-      if (tok0 + r < j1) split_row8(dY + (rowbase + tok0 + r) * kD + 8 * ch, hi, lo);
+    __syncthreads();   // the previous tile's reads of LDS are done
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {   // Q; dY as bf16 hi and lo
+      const int c = t + NT * i, r = c >> 3, ch = c & 7;
+      *reinterpret_cast<u32x4*>(qt + swz(r, ch)) = pq[i];
+      const float x[8] = {pdy[2 * i][0], pdy[2 * i][1], pdy[2 * i][2], pdy[2 * i][3],
+                          pdy[2 * i + 1][0], pdy[2 * i + 1][1], pdy[2 * i + 1][2], pdy[2 * i + 1][3]};
+      u32x4 hi, lo;
+      split8(x, 0, hi, lo);
       *reinterpret_cast<u32x4*>(dh + swz(r, ch)) = hi;
       *reinterpret_cast<u32x4*>(dlo + swz(r, ch)) = lo;
     }
-    for (int r = t; r < 64; r += NT) {   // (M_i, 1 / D_i, delta_i)
-      const f32x4 a = tok0 + r < j1 ? *reinterpret_cast<const f32x4*>(aux + (rowbase + tok0 + r) * 4)
-                                    : f32x4{0.f, 1.f, 0.f, 0.f};
-      ax[r] = f32x4{a[0], 1.f / a[1], a[2], 0.f};
-    }
+    if (t < 64) ax[t] = f32x4{pa[0], 1.f / pa[1], pa[2], 0.f};   // (M_i, 1 / D_i, delta_i)
     __syncthreads();
+    if (tok0 + 64 < j1) fetch(tok0 + 64);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       f32x16 pr = {};
