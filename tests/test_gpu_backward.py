@@ -84,6 +84,18 @@ def test_backward_matches_oracle(n, m, causal):
         assert gerr(g, w) < TOL, (name, gerr(g, w))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,n,m", [(3, 40, 17, 64), (2, 64, 40, 256)])
+def test_backward_many_heads_short(B, H, n, m, causal):
+    # more (b, h) pairs than workgroups per pass, each shorter than one 64-token tile
+    x, dy = make(B, H, n, m, 320 + H)
+    got = gpu_backward(x, fwd(x, causal), dy, causal=causal)
+    want = oracle.attention_backward(x["q"], x["k"], x["v"], x["W"], dy, causal=causal)
+    for g, w, name in zip(got, want, ("dq", "dk", "dv")):
+        assert np.all(np.isfinite(g)), name
+        assert gerr(g, w) < TOL, (name, gerr(g, w))
+
+
 @pytest.mark.parametrize("B,H,n,m", [(4, 8, 1000, 128), (2, 4, 3000, 64), (8, 8, 777, 256)])
 def test_backward_causal_long_ranges(B, H, n, m):
     # many (b, h): few ranges per head, each several chunks long, the last one ragged
