@@ -4,9 +4,10 @@
 // gradients but print no formulas.
 //
 // Exact rewrite used throughout (log2 units): with e_jf = log2e (w_f.k_j -
-// |k_j|^2/2), C_f = max_j e_jf over the head's keys and g_if = log2e w_f.q_i +
-// C_f, M_i = max_f g_if,
-//   b_jf = 2^(e_jf - C_f) in (0, 1],   a_if = 2^(g_if - M_i) in (0, 1],
+// |k_j|^2/2), C_f = max_j e_jf over the head's keys, g_if = log2e w_f.q_i + C_f
+// and a per-query shift M_i (the row maximum max_f g_if; the non-causal query
+// pass takes the first feature tile's, with a_if checked to stay below 2^64),
+//   b_jf = 2^(e_jf - C_f) in (0, 1],   a_if = 2^(g_if - M_i),
 // phi(q_i).phi(k_j) = lambda_i a_i.b_j for a per-query constant lambda_i, which
 // cancels in y and in every gradient below.  With S = sum_j b_j v_j^T, z =
 // sum_j b_j, D_i = a_i.z, delta_i = dy_i.y_i (y the forward output):
@@ -20,8 +21,11 @@
 // Kernels (non-causal): k_bw_keys (S, z partials with a running shift per
 // range), k_bw_merge (C_f; the sum, written as bf16 hi + lo row-major tiles),
 // k_bw_query (dq; M_i, D_i, delta_i per query), k_bw_rstate (R, rho partials),
-// k_bw_merge, k_bw_key (dk, dv).  bf16 MFMA with fp32 accumulation; fp32
-// operands enter as bf16 hi + lo pairs, the bf16 inputs exactly.
+// k_bw_merge, k_bw_key (dk, dv).  Causal: k_bw_keys (segment states), k_bw_cmax
+// (C_f), k_bw_query_causal (a forward chunk walk per segment), k_bw_rstate
+// (segment partials of R, rho), k_bw_key_causal (a backward chunk walk).  bf16
+// MFMA with fp32 accumulation; fp32 operands enter as bf16 hi + lo pairs, the
+// bf16 inputs exactly.
 #include <math.h>
 
 #include "favor_bf16_common.h"
