@@ -22,6 +22,7 @@ import hashlib
 import json
 import multiprocessing as mp
 import os
+import re
 import sys
 import time
 
@@ -51,16 +52,24 @@ def kernel_bytes(name: str, B: int, H: int, n: int, d: int, m: int) -> float:
     return float(table.get(name, 0.0))
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks and empty lines (the
+    device sources hold no "//" inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (ln.split("//", 1)[0].rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def source_digest() -> str:
-    """Digest of the device-code sources (kernels and their headers; the host
-    layer does not change what the counters measure)."""
+    """Digest of the device code (kernels and their headers, comments left out;
+    the host layer does not change what the counters measure)."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if not f.endswith((".hip", ".h")):
             continue
-        with open(os.path.join(CSRC, f), "rb") as fh:
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
             h.update(f.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
