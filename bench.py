@@ -14,6 +14,10 @@ Prints one JSON line:
                  time (HIP events on the launch stream), against 8 TB/s HBM
   cpu_baseline   the fp64 oracle timed on host cores on a sample of the same
                  workload (whole (b, h) slices)
+and, each measured outside the timed step with its own HIP events and the
+oracle timed beside it: decode (streaming decode on the same shape),
+feature_maps (ReLU and elu+1 maps), feature_draw (on-device W), backward and
+backward_causal (dq, dk, dv for an upstream gradient).
 """
 from __future__ import annotations
 
