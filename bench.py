@@ -505,6 +505,26 @@ def main() -> int:
           ", ".join(f"{k} {c}x {t / c * 1e3:.1f}us" for k, (c, t) in bprof.items()),
           file=sys.stderr, flush=True)
 
+    # the self-allocating entries: no workspace argument, so each call allocates,
+    # clears and frees its scratch stream-ordered (timed the same way, for comparison)
+    def step_alloc(i):
+        t = sets[i % len(sets)]
+        favor.attention(t["q"], t["k"], t["v"], W, causal=False, out=outs_nc[i % len(sets)])
+        if causal_ok:
+            favor.attention(t["q"], t["k"], t["v"], W, causal=True, out=outs_c[i % len(sets)])
+
+    for i in range(3):
+        step_alloc(i)
+    torch.cuda.synchronize()
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for i in range(args.steps):
+        step_alloc(i)
+    a1.record()
+    torch.cuda.synchronize()
+    ms_alloc = a0.elapsed_time(a1) / args.steps
+
     tokens = B * n
     value = tokens / (ms * 1e-3)
     dbytes = kernel_bytes(dname, B, H, n, d, m)
@@ -600,6 +620,9 @@ def main() -> int:
         "decode": dec,
         "feature_maps": phi,
         "feature_draw": draw,
+        "self_alloc": {"ms_per_step": round(ms_alloc, 5), "tokens_per_s": round(tokens / (ms_alloc * 1e-3), 1),
+                       "note": "the same step through the entries without a workspace argument (scratch "
+                               "allocated, cleared and freed stream-ordered in every call)"},
         "backward": bwd,
         "backward_causal": bwd_c,
         "sources": digest,
