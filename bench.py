@@ -52,6 +52,11 @@ def kernel_bytes(name: str, B: int, H: int, n: int, d: int, m: int) -> float:
         "k_output": tok * 2 + tok * 4 + W,           # Q in, y out
         "k_causal_state": 2 * tok * 2 + W,           # K, V
         "k_causal_output": 3 * tok * 2 + tok * 4 + W,  # Q, K, V in, y out
+        # backward: bf16 q, k, v and fp32 y, dy, aux (M, D, delta) in; fp32 dq, dk, dv out
+        "k_bw_query": tok * 2 + 2 * tok * 4 + tok * 4 + BH * n * 16 + W,         # q, y, dy -> dq, aux
+        "k_bw_key": 2 * tok * 2 + 2 * tok * 4 + W,                              # k, v -> dk, dv
+        "k_bw_query_causal": 3 * tok * 2 + 2 * tok * 4 + tok * 4 + BH * n * 16 + W,
+        "k_bw_key_causal": 3 * tok * 2 + tok * 4 + BH * n * 16 + 2 * tok * 4 + W,  # q, k, v, dy, aux -> dk, dv
     }
     return float(table.get(name, 0.0))
 
@@ -362,9 +367,18 @@ def bench_backward(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s:
     call_bytes = 3 * 2.0 * B * H * n * d + 2 * 4.0 * B * H * n * d + 3 * 4.0 * B * H * n * d + 2.0 * H * m * d
     assert all(bool(torch.isfinite(o).all()) for o in outs), "non-finite gradients"
     kind = "causal" if causal else "non-causal"
+    # the call's dominant kernel against the HBM roof (algorithmic bytes per launch)
+    dom = max(kernels, key=kernels.get)
+    dbytes = kernel_bytes(dom, B, H, n, d, m)
+    droof = None
+    if dbytes > 0:
+        ach = dbytes / (kernels[dom] * 1e-6) / 1e9
+        droof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": dbytes}
     out = {"workload": f"{kind} backward B={B} H={H} n={n} d={d} m={m}", "kernel_us": round(us, 2),
            "tokens_per_s": round(B * n / (us * 1e-6), 1), "bytes_per_call": call_bytes,
-           "hbm_frac": round(call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "kernels_us": kernels}
+           "hbm_frac": round(call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "kernels_us": kernels,
+           "roofline": droof}
     if cpu_budget_s > 0:
         import numpy as np
         import oracle  # cpu_baseline leg only
