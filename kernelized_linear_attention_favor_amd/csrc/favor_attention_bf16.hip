@@ -446,29 +446,60 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
   const int fb = blockIdx.x - bh * nfb;
   const int t = threadIdx.x;
   const int f = 16 * fb + (t >> 4), cq = t & 15;
-  float vm = 0.f;
-  for (int s = 0; s < splits; ++s) vm = fmaxf(vm, part_vmax[static_cast<size_t>(bh) * splits + s]);
+  const float* zc0 = part_zc + static_cast<size_t>(bh) * splits * 2 * m;
+  const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 4 * cq;
+  float vm = 0.f, cm = -kFInf, zt = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (splits <= 8) {
+    // every split's values read at once, then combined in index order
+    float vs[8], cs[8], zs[8];
+    f32x4 r[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s < splits) {
+        vs[s] = part_vmax[static_cast<size_t>(bh) * splits + s];
+        cs[s] = zc0[static_cast<size_t>(s) * 2 * m + m + f];
+        zs[s] = zc0[static_cast<size_t>(s) * 2 * m + f];
+        r[s] = *reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
+      } else {
+        vs[s] = 0.f;
+        cs[s] = -kFInf;
+        zs[s] = 0.f;
+        r[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      vm = fmaxf(vm, vs[s]);
+      cm = fmaxf(cm, cs[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      // an empty range (or a slot past the splits) has c = -inf and contributes nothing
+      const float a = (cs[s] == -kFInf) ? 0.f : exp2f(cs[s] - cm);
+      zt = fmaf(a, zs[s], zt);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) acc[cc] = fmaf(a, r[s][cc], acc[cc]);
+    }
+  } else {
+    for (int s = 0; s < splits; ++s) {
+      vm = fmaxf(vm, part_vmax[static_cast<size_t>(bh) * splits + s]);
+      cm = fmaxf(cm, zc0[static_cast<size_t>(s) * 2 * m + m + f]);
+    }
+#pragma unroll 8
+    for (int s = 0; s < splits; ++s) {
+      const float cs = zc0[static_cast<size_t>(s) * 2 * m + m + f];
+      const float zs = zc0[static_cast<size_t>(s) * 2 * m + f];
+      const f32x4 r = *reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
+      const float a = (cs == -kFInf) ? 0.f : exp2f(cs - cm);
+      zt = fmaf(a, zs, zt);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) acc[cc] = fmaf(a, r[cc], acc[cc]);
+    }
+  }
   int ex = 0;   // smallest power of two strictly above vm (1 for all-zero values)
   if (vm > 0.f && vm <= 3.0e38f) frexpf(vm, &ex);
   const float sg = ldexpf(1.0f, ex);
-
-  const float* zc0 = part_zc + static_cast<size_t>(bh) * splits * 2 * m;
-  float cm = -kFInf;
-  for (int s = 0; s < splits; ++s) cm = fmaxf(cm, zc0[static_cast<size_t>(s) * 2 * m + m + f]);
-  float zt = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* S0 = part_S + (static_cast<size_t>(bh) * splits * m + f) * kD + 4 * cq;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) {
-    const float cs = zc0[static_cast<size_t>(s) * 2 * m + m + f];
-    const float zs = zc0[static_cast<size_t>(s) * 2 * m + f];
-    const f32x4 r = *reinterpret_cast<const f32x4*>(S0 + static_cast<size_t>(s) * m * kD);
-    // an empty range has c = -inf and contributes nothing
-    const float a = (cs == -kFInf) ? 0.f : exp2f(cs - cm);
-    zt = fmaf(a, zs, zt);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) acc[cc] = fmaf(a, r[cc], acc[cc]);
-  }
   const float inv = 1.0f / zt;
   const int pos = kblock_pos(f & 15);
 #pragma unroll
