@@ -224,19 +224,43 @@ __global__ __launch_bounds__(256) void k_bw_merge(const float* __restrict__ part
   const int q4 = M / 4;
   const int bh = blockIdx.x / q4, r = (blockIdx.x % q4) * 4 + (threadIdx.x >> 6), c = threadIdx.x & 63;
   // with cpart: each range's sums carry the shift m_r, and enter at 2^(m_r - C)
-  float C = 0.f;
-  if (cpart) {
-    C = kNegInf;
-    for (int sp = 0; sp < splits; ++sp) C = fmaxf(C, cpart[(static_cast<size_t>(bh) * splits + sp) * M + r]);
-  }
-  float a = 0.f, s = 0.f;
+  float C = 0.f, a = 0.f, s = 0.f;
   const float* P = part + (static_cast<size_t>(bh) * splits * M + r) * kD + c;
   const float* Z = pvec + static_cast<size_t>(bh) * splits * M + r;
+  const float* CP = cpart ? cpart + static_cast<size_t>(bh) * splits * M + r : nullptr;
+  if (splits <= 16) {
+    // every range's values read at once, then combined in index order (slots past
+    // the ranges add exact zeros)
+    float pv[16], zv[16], mv[16];
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp) {
+      const bool in = sp < splits;
+      pv[sp] = in ? P[static_cast<size_t>(sp) * M * kD] : 0.f;
+      zv[sp] = in ? Z[static_cast<size_t>(sp) * M] : 0.f;
+      mv[sp] = in && CP ? CP[static_cast<size_t>(sp) * M] : kNegInf;
+    }
+    if (CP) {
+      C = kNegInf;
+#pragma unroll
+      for (int sp = 0; sp < 16; ++sp) C = fmaxf(C, mv[sp]);
+    }
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp) {
+      const float w = CP ? fast_exp2(mv[sp] - C) : 1.f;
+      a = fmaf(pv[sp], w, a);
+      s = fmaf(zv[sp], w, s);
+    }
+  } else {
+    if (CP) {
+      C = kNegInf;
+      for (int sp = 0; sp < splits; ++sp) C = fmaxf(C, CP[static_cast<size_t>(sp) * M]);
+    }
 #pragma unroll 8
-  for (int sp = 0; sp < splits; ++sp) {
-    const float w = cpart ? fast_exp2(cpart[(static_cast<size_t>(bh) * splits + sp) * M + r] - C) : 1.f;
-    a = fmaf(P[static_cast<size_t>(sp) * M * kD], w, a);
-    s = fmaf(Z[static_cast<size_t>(sp) * M], w, s);
+    for (int sp = 0; sp < splits; ++sp) {
+      const float w = CP ? fast_exp2(CP[static_cast<size_t>(sp) * M] - C) : 1.f;
+      a = fmaf(P[static_cast<size_t>(sp) * M * kD], w, a);
+      s = fmaf(Z[static_cast<size_t>(sp) * M], w, s);
+    }
   }
   const uint32_t pk = pack_bf16(a, 0.f);
   const uint16_t hi = static_cast<uint16_t>(pk & 0xffffu);
