@@ -420,8 +420,8 @@ def main() -> int:
                          "times; its HBM counters calibrate the per-kernel traffic figures")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards over (b, h) or over the sequence without running here)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard over (b, h) or over the sequence)", file=sys.stderr)
         return 2
 
     import numpy as np

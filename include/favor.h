@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   FAVOR_OK = 0,
   FAVOR_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad flag */
-  FAVOR_ERR_UNSUPPORTED = 2,      /* valid but outside what this build implements */
+  FAVOR_ERR_UNSUPPORTED = 2,      /* valid but outside what the library implements */
   FAVOR_ERR_HIP = 3,              /* a HIP call or kernel launch failed */
   FAVOR_ERR_OUT_OF_MEMORY = 4     /* scratch allocation failed, or workspace too small */
 } favor_status_t;
