@@ -1053,33 +1053,38 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
 }
 
 // ---------------------------------------------------------------------------
-// k_bw_key_causal: dk and dv, walking the range's chunks from the last.
-// R (lane = value column) and rho hold the sums over queries after the chunk
-// (the ranges after this one, then the later chunks); R.v reads R a feature per
-// lane after a pass through LDS.
-// Per chunk, wave w, coef_if = 2^(g_if - M_i) / D_i:
+// k_bw_key_causal: dk and dv, walking the range's chunks from the last.  Wave w
+// owns TPW feature tiles of 32 (features [32 TPW w, 32 TPW (w+1))); per tile, R
+// (lane = value column) and rho hold the sums over queries after the chunk (the
+// ranges after this one, then the later chunks); R.v reads R a feature per lane
+// after a pass through LDS.  Per chunk, coef_if = 2^(g_if - M_i) / D_i:
 //   dv_j = b_j.R + sum_{i >= j in chunk} (coef_i.b_j) dy_i
 //   db_jf = R_f.v_j - rho_f + sum_{i >= j in chunk} coef_if (dy_i.v_j - delta_i)
 //   H = b db,  dk_j = W^T H_j - k_j sum_f H_jf
-// then R and rho take the chunk's queries.  Staging as for the query side.
+// then R and rho take the chunk's queries.  A wave's share of dv and dk sums
+// over its tiles, so the terms that do not depend on the feature (dY V^T and the
+// product of the masked chunk matrix with dY) are formed once per wave; the dv
+// and dk shares meet in two LDS areas after one barrier.  Staging as for the
+// query side.
 // ---------------------------------------------------------------------------
-template <int M>
-__global__ __launch_bounds__(2 * M) void k_bw_key_causal(
+template <int M, int TPW>
+__global__ __launch_bounds__(M * 2 / TPW) void k_bw_key_causal(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ W, const float* __restrict__ dY, const float* __restrict__ cfin,
     const float* __restrict__ aux, const float* __restrict__ part_R, const float* __restrict__ part_rho,
     float* __restrict__ dK, float* __restrict__ dV, int H, int n, int segs, int span) {
-  constexpr int NW = M / 32, NT = 2 * M;
+  constexpr int NW = M / (32 * TPW), NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t wl[M * kD];
   __shared__ __attribute__((aligned(16))) ChunkBuf buf[2];
-  __shared__ __attribute__((aligned(16))) float ul[NW][32][kD];
+  __shared__ __attribute__((aligned(16))) float ulv[NW][32][kD];
+  __shared__ __attribute__((aligned(16))) float ulk[NW][32][kD];
   __shared__ float sl_h[NW][32];
-  __shared__ __attribute__((aligned(16))) float rl[NW][32];
+  __shared__ __attribute__((aligned(16))) float rl[NW][TPW * 32];
   __shared__ __attribute__((aligned(16))) float cl[M];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5, ql = lane & 31;
   const int bh = blockIdx.x / segs, sg = blockIdx.x % segs, hh = bh % H;
   const int t0 = sg * span, t1 = min(n, t0 + span);
-  const int fb = 32 * wave, f = fb + ql;
+  const int fw = 32 * TPW * wave;   // the wave's first feature; tile p starts at fw + 32 p
   const size_t rowbase = static_cast<size_t>(bh) * n;
   const int nch = (t1 - t0 + 31) / 32;
   ChunkRegs<NT, false> pre;
@@ -1088,24 +1093,27 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
   for (int c = t; c < M * 8; c += NT)
     *reinterpret_cast<u32x4*>(wl + tile_at(c >> 3, c & 7)) = *reinterpret_cast<const u32x4*>(Wh + 8 * c);
   for (int i = t; i < M; i += NT) cl[i] = cfin[static_cast<size_t>(bh) * M + i];
-  const float C = cfin[static_cast<size_t>(bh) * M + f];
-  // R (D[f][c]: lane = column) and rho: ranges after this one
-  f32x16 R[2];
-  {
+  float C[TPW];
+  // R (D[f][c]: lane = column) and rho per tile: ranges after this one
+  f32x16 R[TPW][2];
+#pragma unroll
+  for (int p = 0; p < TPW; ++p) {
+    const int fb = fw + 32 * p, f = fb + ql;
+    C[p] = cfin[static_cast<size_t>(bh) * M + f];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) R[x][i] = 0.f;
+      for (int i = 0; i < 16; ++i) R[p][x][i] = 0.f;
     float rho = 0.f;
     for (int s = segs - 1; s > sg; --s) {
       const float* PR = part_R + (static_cast<size_t>(bh) * segs + s) * M * kD;
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) R[x][i] += PR[static_cast<size_t>(fb + drow(i, lane)) * kD + 32 * x + ql];
+        for (int i = 0; i < 16; ++i) R[p][x][i] += PR[static_cast<size_t>(fb + drow(i, lane)) * kD + 32 * x + ql];
       rho += part_rho[(static_cast<size_t>(bh) * segs + s) * M + f];
     }
-    if (lane < 32) rl[wave][lane] = rho;
+    if (lane < 32) rl[wave][32 * p + lane] = rho;
   }
   chunk_store<NT, false>(pre, buf[0], t);
   if (nch > 1) chunk_load<NT, false>(pre, Q, K, V, dY, nullptr, aux, rowbase, t0 + 32 * (nch - 2), t1, t);
@@ -1119,112 +1127,127 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
     const bool ok = c0 + ql < t1;
     // the phases below are kept apart (sched_barrier) so that each one's operands
     // are read from LDS when used and die after it
-    // 0. R.v_j (FT: lane = key): R passes through the wave's own share rows (free
-    // until the dv share below) to be read back a feature per lane, the A operand
+    // 0. R.v_j (FT: lane = key) per tile: R passes through the wave's dv share rows
+    // (free until the dv share below) to be read back a feature per lane
+    f32x16 rvd[TPW];
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int p = 0; p < TPW; ++p) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = R[dt][i];
-    __builtin_amdgcn_wave_barrier();
-    f32x16 rvd = {};
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f32x4 ra = *reinterpret_cast<const f32x4*>(&ul[wave][ql][16 * ks + 8 * h]);
-      const f32x4 rb = *reinterpret_cast<const f32x4*>(&ul[wave][ql][16 * ks + 8 * h + 4]);
-      const float x[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
-      u32x4 rh, rlo;
-      split8(x, 0, rh, rlo);
-      const u32x4 xv = tile_row8(B.v, ql, ks, h);
-      rvd = mfma_bf16(as_bf16x8(rh), as_bf16x8(xv), rvd);
-      rvd = mfma_bf16(as_bf16x8(rlo), as_bf16x8(xv), rvd);
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // 1. coef (FT: lane = query, and TF: lane = feature) and b (FT: lane = key);
-    // rho's new part
-    float bk[16], cff[16];
-    u32x4 cth[2], ctl[2];
-    float rs = 0.f;
-    {
-      f32x16 pqf = {}, pqt = {}, pkf = {};
+        for (int i = 0; i < 16; ++i) ulv[wave][drow(i, lane)][32 * dt + ql] = R[p][dt][i];
+      __builtin_amdgcn_wave_barrier();
+      rvd[p] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 xq = tile_row8(B.q, ql, ks, h);
-        const u32x4 wa = rows_operand(wl, fb, lane, ks);
-        pqf = mfma_bf16(as_bf16x8(wa), as_bf16x8(xq), pqf);
-        pqt = mfma_bf16(as_bf16x8(xq), as_bf16x8(wa), pqt);
-        pkf = mfma_bf16(as_bf16x8(wa), as_bf16x8(tile_row8(B.k, ql, ks, h)), pkf);
+        const f32x4 ra = *reinterpret_cast<const f32x4*>(&ulv[wave][ql][16 * ks + 8 * h]);
+        const f32x4 rb = *reinterpret_cast<const f32x4*>(&ulv[wave][ql][16 * ks + 8 * h + 4]);
+        const float x[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+        u32x4 rh, rlo;
+        split8(x, 0, rh, rlo);
+        const u32x4 xv = tile_row8(B.v, ql, ks, h);
+        rvd[p] = mfma_bf16(as_bf16x8(rh), as_bf16x8(xv), rvd[p]);
+        rvd[p] = mfma_bf16(as_bf16x8(rlo), as_bf16x8(xv), rvd[p]);
       }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 1. per tile: coef (FT: lane = query, and TF: lane = feature) and b (FT: lane =
+    // key) as bf16 hi / lo; P'^T[i][j] = coef_i . b_j summed over the wave's tiles;
+    // rho's new part
+    u32x4 bh_[TPW][2], bl_[TPW][2], cth[TPW][2], ctl[TPW][2];
+    float rs[TPW];
+    f32x16 pp = {};
+    {
       const float aqm = B.am[ql], aqr = B.ar[ql];   // the lane's query
       const float kk = B.kk[ql];                     // the lane's key
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[fb + 8 * j + 4 * h]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * j + e;
-          cff[i] = ok ? fast_exp2(fmaf(kLog2e, pqf[i], cc[e]) - aqm) * aqr : 0.f;
-          bk[i] = ok ? fast_exp2(kLog2e * fmaf(-0.5f, kk, pkf[i]) - cc[e]) : 0.f;
-        }
-      }
-      float cft[16], rm[16], rr[16], rd[16];
+      float rm[16], rr[16], rd[16];
       rows16(B.am, h, rm);
       rows16(B.ar, h, rr);
       rows16(B.ad, h, rd);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = drow(i, lane);
-        const float x = fast_exp2(fmaf(kLog2e, pqt[i], C) - rm[i]) * rr[i];
-        cft[i] = c0 + r < t1 ? x : 0.f;   // register = query
-        rs = fmaf(cft[i], rd[i], rs);
-      }
+      for (int p = 0; p < TPW; ++p) {
+        const int fb = fw + 32 * p;
+        f32x16 pqf = {}, pqt = {}, pkf = {};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) split8(cft, kb, cth[kb], ctl[kb]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 xq = tile_row8(B.q, ql, ks, h);
+          const u32x4 wa = rows_operand(wl, fb, lane, ks);
+          pqf = mfma_bf16(as_bf16x8(wa), as_bf16x8(xq), pqf);
+          pqt = mfma_bf16(as_bf16x8(xq), as_bf16x8(wa), pqt);
+          pkf = mfma_bf16(as_bf16x8(wa), as_bf16x8(tile_row8(B.k, ql, ks, h)), pkf);
+        }
+        float cff[16], bk[16], cft[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[fb + 8 * j + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * j + e;
+            cff[i] = ok ? fast_exp2(fmaf(kLog2e, pqf[i], cc[e]) - aqm) * aqr : 0.f;
+            bk[i] = ok ? fast_exp2(kLog2e * fmaf(-0.5f, kk, pkf[i]) - cc[e]) : 0.f;
+          }
+        }
+        rs[p] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = drow(i, lane);
+          const float x = fast_exp2(fmaf(kLog2e, pqt[i], C[p]) - rm[i]) * rr[i];
+          cft[i] = c0 + r < t1 ? x : 0.f;   // register = query
+          rs[p] = fmaf(cft[i], rd[i], rs[p]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          split8(cft, kb, cth[p][kb], ctl[p][kb]);
+          split8(bk, kb, bh_[p][kb], bl_[p][kb]);
+          u32x4 cfh, cfl;
+          split8(cff, kb, cfh, cfl);
+          pp = mfma_bf16(as_bf16x8(cfh), as_bf16x8(bh_[p][kb]), pp);
+          pp = mfma_bf16(as_bf16x8(cfh), as_bf16x8(bl_[p][kb]), pp);
+          pp = mfma_bf16(as_bf16x8(cfl), as_bf16x8(bh_[p][kb]), pp);
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 2. dv: carry b R + chunk P' dY (P'^T[i][j] = coef_i . b_j kept for i >= j),
-    // written as the wave's share; b stays on as its bf16 hi + lo
-    u32x4 bh_[2], bl_[2];
+    // 2. dv: carry sum_p b R + chunk P' dY (kept for i >= j), written as the wave's
+    // share; b stays on as its bf16 hi + lo
     {
-      f32x16 pp = {};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        split8(bk, kb, bh_[kb], bl_[kb]);
-        u32x4 cfh, cfl;
-        split8(cff, kb, cfh, cfl);
-        pp = mfma_bf16(as_bf16x8(cfh), as_bf16x8(bh_[kb]), pp);
-        pp = mfma_bf16(as_bf16x8(cfh), as_bf16x8(bl_[kb]), pp);
-        pp = mfma_bf16(as_bf16x8(cfl), as_bf16x8(bh_[kb]), pp);
-      }
       float pm[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pm[i] = drow(i, lane) >= ql ? pp[i] : 0.f;
-      f32x16 adv[2] = {};
+      u32x4 ph[2], pl[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        u32x4 ph, pl;
-        split8(pm, kb, ph, pl);
+      for (int kb = 0; kb < 2; ++kb) split8(pm, kb, ph[kb], pl[kb]);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          u32x4 rh, rlo;
-          split8(R[dt], kb, rh, rlo);
-          adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rh), adv[dt]);
-          adv[dt] = mfma_bf16(as_bf16x8(bh_[kb]), as_bf16x8(rlo), adv[dt]);
-          adv[dt] = mfma_bf16(as_bf16x8(bl_[kb]), as_bf16x8(rh), adv[dt]);
+      for (int dt = 0; dt < 2; ++dt) {
+        f32x16 adv = {};
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            u32x4 rh, rlo;
+            split8(R[p][dt], kb, rh, rlo);
+            adv = mfma_bf16(as_bf16x8(bh_[p][kb]), as_bf16x8(rh), adv);
+            adv = mfma_bf16(as_bf16x8(bh_[p][kb]), as_bf16x8(rlo), adv);
+            adv = mfma_bf16(as_bf16x8(bl_[p][kb]), as_bf16x8(rh), adv);
+          }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
           const u32x4 yh = v_operand(B.dh, 16 * kb, dt, lane), ym = v_operand(B.dm, 16 * kb, dt, lane);
-          adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(yh), adv[dt]);
-          adv[dt] = mfma_bf16(as_bf16x8(ph), as_bf16x8(ym), adv[dt]);
-          adv[dt] = mfma_bf16(as_bf16x8(pl), as_bf16x8(yh), adv[dt]);
+          adv = mfma_bf16(as_bf16x8(ph[kb]), as_bf16x8(yh), adv);
+          adv = mfma_bf16(as_bf16x8(ph[kb]), as_bf16x8(ym), adv);
+          adv = mfma_bf16(as_bf16x8(pl[kb]), as_bf16x8(yh), adv);
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ulv[wave][drow(i, lane)][32 * dt + ql] = adv[i];
       }
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = adv[dt][i];
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 3. db (FT: lane = key): R.v - rho + coef^T N with N = dY V^T - delta masked to
-    // i >= j (dy to all its 24 bits); H = b db; the wave's dk share H W
+    // 3. db (FT: lane = key) per tile: R.v - rho + coef^T N with N = dY V^T - delta
+    // masked to i >= j (formed once; dy to all its 24 bits); H = b db; the wave's
+    // dk share sum_p H W
+    f32x16 adk[2] = {};
+    float Hs = 0.f;
     {
       f32x16 ndv = {};
 #pragma unroll
@@ -1241,94 +1264,94 @@ __global__ __launch_bounds__(2 * M) void k_bw_key_causal(
         const float x = ndv[i] - rd[i];
         nm[i] = drow(i, lane) >= ql ? x : 0.f;
       }
+      u32x4 nh[2], nl[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        u32x4 nh, nl;
-        split8(nm, kb, nh, nl);
-        rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nh), rvd);
-        rvd = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(nl), rvd);
-        rvd = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(nh), rvd);
-      }
-    }
-    float Hh[16], Hs = 0.f;
+      for (int kb = 0; kb < 2; ++kb) split8(nm, kb, nh[kb], nl[kb]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 rr = *reinterpret_cast<const f32x4*>(&rl[wave][8 * j + 4 * h]);
+      for (int p = 0; p < TPW; ++p) {
+        const int fb = fw + 32 * p;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * j + e;
-        const uint32_t wh = bh_[i >> 3][(i & 7) >> 1], wl_ = bl_[i >> 3][(i & 7) >> 1];
-        const float bv = (i & 1) ? bf16_hi_as_f32(wh) + bf16_hi_as_f32(wl_) : bf16_lo_as_f32(wh) + bf16_lo_as_f32(wl_);
-        Hh[i] = bv * (rvd[i] - rr[e]);
-        Hs += Hh[i];
-      }
-    }
-    f32x16 adk[2] = {};
+        for (int kb = 0; kb < 2; ++kb) {
+          rvd[p] = mfma_bf16(as_bf16x8(cth[p][kb]), as_bf16x8(nh[kb]), rvd[p]);
+          rvd[p] = mfma_bf16(as_bf16x8(cth[p][kb]), as_bf16x8(nl[kb]), rvd[p]);
+          rvd[p] = mfma_bf16(as_bf16x8(ctl[p][kb]), as_bf16x8(nh[kb]), rvd[p]);
+        }
+        float Hh[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 hh_, hl_;
-      split8(Hh, kb, hh_, hl_);
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 rr = *reinterpret_cast<const f32x4*>(&rl[wave][32 * p + 8 * j + 4 * h]);
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const u32x4 wb = cols_operand(wl, fb, kb, dt, lane);
-        adk[dt] = mfma_bf16(as_bf16x8(hh_), as_bf16x8(wb), adk[dt]);
-        adk[dt] = mfma_bf16(as_bf16x8(hl_), as_bf16x8(wb), adk[dt]);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * j + e;
+            const uint32_t wh = bh_[p][i >> 3][(i & 7) >> 1], wlo = bl_[p][i >> 3][(i & 7) >> 1];
+            const float bv = (i & 1) ? bf16_hi_as_f32(wh) + bf16_hi_as_f32(wlo) : bf16_lo_as_f32(wh) + bf16_lo_as_f32(wlo);
+            Hh[i] = bv * (rvd[p][i] - rr[e]);
+            Hs += Hh[i];
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          u32x4 hh_, hl_;
+          split8(Hh, kb, hh_, hl_);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const u32x4 wb = cols_operand(wl, fb, kb, dt, lane);
+            adk[dt] = mfma_bf16(as_bf16x8(hh_), as_bf16x8(wb), adk[dt]);
+            adk[dt] = mfma_bf16(as_bf16x8(hl_), as_bf16x8(wb), adk[dt]);
+          }
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    const float Hw = pair_sum(Hs);
-    if (lane < 32) sl_h[wave][lane] = Hw;
-    // the reads of the chunk after next, in flight through the combines below
-    if (ci > 1) chunk_load<NT, false>(pre, Q, K, V, dY, nullptr, aux, rowbase, c0 - 64, t1, t);
-    // 4. the chunk's queries join R and rho (after their use above)
-    rs = pair_sum(rs);
-    if (lane < 32) rl[wave][lane] += rs;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const u32x4 yh = v_operand(B.dh, 16 * kb, dt, lane), ym = v_operand(B.dm, 16 * kb, dt, lane);
-        R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(yh), R[dt]);
-        R[dt] = mfma_bf16(as_bf16x8(cth[kb]), as_bf16x8(ym), R[dt]);
-        R[dt] = mfma_bf16(as_bf16x8(ctl[kb]), as_bf16x8(yh), R[dt]);
-      }
-    __syncthreads();   // dv shares visible
-    constexpr int CPQ = 32 * kD / NT;
-    const int q = t / (kD / CPQ), cb = (t % (kD / CPQ)) * CPQ, r = c0 + q;
-    if (r < t1) {
-#pragma unroll
-      for (int e4 = 0; e4 < CPQ; e4 += 4) {
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < NW; ++w) U += *reinterpret_cast<const f32x4*>(&ul[w][q][cb + e4]);
-        *reinterpret_cast<f32x4*>(dV + (rowbase + r) * kD + cb + e4) = U;
-      }
-    }
-    __syncthreads();   // dv shares read
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ul[wave][drow(i, lane)][32 * dt + ql] = adk[dt][i];
-    __syncthreads();   // dk shares visible
+      for (int i = 0; i < 16; ++i) ulk[wave][drow(i, lane)][32 * dt + ql] = adk[dt][i];
+    const float Hw = pair_sum(Hs);
+    if (lane < 32) sl_h[wave][lane] = Hw;
+    // the reads of the chunk after next, in flight through the combine below
+    if (ci > 1) chunk_load<NT, false>(pre, Q, K, V, dY, nullptr, aux, rowbase, c0 - 64, t1, t);
+    // 4. the chunk's queries join R and rho (after their use above)
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      const float rsum = pair_sum(rs[p]);
+      if (lane < 32) rl[wave][32 * p + lane] += rsum;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const u32x4 yh = v_operand(B.dh, 16 * kb, dt, lane), ym = v_operand(B.dm, 16 * kb, dt, lane);
+          R[p][dt] = mfma_bf16(as_bf16x8(cth[p][kb]), as_bf16x8(yh), R[p][dt]);
+          R[p][dt] = mfma_bf16(as_bf16x8(cth[p][kb]), as_bf16x8(ym), R[p][dt]);
+          R[p][dt] = mfma_bf16(as_bf16x8(ctl[p][kb]), as_bf16x8(yh), R[p][dt]);
+        }
+    }
+    __syncthreads();   // dv and dk shares visible
+    constexpr int CPQ = 32 * kD / NT;
+    const int q = t / (kD / CPQ), cb = (t % (kD / CPQ)) * CPQ, r = c0 + q;
     if (r < t1) {
       float hs = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) hs += sl_h[w][q];
 #pragma unroll
       for (int e4 = 0; e4 < CPQ; e4 += 4) {
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
+        f32x4 U = {0.f, 0.f, 0.f, 0.f}, Uk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < NW; ++w) U += *reinterpret_cast<const f32x4*>(&ul[w][q][cb + e4]);
+        for (int w = 0; w < NW; ++w) {
+          U += *reinterpret_cast<const f32x4*>(&ulv[w][q][cb + e4]);
+          Uk += *reinterpret_cast<const f32x4*>(&ulk[w][q][cb + e4]);
+        }
+        *reinterpret_cast<f32x4*>(dV + (rowbase + r) * kD + cb + e4) = U;
         const u32x2 kw = *reinterpret_cast<const u32x2*>(B.k + swz(q, (cb + e4) >> 3) + ((cb + e4) & 7));
         const float kv[4] = {bf16_lo_as_f32(kw[0]), bf16_hi_as_f32(kw[0]), bf16_lo_as_f32(kw[1]),
                              bf16_hi_as_f32(kw[1])};
         f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = U[e] - kv[e] * hs;
+        for (int e = 0; e < 4; ++e) o[e] = Uk[e] - kv[e] * hs;
         *reinterpret_cast<f32x4*>(dK + (rowbase + r) * kD + cb + e4) = o;
       }
     }
-    __syncthreads();   // dk shares and this chunk's buffer free
+    __syncthreads();   // shares and this chunk's buffer free
   }
 }
 
@@ -1355,8 +1378,11 @@ hipError_t launch_causal_m(const BwPlan& p, const uint16_t* q, const uint16_t* k
                p.splits, p.span);
   auto kr = k_bw_rstate<M>;
   FAVOR_LAUNCH("k_bw_rstate", kr, gs, bs, 0, s, q, dy, W, cfin, aux, pR, prho, p.H, p.n, p.splits, p.span);
-  auto kc = k_bw_key_causal<M>;
-  FAVOR_LAUNCH("k_bw_key_causal", kc, gs, bs, 0, s, q, k, v, W, dy, cfin, aux, pR, prho, dk, dv, p.H, p.n,
+  // m = 256: 4 waves of two feature tiles (the dv and dk share areas fit in LDS
+  // beside the staged chunks); else a tile per wave
+  constexpr int TPW = M == 256 ? 2 : 1;
+  auto kc = k_bw_key_causal<M, TPW>;
+  FAVOR_LAUNCH("k_bw_key_causal", kc, gs, dim3(2 * M / TPW), 0, s, q, k, v, W, dy, cfin, aux, pR, prho, dk, dv, p.H, p.n,
                p.splits, p.span);
   return hipGetLastError();
 }
