@@ -818,33 +818,36 @@ __device__ __forceinline__ u32x4 tile_perm8(const uint16_t* tile, int row, int k
 }
 
 // ---------------------------------------------------------------------------
-// k_bw_query_causal: dq and (M_i, D_i, delta_i) per query.  Per chunk, wave w:
-//   a_if = 2^(g_if - M_wi) (FT, M_wi the wave's row maximum);
+// k_bw_query_causal: dq and (M_i, D_i, delta_i) per query.  Wave w owns TPW
+// feature tiles of 32 (features [32 TPW w, 32 TPW (w+1))).  Per chunk, wave w:
+//   a_if = 2^(g_if - M_wi) (FT, M_wi the wave's row maximum over its features);
 //   T_if - z_if delta_i = (S_f.dy_i - z_f delta_i over keys before the chunk,
 //   S^T in registers) + sum over keys j <= i of the chunk b_jf (v_j.dy_i - delta_i);
 //   D_w = sum_f a z,  Ghat = a (T - z delta),  u_w = sum_f Ghat,  U_w = Ghat W;
 // then S^T, z take the chunk's keys.  Combine: scale_w = 2^(M_wi - M_i),
 // dq_i = (sum_w scale_w U_w - q_i sum_w scale_w u_w) / sum_w scale_w D_w.
-// Chunks are staged in LDS (two buffers) with the next chunk's reads in flight.
+// The masked chunk matrix V dY^T - delta does not depend on the feature and is
+// formed once per wave.  Chunks are staged in LDS (two buffers) with the next
+// chunk's reads in flight.
 // ---------------------------------------------------------------------------
-template <int M>
-__global__ __launch_bounds__(2 * M) void k_bw_query_causal(
+template <int M, int TPW>
+__global__ __launch_bounds__(M * 2 / TPW) void k_bw_query_causal(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ W, const float* __restrict__ Y, const float* __restrict__ dY,
     const float* __restrict__ cfin, const float* __restrict__ cpart, const float* __restrict__ part_S,
     const float* __restrict__ part_z, float* __restrict__ dQ, float* __restrict__ aux, int H, int n, int segs,
     int span) {
-  constexpr int NW = M / 32, NT = 2 * M;
+  constexpr int NW = M / (32 * TPW), NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t wl[M * kD];
   __shared__ __attribute__((aligned(16))) ChunkBuf buf[2];
   __shared__ __attribute__((aligned(16))) float ul[NW][32][kD];
   __shared__ float sl_u[NW][32], sl_d[NW][32], sl_m[NW][32];
-  __shared__ __attribute__((aligned(16))) float zl[NW][32];
+  __shared__ __attribute__((aligned(16))) float zl[NW][TPW * 32];
   __shared__ __attribute__((aligned(16))) float cl[M];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, h = lane >> 5, ql = lane & 31;
   const int bh = blockIdx.x / segs, sg = blockIdx.x % segs, hh = bh % H;
   const int t0 = sg * span, t1 = min(n, t0 + span);
-  const int fb = 32 * wave, f = fb + ql;
+  const int fw = 32 * TPW * wave;   // the wave's first feature; tile p starts at fw + 32 p
   const size_t rowbase = static_cast<size_t>(bh) * n;
   ChunkRegs<NT, true> pre;
   chunk_load<NT, true>(pre, Q, K, V, dY, Y, nullptr, rowbase, t0, t1, t);
@@ -852,26 +855,29 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
   for (int c = t; c < M * 8; c += NT)
     *reinterpret_cast<u32x4*>(wl + tile_at(c >> 3, c & 7)) = *reinterpret_cast<const u32x4*>(Wh + 8 * c);
   for (int i = t; i < M; i += NT) cl[i] = cfin[static_cast<size_t>(bh) * M + i];
-  const float C = cfin[static_cast<size_t>(bh) * M + f];
-  // S^T (rows = value columns, lane = feature) and z of the keys before the range
-  f32x16 St[2];
-  {
+  float C[TPW];
+  // S^T (rows = value columns, lane = feature) and z per tile, of the keys before the range
+  f32x16 St[TPW][2];
+#pragma unroll
+  for (int p = 0; p < TPW; ++p) {
+    const int f = fw + 32 * p + ql;
+    C[p] = cfin[static_cast<size_t>(bh) * M + f];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) St[ct][i] = 0.f;
+      for (int i = 0; i < 16; ++i) St[p][ct][i] = 0.f;
     float z = 0.f;
     for (int s = 0; s < sg; ++s) {   // each range's sums at its own shift m_s: times 2^(m_s - C)
       const size_t slot = static_cast<size_t>(bh) * segs + s;
-      const float w = fast_exp2(cpart[slot * M + f] - C);
+      const float w = fast_exp2(cpart[slot * M + f] - C[p]);
       const float* PS = part_S + slot * M * kD + static_cast<size_t>(f) * kD;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) St[ct][i] = fmaf(PS[32 * ct + drow(i, lane)], w, St[ct][i]);
+        for (int i = 0; i < 16; ++i) St[p][ct][i] = fmaf(PS[32 * ct + drow(i, lane)], w, St[p][ct][i]);
       z = fmaf(part_z[slot * M + f], w, z);
     }
-    if (lane < 32) zl[wave][lane] = z;
+    if (lane < 32) zl[wave][32 * p + lane] = z;
   }
   chunk_store<NT, true>(pre, buf[0], t);
   if (t0 + 32 < t1) chunk_load<NT, true>(pre, Q, K, V, dY, Y, nullptr, rowbase, t0 + 32, t1, t);
@@ -886,32 +892,38 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
     }
     // the phases below are kept apart (sched_barrier) so that each one's operands
     // are read from LDS when used and die after it
-    // 1. key features b (TF: lane = feature, register = key), as bf16 hi / lo
-    u32x4 bth[2], btl[2];
-    float zs = 0.f;
+    // 1. per tile: key features b (TF: lane = feature, register = key), as bf16 hi / lo
+    u32x4 bth[TPW][2], btl[TPW][2];
+    float zs[TPW];
     {
-      f32x16 pkt = {};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        pkt = mfma_bf16(as_bf16x8(tile_row8(B.k, ql, ks, h)), as_bf16x8(rows_operand(wl, fb, lane, ks)), pkt);
-      float b[16], kr[16];
+      float kr[16];
       rows16(B.kk, h, kr);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = drow(i, lane);
-        const float x = fast_exp2(kLog2e * fmaf(-0.5f, kr[i], pkt[i]) - C);
-        b[i] = c0 + r < t1 ? x : 0.f;
-        zs += b[i];
-      }
+      for (int p = 0; p < TPW; ++p) {
+        f32x16 pkt = {};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) split8(b, kb, bth[kb], btl[kb]);
+        for (int ks = 0; ks < 4; ++ks)
+          pkt = mfma_bf16(as_bf16x8(tile_row8(B.k, ql, ks, h)), as_bf16x8(rows_operand(wl, fw + 32 * p, lane, ks)),
+                          pkt);
+        float b[16];
+        zs[p] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = drow(i, lane);
+          const float x = fast_exp2(kLog2e * fmaf(-0.5f, kr[i], pkt[i]) - C[p]);
+          b[i] = c0 + r < t1 ? x : 0.f;
+          zs[p] += b[i];
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) split8(b, kb, bth[p][kb], btl[p][kb]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // 2. the chunk's part of T - z delta and of z (FT: lane = query): b^T N with
     // N = V dY^T - delta masked to keys j <= i (v_j.dy_i - delta_i = dy_i.(v_j - y_i),
-    // formed before the product with b; dy to all its 24 bits)
+    // formed once, before the product with b; dy to all its 24 bits)
     const float delta = B.ad[ql];
-    f32x16 tacc = {}, zacc = {};
+    f32x16 tacc[TPW], zacc[TPW];
     {
       f32x16 mvd = {};
 #pragma unroll
@@ -924,69 +936,88 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
       float mm[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) mm[i] = drow(i, lane) <= ql ? mvd[i] - delta : 0.f;
+      u32x4 mh[2], ml[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        u32x4 mh, ml;
-        split8(mm, kb, mh, ml);
-        tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(mh), tacc);
-        tacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ml), tacc);
-        tacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(mh), tacc);
-        const u32x4 ones = tril_ones(kb, ql, lane);
-        zacc = mfma_bf16(as_bf16x8(bth[kb]), as_bf16x8(ones), zacc);
-        zacc = mfma_bf16(as_bf16x8(btl[kb]), as_bf16x8(ones), zacc);
+      for (int kb = 0; kb < 2; ++kb) split8(mm, kb, mh[kb], ml[kb]);
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        tacc[p] = f32x16{};
+        zacc[p] = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          tacc[p] = mfma_bf16(as_bf16x8(bth[p][kb]), as_bf16x8(mh[kb]), tacc[p]);
+          tacc[p] = mfma_bf16(as_bf16x8(bth[p][kb]), as_bf16x8(ml[kb]), tacc[p]);
+          tacc[p] = mfma_bf16(as_bf16x8(btl[p][kb]), as_bf16x8(mh[kb]), tacc[p]);
+          const u32x4 ones = tril_ones(kb, ql, lane);
+          zacc[p] = mfma_bf16(as_bf16x8(bth[p][kb]), as_bf16x8(ones), zacc[p]);
+          zacc[p] = mfma_bf16(as_bf16x8(btl[p][kb]), as_bf16x8(ones), zacc[p]);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     // 3. the carry: S^T x dy (dy hi / mid in register order)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      u32x4 sh, slo;
-      split8(St[kb >> 1], kb & 1, sh, slo);
       const u32x4 dph = tile_perm8(B.dh, ql, kb, h), dpl = tile_perm8(B.dm, ql, kb, h);
-      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dph), tacc);
-      tacc = mfma_bf16(as_bf16x8(sh), as_bf16x8(dpl), tacc);
-      tacc = mfma_bf16(as_bf16x8(slo), as_bf16x8(dph), tacc);
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        u32x4 sh, slo;
+        split8(St[p][kb >> 1], kb & 1, sh, slo);
+        tacc[p] = mfma_bf16(as_bf16x8(sh), as_bf16x8(dph), tacc[p]);
+        tacc[p] = mfma_bf16(as_bf16x8(sh), as_bf16x8(dpl), tacc[p]);
+        tacc[p] = mfma_bf16(as_bf16x8(slo), as_bf16x8(dph), tacc[p]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 4. a (FT), the wave's row maximum, and the wave's shares
-    f32x16 pq = {};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      pq = mfma_bf16(as_bf16x8(rows_operand(wl, fb, lane, ks)), as_bf16x8(tile_row8(B.q, ql, ks, h)), pq);
+    // 4. a (FT), the wave's row maximum over its tiles, and the wave's shares
+    f32x16 pq[TPW];
     float mx = kNegInf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[fb + 8 * j + 4 * h]);
+    for (int p = 0; p < TPW; ++p) {
+      const int fb = fw + 32 * p;
+      pq[p] = f32x16{};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pq[4 * j + e] = fmaf(kLog2e, pq[4 * j + e], cc[e]);
-        mx = fmaxf(mx, pq[4 * j + e]);
+      for (int ks = 0; ks < 4; ++ks)
+        pq[p] = mfma_bf16(as_bf16x8(rows_operand(wl, fb, lane, ks)), as_bf16x8(tile_row8(B.q, ql, ks, h)), pq[p]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 cc = *reinterpret_cast<const f32x4*>(&cl[fb + 8 * j + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pq[p][4 * j + e] = fmaf(kLog2e, pq[p][4 * j + e], cc[e]);
+          mx = fmaxf(mx, pq[p][4 * j + e]);
+        }
       }
     }
     const float Mw = pair_max(mx);
-    float G[16], Dp = 0.f, Gs = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 zc = *reinterpret_cast<const f32x4*>(&zl[wave][8 * j + 4 * h]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * j + e;
-        const float a = fast_exp2(pq[i] - Mw);
-        Dp = fmaf(a, zc[e] + zacc[i], Dp);
-        G[i] = a * fmaf(-zc[e], delta, tacc[i]);
-        Gs += G[i];
-      }
-    }
+    float Dp = 0.f, Gs = 0.f;
     f32x16 acc[2] = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 gh, gl;
-      split8(G, kb, gh, gl);
+    for (int p = 0; p < TPW; ++p) {
+      const int fb = fw + 32 * p;
+      float G[16];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const u32x4 wb = cols_operand(wl, fb, kb, dt, lane);
-        acc[dt] = mfma_bf16(as_bf16x8(gh), as_bf16x8(wb), acc[dt]);
-        acc[dt] = mfma_bf16(as_bf16x8(gl), as_bf16x8(wb), acc[dt]);
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 zc = *reinterpret_cast<const f32x4*>(&zl[wave][32 * p + 8 * j + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          const float a = fast_exp2(pq[p][i] - Mw);
+          Dp = fmaf(a, zc[e] + zacc[p][i], Dp);
+          G[i] = a * fmaf(-zc[e], delta, tacc[p][i]);
+          Gs += G[i];
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4 gh, gl;
+        split8(G, kb, gh, gl);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const u32x4 wb = cols_operand(wl, fb, kb, dt, lane);
+          acc[dt] = mfma_bf16(as_bf16x8(gh), as_bf16x8(wb), acc[dt]);
+          acc[dt] = mfma_bf16(as_bf16x8(gl), as_bf16x8(wb), acc[dt]);
+        }
       }
     }
     const float Dw = pair_sum(Dp), Gw = pair_sum(Gs);
@@ -1006,11 +1037,17 @@ __global__ __launch_bounds__(2 * M) void k_bw_query_causal(
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const u32x4 va = v_operand(B.v, 16 * kb, ct, lane);
-        St[ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(bth[kb]), St[ct]);
-        St[ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(btl[kb]), St[ct]);
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          St[p][ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(bth[p][kb]), St[p][ct]);
+          St[p][ct] = mfma_bf16(as_bf16x8(va), as_bf16x8(btl[p][kb]), St[p][ct]);
+        }
       }
-    zs = pair_sum(zs);
-    if (lane < 32) zl[wave][lane] += zs;
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      const float zsum = pair_sum(zs[p]);
+      if (lane < 32) zl[wave][32 * p + lane] += zsum;
+    }
     __syncthreads();   // shares visible
     // combine: thread -> one query and CPQ columns
     {
@@ -1373,7 +1410,8 @@ hipError_t launch_causal_m(const BwPlan& p, const uint16_t* q, const uint16_t* k
   FAVOR_LAUNCH("k_bw_kstate", kst, gs, bs, 0, s, k, v, W, cpart, pS, pz, p.H, p.n, p.splits, p.span);
   FAVOR_LAUNCH("k_bw_cmax", k_bw_cmax, dim3((BH * p.m + 255) / 256), dim3(256), 0, s, cpart, cfin, BH * p.m, p.m,
                p.splits);
-  auto kq = k_bw_query_causal<M>;
+  // a tile per wave: two tiles per wave (4 waves at m = 256) walked slower (453 against 400 us)
+  auto kq = k_bw_query_causal<M, 1>;
   FAVOR_LAUNCH("k_bw_query_causal", kq, gs, bs, 0, s, q, k, v, W, y, dy, cfin, cpart, pS, pz, dq, aux, p.H, p.n,
                p.splits, p.span);
   auto kr = k_bw_rstate<M>;
