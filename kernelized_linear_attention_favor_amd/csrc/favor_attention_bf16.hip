@@ -320,9 +320,9 @@ __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, con
     kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, augB, fs, lane & 31, lane >> 5, lane);
 }
 
-// NW waves of FT 32-feature tiles each cover all m = 32 NW FT features.  With
-// FT = 2 a workgroup has half the waves, so two workgroups (independent key
-// ranges, not in barrier lockstep) share each CU.
+// NW waves of FT 32-feature tiles each cover all m = 32 NW FT features.  The
+// library launches FT = 1: with FT = 2 (half the waves, so that two workgroups
+// share a CU) the kernel does not fit its register budget without spills.
 template <int NW, int FT>
 __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void k_kv_state(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
@@ -715,15 +715,6 @@ hipError_t launch_out(const Bf16Plan& p, const uint16_t* q, const uint16_t* W, c
 
 }  // namespace
 
-// Feature tiles per state wave: the non-causal pass (many key ranges) uses
-// two per wave so that two independent workgroups share a CU; the causal
-// segment pass (one range per CU) keeps one.
-#ifndef FAVOR_KV_FT
-#define FAVOR_KV_FT 1
-#endif
-static int kv_features_per_wave(int m, int causal) { return (!causal && m >= 128) ? FAVOR_KV_FT : 1; }
-static int kv_features_per_wave(const Bf16Plan& p) { return kv_features_per_wave(p.m, p.causal); }
-
 bool bf16_supported(int d, int m) { return d == kD && (m == 64 || m == 128 || m == 256); }
 
 Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
@@ -741,8 +732,8 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
     // one chunk-walking workgroup per CU: segments per (b, h)
     splits = (256 + BH - 1) / BH;
   } else {
-    // about 2048 state waves (8 per CU); a workgroup has m/(32 FT) waves
-    const long long wgs = 2048 / (m / (32 * kv_features_per_wave(m, causal)));
+    // about 2048 state waves (8 per CU); a workgroup has m/32 waves
+    const long long wgs = 2048 / (m / 32);
     splits = (wgs + BH - 1) / BH;
   }
   if (splits > max_splits) splits = max_splits;
@@ -776,14 +767,8 @@ hipError_t launch_state_bf16(const Bf16Plan& p, const uint16_t* k, const uint16_
   hipError_t e = hipSuccess;
   switch (p.m) {
     case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-    case 128:
-      e = kv_features_per_wave(p) == 2 ? launch_kv<2, 2>(p, k, v, W, pS, pzc, pvm, s)
-                                       : launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s);
-      break;
-    case 256:
-      e = kv_features_per_wave(p) == 2 ? launch_kv<4, 2>(p, k, v, W, pS, pzc, pvm, s)
-                                       : launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s);
-      break;
+    case 128: e = launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s); break;
+    case 256: e = launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
@@ -806,14 +791,8 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   if (!p.causal || p.splits > 1) {
     switch (p.m) {
       case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-      case 128:
-        e = kv_features_per_wave(p) == 2 ? launch_kv<2, 2>(p, k, v, W, pS, pzc, pvm, s)
-                                         : launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s);
-        break;
-      case 256:
-        e = kv_features_per_wave(p) == 2 ? launch_kv<4, 2>(p, k, v, W, pS, pzc, pvm, s)
-                                         : launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s);
-        break;
+      case 128: e = launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s); break;
+      case 256: e = launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s); break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
