@@ -9,11 +9,18 @@ independent input sets rotate between steps so that the 256 MB Infinity Cache
 cannot hold a step's working set.  Inputs are resident in HBM before timing.
 
 Prints one JSON line:
-  value          tokens/s for the step (B*n tokens per step)
+  value          tokens/s for the step (B*n tokens per step); the timed region
+                 holds the K steps only, with events at its two ends
   roofline       dominant kernel: algorithmic bytes per launch / mean launch
-                 time (HIP events on the launch stream), against 8 TB/s HBM
+                 time (HIP events around that kernel alone, on its launch
+                 stream, in a separate pass), against 8 TB/s HBM
   cpu_baseline   the fp64 oracle timed on host cores on a sample of the same
                  workload (whole (b, h) slices)
+  per_call       per-call kernel totals and median / p10 / p90 call times
+  valu, rates    instruction-rate probes (v_exp_f32, v_fma_f32) and each
+                 exp-forming kernel's exponential floor at the measured rate
+  workloads      the causal n=32768 and vision-style workloads, per call
+  environment    GPU, clocks, ROCm / HIP versions, the library file timed
 and, each measured outside the timed step with its own HIP events and the
 oracle timed beside it: decode (streaming decode on the same shape),
 feature_maps (ReLU and elu+1 maps), feature_draw (on-device W), backward and
@@ -97,6 +104,98 @@ def read_traffic(kernel: str, digest: str):
     return None
 
 
+def _pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    k = (len(xs) - 1) * q
+    lo = int(k)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def dist(us_list) -> dict:
+    """median / p10 / p90 / mean of a list of per-call times (microseconds)."""
+    return {"median_us": round(_pct(us_list, 0.5), 2), "p10_us": round(_pct(us_list, 0.1), 2),
+            "p90_us": round(_pct(us_list, 0.9), 2), "mean_us": round(sum(us_list) / len(us_list), 2),
+            "calls": len(us_list)}
+
+
+def environment(torch) -> dict:
+    """GPU, clocks, software versions and the library that was timed."""
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    env = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        clocks = [ln.split(":", 1)[1].strip() if ":" in ln else ln.strip()
+                  for ln in r.stdout.splitlines() if "sclk" in ln.lower() or "mclk" in ln.lower()]
+        env["clocks"] = clocks[:4] or None
+    except Exception as e:  # the tool may be absent; the line still prints
+        env["clocks"] = f"unavailable ({type(e).__name__})"
+    from kernelized_linear_attention_favor_amd import _lib as L
+    h = hashlib.sha256()
+    with open(L.LIB_PATH, "rb") as fh:
+        h.update(fh.read())
+    env["library"] = {"path": os.path.relpath(L.LIB_PATH, ROOT), "sha256": h.hexdigest()[:16]}
+    return env
+
+
+def probe_rates(torch) -> dict | None:
+    """Vector-unit rates from libfavor_ubench (v_exp_f32, v_fma_f32, both
+    interleaved), per second over the whole chip.  None if the probe library
+    is missing."""
+    import ctypes
+    path = os.path.join(ROOT, "kernelized_linear_attention_favor_amd", "libfavor_ubench.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    blocks, threads, iters = 8192, 256, 2048
+    out = torch.empty(blocks * threads, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, per_iter in (("exp2", (8, 0)), ("fma", (0, 8)), ("mix", (8, 32))):
+        fn = getattr(L, f"favor_ubench_{name}")
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        assert fn(out.data_ptr(), blocks, threads, 16, st) == 0
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            assert fn(out.data_ptr(), blocks, threads, iters, st) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(times)[len(times) // 2]
+        lanes = blocks * threads * iters
+        res[name] = {"exp_per_s": lanes * per_iter[0] / t, "fma_per_s": lanes * per_iter[1] / t,
+                     "seconds": t}
+    return {
+        "exp2_per_s": round(res["exp2"]["exp_per_s"], -9),
+        "fma_per_s": round(res["fma"]["fma_per_s"], -9),
+        "mix_exp_per_s": round(res["mix"]["exp_per_s"], -9),
+        "mix_fma_per_s": round(res["mix"]["fma_per_s"], -9),
+        "note": "lane operations per second over the chip; mix interleaves 1 exp with 4 fma per chain step",
+    }
+
+
+def exps_per_launch(name: str, B: int, H: int, n: int, m: int) -> float:
+    """Exponentials a kernel must evaluate per launch: one per (token, feature)
+    pair on each side it forms features for (the causal chunk kernel forms the
+    query features, the key features of the running state and the key features
+    of the chunk term)."""
+    tf = float(B * H * n * m)
+    return {"k_kv_state": tf, "k_causal_state": tf, "k_output": tf, "k_causal_output": 3 * tf}.get(name, 0.0)
+
+
 # ----------------------------------------------------------- CPU baseline
 _ORACLE_INPUT = None
 
@@ -114,7 +213,8 @@ def cpu_baseline(x, cfg, with_causal: bool, budget_s: float = 10.0) -> dict:
     """Time the fp64 oracle (as it stands) on whole (b, h) slices of the workload."""
     global _ORACLE_INPUT
     _ORACLE_INPUT = x
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    host = len(os.sched_getaffinity(0))
+    cores = min(host, 16)   # a GPU box's CPU share is 16 cores for one GPU, whatever it reports
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     slices = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     ctx = mp.get_context("fork")
@@ -142,8 +242,22 @@ def cpu_baseline(x, cfg, with_causal: bool, budget_s: float = 10.0) -> dict:
         "cores": cores,
         "kind": "oracle",
         "sample": f"{done} whole (b,h) slices of n={cfg.n} (d={cfg.d}, m={cfg.m}) through {variants} "
-                  f"fp64 NumPy oracle in {wall:.1f} s on {cores} worker processes",
+                  f"fp64 NumPy oracle in {wall:.1f} s on {cores} worker processes (one per core; "
+                  f"{host} cores visible, capped at 16, the CPU share of one GPU)",
+        "host_cores_visible": host,
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ---------------------------------------------------------- streaming decode
@@ -402,6 +516,53 @@ def bench_backward(favor, _lib, torch, cfg, sets, dev, steps: int, cpu_budget_s:
     return out
 
 
+# ----------------------------------------------------------- other workloads
+BUDGETS_US = {"C3": 70.0, "C4": 104.9, "C5": 209.8}   # 60% of the HBM roof per call
+
+
+def bench_workload(favor, torch, fi, name: str, causal: bool, dev, calls: int, sets: int = 2) -> dict:
+    """One attention call per step on another workload (its own inputs, rotated
+    sets, workspace pre-allocated): per-call HIP-event times on the launch
+    stream (median / p10 / p90), tokens/s and HBM fraction against its budget."""
+    cfg = fi.config(name)
+    B, H, n, d, m = cfg.B, cfg.H, cfg.n, cfg.d, cfg.m
+    xs = []
+    for si in range(sets):
+        x = fi.make_inputs(cfg, set_index=si)
+        xs.append({k: torch.from_numpy(v).to(device=dev, dtype=torch.bfloat16) for k, v in x.items()})
+        del x
+    ws = favor.Workspace(B, H, n, d, m, causal=causal)
+    outs = [torch.empty((B, H, n, d), dtype=torch.float32, device=dev) for _ in range(sets)]
+
+    def call(i):
+        t = xs[i % sets]
+        favor.attention(t["q"], t["k"], t["v"], t["W"], causal=causal, out=outs[i % sets], workspace=ws)
+
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i in range(calls):
+        ev[i][0].record()
+        call(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    assert all(bool(torch.isfinite(o).all()) for o in outs), f"{name} produced non-finite outputs"
+    dd = dist(us)
+    call_bytes = 10.0 * B * H * n * d + 2.0 * H * m * d
+    med = dd["median_us"]
+    return {
+        "workload": f"{name}: FAVOR+ {'causal (chunk 64)' if causal else 'non-causal'} B={B} H={H} n={n} d={d} "
+                    f"m={m}" + (" (low-rank Q/K vision stand-in)" if cfg.qk == "lowrank" else ""),
+        "per_call": dd,
+        "tokens_per_s": round(B * n / (med * 1e-6), 1),
+        "bytes_per_call": call_bytes,
+        "hbm_frac": round(call_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "budget_us": BUDGETS_US.get(name),
+    }
+
+
 # ------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -415,6 +576,8 @@ def main() -> int:
     ap.add_argument("--no-phi", action="store_true", help="skip the ReLU / elu+1 feature-map measurement")
     ap.add_argument("--no-draw", action="store_true", help="skip the on-device feature draw measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the C4 causal and C5 vision legs")
+    ap.add_argument("--no-probes", action="store_true", help="skip the instruction-rate probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="before timing, run a plain elementwise copy (negation) of MB MiB fp32 three "
                          "times; its HBM counters calibrate the per-kernel traffic figures")
@@ -424,7 +587,7 @@ def main() -> int:
               "(the path would shard over (b, h) or over the sequence)", file=sys.stderr)
         return 2
 
-    import numpy as np
+    import numpy as np  # noqa: F401
     import torch
 
     import favor_inputs as fi
@@ -474,49 +637,70 @@ def main() -> int:
               file=sys.stderr, flush=True)
         del src, dst
 
-    def step(i):
+    def call_nc(i):
         t = sets[i % len(sets)]
         favor.attention(t["q"], t["k"], t["v"], W, causal=False, out=outs_nc[i % len(sets)], workspace=ws_nc)
-        if causal_ok:
-            favor.attention(t["q"], t["k"], t["v"], W, causal=True, out=outs_c[i % len(sets)], workspace=ws_c)
 
-    # warmup, with every kernel timed to find the dominant one
+    def call_c(i):
+        t = sets[i % len(sets)]
+        favor.attention(t["q"], t["k"], t["v"], W, causal=True, out=outs_c[i % len(sets)], workspace=ws_c)
+
+    def step(i):
+        call_nc(i)
+        if causal_ok:
+            call_c(i)
+
+    # warmup (no instrumentation)
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    _lib.check(_lib.favor_profile_enable())
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    wprof = _lib.favor_profile_collect()
-    if wprof:
-        dname = max(wprof.items(), key=lambda kv: kv[1][1])[0]
-    else:
-        dname = "k_causal_output" if causal_ok else "k_output"
 
-    # timed region: HIP events bracket only the dominant kernel's launches (on
-    # its launch stream), so the other kernels run back to back as they would
+    # timed region: K steps back to back, events only at its two ends (on the
+    # stream every kernel is launched on: torch's current stream)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    _lib.check(_lib.favor_profile_enable_only(dname))
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
         step(i)
     e1.record()
     torch.cuda.synchronize()
-    prof = _lib.favor_profile_collect()
     ms = e0.elapsed_time(e1) / args.steps
-    dcount, dtotal = prof[dname]
-    avg_ms = dtotal / dcount
 
-    # per-kernel breakdown from a further pass with every kernel timed (not the timed region)
+    # per-kernel breakdown (every launch bracketed by events; outside the timed region)
     _lib.check(_lib.favor_profile_enable())
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     bprof = _lib.favor_profile_collect()
-    print(f"[bench] {ms:.4f} ms/step; {dname} {avg_ms * 1e3:.1f}us in the timed region; kernels: " +
-          ", ".join(f"{k} {c}x {t / c * 1e3:.1f}us" for k, (c, t) in bprof.items()),
+    dname = max(bprof.items(), key=lambda kv: kv[1][1])[0]
+
+    # the dominant kernel alone bracketed (its launch stream), for the roofline
+    _lib.check(_lib.favor_profile_enable_only(dname))
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dcount, dtotal = _lib.favor_profile_collect()[dname]
+    avg_ms = dtotal / dcount
+
+    # per-call distributions (events between calls only)
+    calls = {"noncausal": [], "causal": []}
+    for i in range(args.steps):
+        for g, fn in (("noncausal", call_nc), ("causal", call_c)):
+            if g == "causal" and not causal_ok:
+                continue
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(i)
+            b.record()
+            calls[g].append((a, b))
+    torch.cuda.synchronize()
+    call_dist = {g: dist([a.elapsed_time(b) * 1e3 for a, b in ev]) for g, ev in calls.items() if ev}
+    print(f"[bench] {ms:.4f} ms/step; {dname} {avg_ms * 1e3:.1f}us (alone bracketed); calls: "
+          + json.dumps(call_dist) + "; kernels: "
+          + ", ".join(f"{k} {c}x {t / c * 1e3:.1f}us" for k, (c, t) in bprof.items()),
           file=sys.stderr, flush=True)
 
     # the self-allocating entries: no workspace argument, so each call allocates,
@@ -571,7 +755,34 @@ def main() -> int:
                 "tokens_per_s": round(tokens / (us * 1e-6), 1),
                 "hbm_frac": round(call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "tflops": round(call_flops / (us * 1e-6) / 1e12, 2),
+                "call": call_dist.get(g),
+                "budget_us": BUDGETS_US["C3"],
             }
+
+    rates = None
+    if not args.no_probes:
+        print("[bench] instruction-rate probes", file=sys.stderr, flush=True)
+        rates = probe_rates(torch)
+        print(f"[bench] rates: {json.dumps(rates)}", file=sys.stderr, flush=True)
+    valu = None
+    if rates:
+        # the exponential floor of each exp-forming kernel: its exps at the measured rate
+        valu = {"exp2_per_s": rates["exp2_per_s"], "kernels": {}}
+        for k, v in kernels.items():
+            ne = exps_per_launch(k, B, H, n, m)
+            if ne > 0:
+                fl = ne / rates["exp2_per_s"] * 1e6
+                valu["kernels"][k] = {"exps_per_launch": ne, "exp_floor_us": round(fl, 2),
+                                      "frac": round(fl / v["mean_us"], 4)}
+
+    extra = None
+    if not args.no_workloads:
+        extra = {}
+        for name, causal in (("C4", True), ("C5", False)):
+            print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+            extra[name] = bench_workload(favor, torch, fi, name, causal, dev, calls=args.steps)
+            print(f"[bench] {name}: {json.dumps(extra[name])}", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
 
     dec = None
     if not args.no_decode:
@@ -631,6 +842,9 @@ def main() -> int:
         "cpu_baseline": cpu,
         "per_call": per_call,
         "kernels": kernels,
+        "valu": valu,
+        "rates": rates,
+        "workloads": extra,
         "decode": dec,
         "feature_maps": phi,
         "feature_draw": draw,
@@ -639,6 +853,7 @@ def main() -> int:
                                "allocated, cleared and freed stream-ordered in every call)"},
         "backward": bwd,
         "backward_causal": bwd_c,
+        "environment": environment(torch),
         "sources": digest,
     }
     print(json.dumps(out))

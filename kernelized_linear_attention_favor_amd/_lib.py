@@ -10,8 +10,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# LIBFAVOR_PATH selects another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("LIBFAVOR_PATH") or os.path.join(_HERE, "libfavor.so")
+# Always the library build.py writes next to this file: no other build is ever loaded.
+LIB_PATH = os.path.join(_HERE, "libfavor.so")
 
 FAVOR_OK = 0
 FAVOR_ERR_INVALID_ARGUMENT = 1

@@ -2,6 +2,8 @@
 
 Every .hip / .cpp file under csrc/ is compiled to an object under _build/ (in
 parallel) and linked into kernelized_linear_attention_favor_amd/libfavor.so.
+The instruction-rate probes under ubench/ (used by bench.py's measurements,
+not part of the attention library) go into libfavor_ubench.so beside it.
 """
 from __future__ import annotations
 
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfavor.so")
+UBENCH = os.path.join(PKG, "ubench")
+UBENCH_LIB = os.path.join(PKG, "libfavor_ubench.so")
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -49,19 +53,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    usrcs = sorted(glob.glob(os.path.join(UBENCH, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(usrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + usrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], UBENCH_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {UBENCH_LIB}")
     return LIB
 
 

@@ -16,7 +16,10 @@
 //   dv_j = R^T b_j,  H_jf = b_jf (R_f.v_j - rho_f),  dk_j = W^T H_j - k_j sum_f H_jf
 // (d phi_f(x) / dx = phi_f(x) (w_f - x)).  The key shift C_f is one constant per
 // feature for the whole head, so these are plain bounded sums in fp32; a
-// feature's key exponents may spread up to ~2^126 below its largest.
+// feature's key exponents may spread up to ~2^126 below its largest.  A query
+// whose D_i underflows to 0 (all its visible keys beyond that spread in every
+// feature) gets dq_i = 0 and adds nothing to R, rho: a defined, finite result
+// at the range limit instead of inf/NaN.
 //
 // Kernels (non-causal): k_bw_keys (S, z partials with a running shift per
 // range), k_bw_merge (C_f; the sum, written as bf16 hi + lo row-major tiles),
@@ -42,6 +45,12 @@ using bf16k::v_operand;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ int drow(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// 1 / D_i, and 0 where D_i = 0: a query whose visible keys all lie more than
+// ~2^126 below the head's per-feature key maximum C_f in every feature (the
+// range limit of the shift) then contributes nothing: dq_i = 0 and no share of
+// R, rho.  NaN stays NaN.
+__device__ __forceinline__ float recip_or_zero(float D) { return D == 0.f ? 0.f : 1.f / D; }
 
 template <typename X>
 __device__ __forceinline__ void split8(const X& x, int kb, u32x4& hi, u32x4& lo) {
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(512) void k_bw_query(const uint16_t* __restrict__ Q
     }
     const float Di = pair_sum(Dp), Gsum = pair_sum(Gs);
     if (lane < 32) {
-      rdl[wave][lane] = 1.f / Di;
+      rdl[wave][lane] = recip_or_zero(Di);
       gsl[wave][lane] = Gsum;
       if (ok) *reinterpret_cast<f32x4*>(aux + (rowbase + row) * 4) = f32x4{Mi, Di, delta, 0.f};
     }
@@ -512,7 +521,7 @@ __global__ __launch_bounds__(2 * M) void k_bw_rstate(const uint16_t* __restrict_
       *reinterpret_cast<u32x4*>(dh + swz(r, ch)) = hi;
       *reinterpret_cast<u32x4*>(dlo + swz(r, ch)) = lo;
     }
-    if (t < 64) ax[t] = f32x4{pa[0], 1.f / pa[1], pa[2], 0.f};   // (M_i, 1 / D_i, delta_i)
+    if (t < 64) ax[t] = f32x4{pa[0], recip_or_zero(pa[1]), pa[2], 0.f};   // (M_i, 1 / D_i, delta_i)
     __syncthreads();
     if (tok0 + 64 < j1) fetch(tok0 + 64);
 #pragma unroll
@@ -799,7 +808,7 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<NT, QSIDE>& R, Chunk
   if constexpr (!QSIDE) {   // (M_i, 1 / D_i, delta_i)
     if (t < 32) {
       B.am[t] = R.ax[0];
-      B.ar[t] = 1.f / R.ax[1];
+      B.ar[t] = recip_or_zero(R.ax[1]);
       B.ad[t] = R.ax[2];
     }
   }
@@ -1064,7 +1073,7 @@ __global__ __launch_bounds__(M * 2 / TPW) void k_bw_query_causal(
         u = fmaf(sc[w], sl_u[w][q], u);
       }
       if (r < t1) {
-        const float rD = 1.f / D;
+        const float rD = recip_or_zero(D);
 #pragma unroll
         for (int e4 = 0; e4 < CPQ; e4 += 4) {
           f32x4 U = {0.f, 0.f, 0.f, 0.f};

@@ -36,6 +36,9 @@ using namespace bf16k;
 // ---------------------------------------------------------------------------
 // phase 3
 // ---------------------------------------------------------------------------
+// Hand-over flag values (per chunk c: value + c; chunks fit in 2^28).
+constexpr int kGive = 1, kNoGive = -(1 << 28), kClaim = 1 << 28, kAbandon = 2 << 28;
+
 template <int NW>
 struct CsSmem {
   static constexpr int M = NW * 32;
@@ -53,7 +56,7 @@ struct CsSmem {
   float dp[NW][32];                  // per wave: partial denominators
   float lp[NW][32];                  // per wave: log2 scale of the partials
   float xs[NW][32];                  // per wave: per-feature scalars, lane -> register layout
-  int hflag[NW / 2];                 // per feature group: key tile 0 handed over (chunk + 1)
+  int hflag[NW / 2];                 // per feature group: key tile 0 hand-over state (kGive ...)
   float htile[NW / 2];               // ... and its shift
   __device__ float* gexp() { return &colmax[0][0]; }
   __device__ const float* gexp() const { return &colmax[0][0]; }
@@ -288,25 +291,46 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   // Key tile 0 is the query tile 0 wave's diagonal tile and the query tile 1
   // wave's off-diagonal one, with the same shared shift unless the former
   // needs per-key shifts.  The tile 0 wave hands its operands over through the
-  // tile 1 wave's partial slot (free until that wave's own partials) and a
-  // per-chunk flag: +(chunk+1) handed over, -(chunk+1) not.  The tile 1 wave
-  // takes its diagonal tile first and computes tile 0 itself when nothing was
-  // handed over (or after a bounded wait).
+  // tile 1 wave's partial slot (free until that wave's own partials), guarded
+  // by a per-chunk flag whose values name the chunk:
+  //   kGive + c   operands handed over       kNoGive + c  none (per-key shifts)
+  //   kClaim + c  tile 0 is writing them     kAbandon + c tile 1 gave up waiting
+  // The tile 0 wave claims the slot (compare-and-swap) before its first write
+  // and writes nothing once tile 1 has abandoned the chunk; the tile 1 wave
+  // abandons only a chunk that tile 0 has not claimed (the same compare-and-
+  // swap), so the slot is never written by both.  A claimed hand-over is
+  // straight-line code up to its release, so waiting for it always ends.
   const int grp = wave % (NW / 2);
   uint32_t* hand = reinterpret_cast<uint32_t*>(sm.np[NW / 2 + grp]);
+  const int cgive = kGive + chunk, cnogive = kNoGive + chunk;
+  const int cclaim = kClaim + chunk, cabandon = kAbandon + chunk;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int kt = qt == 1 ? 1 - kk : kk;   // the diagonal tile first
     if (kt > qt) continue;
     if (qt == 1 && kt == 0) {
-      const int want = chunk + 1;
       int f = 0;
-      for (int it = 0; it < 4096; ++it) {
+      for (int it = 0;;) {
         f = __hip_atomic_load(&sm.hflag[grp], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (f == want || f == -want) break;
+        if (f == cgive || f == cnogive) break;
+        if (f != cclaim && ++it >= 4096) {
+          // tile 0 has not claimed the slot: abandon the hand-over, unless the
+          // flag moved meanwhile (then look again)
+          int ok = 0;
+          if (lane == 0) {
+            int expect = f;
+            ok = __hip_atomic_compare_exchange_strong(&sm.hflag[grp], &expect, cabandon, __ATOMIC_ACQ_REL,
+                                                      __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+          if (__builtin_amdgcn_readfirstlane(ok)) {
+            f = cabandon;
+            break;
+          }
+          continue;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
-      if (f == want) {
+      if (f == cgive) {
         s[0] = sm.htile[grp];
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft)
@@ -342,6 +366,17 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         sh = pk_shift ? -bm : (T == -kFInf ? -kFInf : kn - T);
         s[kt] = T;
         give = qt == 0 && !perkey;
+        if (give) {
+          // claim the slot before the first write (fails once tile 1 abandoned the chunk)
+          int ok = 0;
+          if (lane == 0) {
+            int expect = __hip_atomic_load(&sm.hflag[grp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            ok = expect != cabandon &&
+                 __hip_atomic_compare_exchange_strong(&sm.hflag[grp], &expect, cclaim, __ATOMIC_ACQ_REL,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+          give = __builtin_amdgcn_readfirstlane(ok) != 0;
+        }
       }
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -365,10 +400,11 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       }
     }
     if (qt == 0) {
-      // the flag is released after the operands and the shift
+      // the flag is released after the operands and the shift; an abandoned
+      // chunk keeps its flag (tile 1 computes key tile 0 itself)
       if (give && lane == 0) sm.htile[grp] = s[0];
-      if (lane == 0)
-        __hip_atomic_store(&sm.hflag[grp], give ? chunk + 1 : -(chunk + 1), __ATOMIC_RELEASE,
+      if (lane == 0 && (give || perkey))
+        __hip_atomic_store(&sm.hflag[grp], give ? cgive : cnogive, __ATOMIC_RELEASE,
                            __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }

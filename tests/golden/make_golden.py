@@ -25,17 +25,24 @@ import oracle  # noqa: E402
 B, H, n, d, m = 1, 2, 12, 8, 16
 
 
-def exact_grid(shape, num, den, offset):
-    """Integers in [-den/2, den/2) times 1/den: exact in fp32 and bf16."""
-    k = np.arange(int(np.prod(shape)), dtype=np.int64)
-    return (((k * num + offset) % den) - den // 2).reshape(shape).astype(np.float64) / den
+def exact_grid(shape, a, b, c, den, offset):
+    """Entries ((a r^2 + b j + c r j + 5 s + offset) mod den - den/2) / den for row
+    r, column j and leading (batch, head) index s: exact binary fractions in fp32
+    and bf16 (den a power of two), different from row to row and from head to
+    head."""
+    *lead, rows, cols = shape
+    s = np.arange(int(np.prod(lead)) if lead else 1, dtype=np.int64)[:, None, None]
+    r = np.arange(rows, dtype=np.int64)[None, :, None]
+    j = np.arange(cols, dtype=np.int64)[None, None, :]
+    k = (a * r * r + b * j + c * r * j + 5 * s + offset) % den
+    return ((k - den // 2).astype(np.float64) / den).reshape(shape)
 
 
 def main():
-    q = exact_grid((B, H, n, d), 7, 16, 3) * 0.5
-    k = exact_grid((B, H, n, d), 5, 16, 1) * 0.5
-    v = exact_grid((B, H, n, d), 3, 8, 5)
-    W = exact_grid((H, m, d), 11, 32, 7) * 2.0
+    q = exact_grid((B, H, n, d), 3, 7, 5, 32, 3) * 2.0
+    k = exact_grid((B, H, n, d), 5, 3, 9, 32, 1) * 2.0
+    v = exact_grid((B, H, n, d), 7, 5, 3, 16, 5)
+    W = exact_grid((H, m, d), 1, 11, 13, 32, 7) * 2.0
     out = {
         "description": "FAVOR+ on a tiny exact-binary-fraction input; fp64 oracle outputs",
         "shape": {"B": B, "H": H, "n": n, "d": d, "m": m},

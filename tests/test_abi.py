@@ -38,6 +38,28 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(L.SIGNATURES)
 
 
+UBENCH_HEADER = os.path.join(ROOT, "include", "favor_ubench.h")
+UBENCH_LIB = os.path.join(ROOT, "kernelized_linear_attention_favor_amd", "libfavor_ubench.so")
+
+
+def test_probe_library_exports_its_header():
+    """The instruction-rate probes (bench.py's measurements) are a library of
+    their own; it exports what its header declares and rejects bad launches."""
+    if not os.path.exists(UBENCH_LIB):
+        pytest.skip("libfavor_ubench.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(UBENCH_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(favor_ubench_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["favor_ubench_exp2", "favor_ubench_fma", "favor_ubench_mix"]
+    raw = ctypes.CDLL(UBENCH_LIB)
+    for name in names:
+        fn = getattr(raw, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        assert fn(None, 1, 64, 1, None) == 1          # null out
+        assert fn(0x100000, 1, 96, 1, None) == 1      # threads not a multiple of 64
+        assert fn(0x100000, 1, 64, 0, None) == 1      # no iterations
+
+
 def test_version_and_status_strings():
     L = _lib()
     assert L.favor_version() == 10000

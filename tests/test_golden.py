@@ -42,6 +42,20 @@ def test_fixture_inputs_exact_in_bf16():
         assert np.array_equal(g[key].astype(np.float32).astype(np.float64), g[key])
 
 
+def test_fixture_is_not_degenerate():
+    # every input row differs, and the outputs are not a constant-value or
+    # uniform-weight identity: y moves away from mean(v), rows of y differ, and
+    # the causal rows differ from the non-causal ones
+    g = load()
+    for key in ("q", "k", "v"):
+        rows = g[key].reshape(-1, g[key].shape[-1])
+        assert len({tuple(r) for r in rows}) == rows.shape[0], key
+    y, v, yc = g["y"], g["v"], g["y_causal"]
+    assert np.ptp(y, axis=-2).max() > 0.05
+    assert np.abs(y - v.mean(axis=-2, keepdims=True)).max() > 0.05
+    assert np.abs(yc[..., :-1, :] - y[..., :-1, :]).max() > 0.05
+
+
 def test_fixture_causal_first_row_is_v0():
     # inclusive causal reading: the first query sees only the first key
     g = load()

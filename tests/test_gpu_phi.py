@@ -10,6 +10,7 @@ import pytest
 
 import favor_inputs as fi
 import oracle
+import oracle_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -66,19 +67,19 @@ def test_phi_C2_shape(kind, m, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("kind,m", [("relu", 256), ("elu1", 64)])
-def test_phi_C3_shape_sampled(kind, m, causal):
-    """B=4, H=8, n=16384: the launch the benchmark times; rows sampled per (b, h)."""
+def test_phi_C3_shape_slices(kind, m, causal):
+    """B=4, H=8, n=16384: the launch the benchmark times; whole (b, h) slices
+    (every row) against the oracle, normalised by the oracle's own maximum."""
     x = inputs(4, 8, 16384, m, 3)
     y = run(x, kind, causal)
     assert np.all(np.isfinite(y))
-    rng = np.random.default_rng(5)
-    for b, h in ((0, 0), (1, 5), (3, 7)):
-        rows = np.sort(np.concatenate([[0, 1, 16383], rng.choice(16384, 13, replace=False)]))
-        W = None if kind == "elu1" else x["W"][h]
-        r = oracle.attention_quadratic_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h], W, rows, causal, kind=kind)
-        # normalise by the slice's own largest output, as the metric does
-        scale = np.max(np.abs(y[b, h]))
-        assert np.max(np.abs(y[b, h][rows] - r)) / scale < TOL
+    xx = dict(x)
+    if kind == "elu1":
+        xx["W"] = None
+    slices = [(0, 0), (1, 5), (2, 2), (3, 7)]
+    r = oracle_pool.reference(xx, causal=causal, kind=kind, slices=slices)
+    errs = oracle_pool.slice_errors(y, r, slices)
+    assert max(errs.values()) < TOL, errs
 
 
 @pytest.mark.parametrize("kind,m", [("relu", 128), ("elu1", 64)])
