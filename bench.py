@@ -59,6 +59,7 @@ def kernel_bytes(name: str, B: int, H: int, n: int, d: int, m: int) -> float:
         "k_output": tok * 2 + tok * 4 + W,           # Q in, y out
         "k_causal_state": 2 * tok * 2 + W,           # K, V
         "k_causal_output": 3 * tok * 2 + tok * 4 + W,  # Q, K, V in, y out
+        "k_causal_walk": 3 * tok * 2 + tok * 4 + W,    # Q, K, V in, y out (the general causal walk)
         # backward: bf16 q, k, v and fp32 y, dy, aux (M, D, delta) in; fp32 dq, dk, dv out
         "k_bw_query": tok * 2 + 2 * tok * 4 + tok * 4 + BH * n * 16 + W,         # q, y, dy -> dq, aux
         "k_bw_key": 2 * tok * 2 + 2 * tok * 4 + W,                              # k, v -> dk, dv
@@ -193,7 +194,8 @@ def exps_per_launch(name: str, B: int, H: int, n: int, m: int) -> float:
     query features, the key features of the running state and the key features
     of the chunk term)."""
     tf = float(B * H * n * m)
-    return {"k_kv_state": tf, "k_causal_state": tf, "k_output": tf, "k_causal_output": 3 * tf}.get(name, 0.0)
+    return {"k_kv_state": tf, "k_causal_state": tf, "k_output": tf, "k_causal_output": 3 * tf,
+            "k_causal_walk": 2 * tf}.get(name, 0.0)
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -746,7 +748,7 @@ def main() -> int:
     kernels = {k: {"launches": c, "mean_us": round(t / c * 1e3, 2)} for k, (c, t) in bprof.items()}
     per_call = {}
     groups = {"noncausal": ("k_kv_state", "k_merge", "k_output"),
-              "causal": ("k_causal_state", "k_causal_output")}
+              "causal": ("k_causal_state", "k_causal_output", "k_causal_walk", "k_slice_combine")}
     for g, names in groups.items():
         us = sum(kernels[k]["mean_us"] for k in names if k in kernels)
         if us > 0:

@@ -82,9 +82,11 @@ favor_status_t favor_feature_map_f32(const float* x, const float* W, float* phi,
  * query i sees keys j <= i (Performer for vision, Step 2); identical to
  * favor_attention_causal with chunk = 0.
  *   q, k, v : bf16 [B,H,n,d]     W : bf16 [H,m,d]        out : fp32 [B,H,n,d]
- * bf16 path: d == 64; m in {64, 128, 256}; pointers
- * 16-byte aligned; otherwise FAVOR_ERR_UNSUPPORTED.  Scratch is allocated
- * stream-ordered on `stream` (see favor_attention_ws to supply it).
+ * bf16 path: d in {32, 64}; m any multiple of 16 from 16 to 512 (m is the
+ * estimator's accuracy knob, Performer notes, FAVOR+); pointers 16-byte
+ * aligned; otherwise FAVOR_ERR_UNSUPPORTED.  The causal form uses chunks of 64
+ * tokens.  Scratch is allocated stream-ordered on `stream` (see
+ * favor_attention_ws to supply it).
  */
 favor_status_t favor_attention(const void* q, const void* k, const void* v, const void* W,
                                float* out, int B, int H, int n, int d, int m, int causal,
@@ -95,8 +97,11 @@ favor_status_t favor_attention(const void* q, const void* k, const void* v, cons
  * vision, How It Works, Step 2): the sequence is cut into chunks of `chunk`
  * tokens; each chunk combines the running key/value state of all earlier
  * chunks with the masked pairwise weights inside the chunk.  chunk == 0 picks
- * the default (64).  Supported chunk: 64.  Same shapes and limits as
- * favor_attention.
+ * the default (64).  Supported chunk: 16, 32, 64, 128 (any other positive
+ * value: FAVOR_ERR_UNSUPPORTED; negative: FAVOR_ERR_INVALID_ARGUMENT).  Every
+ * chunk length gives the same sums up to rounding; it sets how many keys join
+ * the running state at once and how large the masked pairwise block is.  Same
+ * shapes and limits as favor_attention.
  */
 favor_status_t favor_attention_causal(const void* q, const void* k, const void* v,
                                       const void* W, float* out, int B, int H, int n, int d,
@@ -118,9 +123,10 @@ favor_status_t favor_attention_causal_f32(const float* q, const float* k, const 
 /*
  * Caller-owned scratch for the bf16 attention path.  favor_workspace_bytes
  * returns the size favor_attention_ws needs for a shape (0 if the shape is not
- * supported).  The workspace must be zero-filled once before its first use
- * (hipMemset); every call leaves it ready for the next call.  Two calls that
- * share one workspace must not overlap in time (same stream is fine).
+ * supported; causal = 1 sizes the default chunk of 64).  The workspace needs
+ * no initialisation: every call writes each scratch word before reading it.
+ * Two calls that share one workspace must not overlap in time (same stream is
+ * fine).
  */
 size_t favor_workspace_bytes(int B, int H, int n, int d, int m, int causal);
 favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, const void* W,

@@ -10,7 +10,8 @@ CPU path, and calls on CPU tensors raise.
     st = State(B, H, d, m); st.from_keys(k, v, W)   # streaming decode: state of a prompt,
     y = decode(q1, k1, v1, W, st)              # then T new tokens at a time (bf16)
 
-Layouts: q, k, v, x [B, H, n, d]; W [H, m, d]; outputs float32.
+Layouts: q, k, v, x [B, H, n, d]; W [H, m, d]; outputs float32.  The bf16
+attention takes d in {32, 64} and m any multiple of 16 from 16 to 512.
 """
 from __future__ import annotations
 
@@ -156,7 +157,7 @@ def _attention_phi(q, k, v, W, causal, out, workspace, stream, code):
 
 def attention_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: torch.Tensor,
                      chunk: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Causal FAVOR+ by chunked prefix sums (chunk 0 = default)."""
+    """Causal FAVOR+ by chunked prefix sums: chunk in {16, 32, 64, 128}, 0 = the default (64)."""
     B, H, n, d, m = _shapes(q, W)
     dt = q.dtype
     for t, name in ((q, "q"), (k, "k"), (v, "v")):

@@ -116,7 +116,20 @@ favor_status_t check_bf16(const void* q, const void* k, const void* v, const voi
   if ((st = check_ptrs(q, k, v, W, out, 16)) != FAVOR_OK) return st;
   if (!favor::bf16_supported(d, m))
     return fail(FAVOR_ERR_UNSUPPORTED,
-                "bf16 attention supports d = 64 and m in {64, 128, 256} (d=%d m=%d)", d, m);
+                "bf16 attention supports d in {32, 64} and m a multiple of 16 from 16 to 512 (d=%d m=%d)", d, m);
+  return FAVOR_OK;
+}
+
+// The shapes of the decode, deterministic feature-map and backward kernels.
+bool fixed_shape(int d, int m) { return d == 64 && (m == 64 || m == 128 || m == 256); }
+
+favor_status_t check_fixed(const void* q, const void* k, const void* v, const void* W, float* out,
+                           int B, int H, int n, int d, int m, const char* what) {
+  favor_status_t st = check_sizes(B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  if ((st = check_ptrs(q, k, v, W, out, 16)) != FAVOR_OK) return st;
+  if (!fixed_shape(d, m))
+    return fail(FAVOR_ERR_UNSUPPORTED, "%s supports d = 64 and m in {64, 128, 256} (d=%d m=%d)", what, d, m);
   return FAVOR_OK;
 }
 
@@ -133,8 +146,8 @@ struct StreamScratch {
 
 favor_status_t run_bf16(const void* q, const void* k, const void* v, const void* W, float* out,
                         int B, int H, int n, int d, int m, int causal, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
-  favor::Bf16Plan plan = favor::bf16_plan(B, H, n, d, m, causal);
+                        hipStream_t stream, int chunk = favor::kDefaultChunk) {
+  favor::Bf16Plan plan = favor::bf16_plan(B, H, n, d, m, causal, chunk);
   StreamScratch own(stream);
   if (!ws) {
     hipError_t e = own.alloc(plan.off_end);
@@ -164,7 +177,7 @@ favor_status_t check_state_shape(const float* state, int B, int H, int d, int m)
     return fail(FAVOR_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (B=%d H=%d d=%d m=%d)", B, H, d, m);
   if (!state) return fail(FAVOR_ERR_INVALID_ARGUMENT, "state is null");
   if (!aligned(state, 16)) return fail(FAVOR_ERR_UNSUPPORTED, "state is not 16-byte aligned");
-  if (!favor::bf16_supported(d, m))
+  if (!fixed_shape(d, m))
     return fail(FAVOR_ERR_UNSUPPORTED, "decode supports d = 64 and m in {64, 128, 256} (d=%d m=%d)",
                 d, m);
   return FAVOR_OK;
@@ -182,7 +195,7 @@ favor_status_t check_phi(const void* q, const void* k, const void* v, const void
   if ((st = check_ptrs(q, k, v, Wc, out, 16)) != FAVOR_OK) return st;
   if (phi == FAVOR_PHI_ELU1 && (d != 64 || m != d))
     return fail(FAVOR_ERR_UNSUPPORTED, "elu(x)+1 features need d = m = 64 (d=%d m=%d)", d, m);
-  if (phi == FAVOR_PHI_RELU && !favor::bf16_supported(d, m))
+  if (phi == FAVOR_PHI_RELU && !fixed_shape(d, m))
     return fail(FAVOR_ERR_UNSUPPORTED, "ReLU features support d = 64 and m in {64, 128, 256} (d=%d m=%d)",
                 d, m);
   return FAVOR_OK;
@@ -298,12 +311,12 @@ favor_status_t favor_attention(const void* q, const void* k, const void* v, cons
 favor_status_t favor_attention_causal(const void* q, const void* k, const void* v, const void* W,
                                       float* out, int B, int H, int n, int d, int m, int chunk,
                                       hipStream_t stream) {
-  if (chunk != 0 && chunk != 64)
+  if (chunk != 0 && !favor::chunk_supported(chunk))
     return fail(chunk < 0 ? FAVOR_ERR_INVALID_ARGUMENT : FAVOR_ERR_UNSUPPORTED,
-                "chunk must be 0 (default) or 64 (got %d)", chunk);
+                "chunk must be 0 (default, %d) or one of 16, 32, 64, 128 (got %d)", favor::kDefaultChunk, chunk);
   favor_status_t st = check_bf16(q, k, v, W, out, B, H, n, d, m);
   if (st != FAVOR_OK) return st;
-  return run_bf16(q, k, v, W, out, B, H, n, d, m, 1, nullptr, 0, stream);
+  return run_bf16(q, k, v, W, out, B, H, n, d, m, 1, nullptr, 0, stream, chunk == 0 ? favor::kDefaultChunk : chunk);
 }
 
 size_t favor_workspace_bytes(int B, int H, int n, int d, int m, int causal) {
@@ -324,7 +337,7 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
 }
 
 size_t favor_state_bytes(int B, int H, int d, int m) {
-  if (B < 1 || H < 1 || !favor::bf16_supported(d, m)) return 0;
+  if (B < 1 || H < 1 || !fixed_shape(d, m)) return 0;
   return sizeof(float) * favor::state_floats(B, H, d, m);
 }
 
@@ -418,7 +431,7 @@ size_t favor_workspace_bytes_phi(int B, int H, int n, int d, int m, int causal, 
   if (phi == FAVOR_PHI_EXP) return favor_workspace_bytes(B, H, n, d, m, causal);
   if (B < 1 || H < 1 || n < 1 || d != 64 || (causal != 0 && causal != 1)) return 0;
   if (phi == FAVOR_PHI_ELU1 && m != d) return 0;
-  if (phi == FAVOR_PHI_RELU && !favor::bf16_supported(d, m)) return 0;
+  if (phi == FAVOR_PHI_RELU && !fixed_shape(d, m)) return 0;
   if (phi != FAVOR_PHI_RELU && phi != FAVOR_PHI_ELU1) return 0;
   return favor::lin::lin_plan(B, H, n, m, phi, causal).off_end;
 }
@@ -478,7 +491,7 @@ favor_status_t favor_draw_features(unsigned long long seed, unsigned long long s
 extern "C" {
 
 size_t favor_backward_workspace_bytes(int B, int H, int n, int d, int m, int causal) {
-  if (B < 1 || H < 1 || n < 1 || (causal != 0 && causal != 1) || !favor::bf16_supported(d, m)) return 0;
+  if (B < 1 || H < 1 || n < 1 || (causal != 0 && causal != 1) || !fixed_shape(d, m)) return 0;
   return favor::bw::bw_plan(B, H, n, m, causal).off_end;
 }
 
@@ -487,7 +500,7 @@ favor_status_t favor_attention_backward(const void* q, const void* k, const void
                                         int m, int causal, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (causal != 0 && causal != 1)
     return fail(FAVOR_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
-  favor_status_t st = check_bf16(q, k, v, W, dq, B, H, n, d, m);
+  favor_status_t st = check_fixed(q, k, v, W, dq, B, H, n, d, m, "the backward pass");
   if (st != FAVOR_OK) return st;
   const void* more[5] = {y, dy, dk, dv, dq};
   const char* names[5] = {"y", "dy", "dk", "dv", "dq"};

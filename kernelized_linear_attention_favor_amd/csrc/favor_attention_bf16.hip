@@ -34,6 +34,7 @@
 #include "favor_bf16_common.h"
 #include "favor_internal.h"
 #include "favor_mfma.h"
+#include "favor_walk.h"
 
 namespace favor {
 namespace {
@@ -57,6 +58,7 @@ using namespace bf16k;
 // recomputed with c_f and sigma_v from an exact max-only pass.
 // ---------------------------------------------------------------------------
 constexpr int kKBuf = 2;   // staged key/value tiles (double buffering)
+constexpr float kBetaNone = -1.0e30f;   // beta of a feature without keys (finite: it is split into bf16 parts)
 
 template <int NW>
 struct KvSmem {
@@ -76,15 +78,18 @@ struct KvRegs {
 
 // Global -> registers for one tile.  Keys past the end of the range are
 // clamped to the last key (finite data; their weights are masked later).
+// Rows are d bf16 wide (d = 32 or 64); the tile keeps 64 columns, the ones
+// past d zero.
 template <int NW>
 __device__ __forceinline__ void load_kv(KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
-                                        int tile0, int ntok, int tid) {
+                                        int tile0, int ntok, int d, int tid) {
 #pragma unroll
   for (int i = 0; i < KvRegs<NW>::R; ++i) {
     const int c = tid + NW * 64 * i;
     const int tok = min(tile0 + (c >> 3), ntok - 1), ch = c & 7;
-    r.k[i] = *reinterpret_cast<const u32x4*>(Kb + static_cast<size_t>(tok) * kD + ch * 8);
-    r.v[i] = *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(tok) * kD + ch * 8);
+    const bool live = 8 * ch < d;
+    r.k[i] = live ? *reinterpret_cast<const u32x4*>(Kb + static_cast<size_t>(tok) * d + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    r.v[i] = live ? *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(tok) * d + ch * 8) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -250,7 +255,7 @@ __device__ __forceinline__ void kv_tile(KvSmem<NW>& sm, int buf, int tile0, int 
 // ahead of use (one tile of compute does not cover the load latency), staged
 // into the LDS buffer the next tile reads, and computed from LDS.
 template <int NW, int FT, int MODE>
-__device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int ntok,
+__device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int ntok, int d,
                                         KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
                                         const u32x4 augB, KvFeat (&fs)[FT], float vinv, float& vmx,
                                         int tid, int lane) {
@@ -264,7 +269,7 @@ __device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int n
   // issued on every path (past the end it re-reads the clamped last key), so
   // the wait before the next stage can leave the other tile's load in flight.
   if (t + 1 < ntiles) stage_kv<NW>(sm, (t + 1) & 1, r, tid, vinv, vmx);
-  load_kv<NW>(r, Kb, Vb, (t + 3) * kKT, ntok, tid);
+  load_kv<NW>(r, Kb, Vb, (t + 3) * kKT, ntok, d, tid);
   lds_barrier();
 }
 
@@ -274,12 +279,12 @@ __device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int n
 // returns the largest |v| of the range (MAX passes).
 template <int NW, int FT, int MODE, bool FIRST>
 __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb,
-                                         int ntok, const u32x4 augB, KvFeat (&fs)[FT], float& vinv,
+                                         int ntok, int d, const u32x4 augB, KvFeat (&fs)[FT], float& vinv,
                                          float& vmx, int tid, int lane) {
   const int ntiles = (ntok + kKT - 1) / kKT;
   if (ntiles == 0) return;   // uniform over the workgroup
   KvRegs<NW> ra, rb;
-  load_kv<NW>(ra, Kb, Vb, 0, ntok, tid);
+  load_kv<NW>(ra, Kb, Vb, 0, ntok, d, tid);
   if (FIRST) {
     // values are staged as fp16 after scaling by 1 / sigma_v, a power of two
     // above tile 0's largest |v| (a later tile over 2^15 larger overflows
@@ -290,8 +295,8 @@ __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, con
     vinv = inv_pow2_above(block_max<NW>(sm, m0, tid));
   }
   stage_kv<NW>(sm, 0, ra, tid, vinv, vmx);
-  load_kv<NW>(ra, Kb, Vb, kKT, ntok, tid);
-  load_kv<NW>(rb, Kb, Vb, 2 * kKT, ntok, tid);
+  load_kv<NW>(ra, Kb, Vb, kKT, ntok, d, tid);
+  load_kv<NW>(rb, Kb, Vb, 2 * kKT, ntok, d, tid);
   lds_barrier();
   if (FIRST) {
     const int col = lane & 31, half = lane >> 5;
@@ -309,26 +314,28 @@ __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, con
   const int nfull = ntok / kKT;
   int t = 0;
   for (; t + 2 <= nfull; t += 2) {
-    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
-    kv_step<NW, FT, MODE>(sm, t + 1, ntiles, ntok, rb, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
+    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, d, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
+    kv_step<NW, FT, MODE>(sm, t + 1, ntiles, ntok, d, rb, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
   }
   if (t < nfull) {
-    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
+    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, d, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
     ++t;
   }
   if (t < ntiles)
     kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, augB, fs, lane & 31, lane >> 5, lane);
 }
 
-// NW waves of FT 32-feature tiles each cover all m = 32 NW FT features.  The
+// NW waves of FT 32-feature tiles each cover the 32 NW FT features fo ..
+// of a piece (blockIdx.y selects the piece: fo = fo0 + blockIdx.y * 32 NW FT);
+// features at or past m are masked (their range state is written empty).  The
 // library launches FT = 1: with FT = 2 (half the waves, so that two workgroups
 // share a CU) the kernel does not fit its register budget without spills.
 template <int NW, int FT>
 __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void k_kv_state(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
     float* __restrict__ part_S, float* __restrict__ part_zc, float* __restrict__ part_vmax, int H,
-    int n, int splits, int span) {
-  constexpr int M = NW * 32 * FT;
+    int n, int d, int m, int ma, int fo0, int splits, int span) {
+  constexpr int MP = NW * 32 * FT;   // features of the piece
   __shared__ __attribute__((aligned(16))) KvSmem<NW> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -336,19 +343,22 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
   const int bh = blockIdx.x / splits;
   const int split = blockIdx.x - bh * splits;
   const int hh = bh % H;
+  const int fo = fo0 + blockIdx.y * MP;
   const int j0 = split * span;
   const int ntok = max(0, min(n, j0 + span) - j0);
-  const uint16_t* Kb = K + (static_cast<size_t>(bh) * n + j0) * kD;
-  const uint16_t* Vb = V + (static_cast<size_t>(bh) * n + j0) * kD;
+  const uint16_t* Kb = K + (static_cast<size_t>(bh) * n + j0) * d;
+  const uint16_t* Vb = V + (static_cast<size_t>(bh) * n + j0) * d;
 
   KvFeat fs[FT];
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
-    const int f = 32 * (FT * wave + ft) + col;   // B operand column of the projection
+    const int f = fo + 32 * (FT * wave + ft) + col;   // B operand column of the projection
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      fs[ft].wB[kb] = *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD +
-                                                      16 * kb + 8 * half);
+      const bool live = f < m && 16 * kb + 8 * half < d;
+      fs[ft].wB[kb] = live ? *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * m + f) * d +
+                                                             16 * kb + 8 * half)
+                           : u32x4{0u, 0u, 0u, 0u};
       // Keep W resident: an opaque definition stops the compiler from re-loading
       // it inside the key loop (whose vmcnt waits would also stall on the prefetch).
       asm volatile("" : "+v"(fs[ft].wB[kb]));
@@ -366,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
   // pass finds the exact maximum over the range and the range is accumulated
   // again with it.
   float vinv = 1.0f, vmx = 0.f;
-  kv_range<NW, FT, kModeAcc, true>(sm, Kb, Vb, ntok, augB, fs, vinv, vmx, tid, lane);
+  kv_range<NW, FT, kModeAcc, true>(sm, Kb, Vb, ntok, d, augB, fs, vinv, vmx, tid, lane);
   bool bad = false;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
@@ -390,34 +400,38 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
       fs[ft].sacc[1] = f32x16{};
     }
     vmx = 0.f;
-    kv_range<NW, FT, kModeMax, false>(sm, Kb, Vb, ntok, augB, fs, vinv, vmx, tid, lane);
+    kv_range<NW, FT, kModeMax, false>(sm, Kb, Vb, ntok, d, augB, fs, vinv, vmx, tid, lane);
     vinv = inv_pow2_above(block_max<NW>(sm, vmx, tid));
-    kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, augB, fs, vinv, vmx, tid, lane);
+    kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, d, augB, fs, vinv, vmx, tid, lane);
   }
 
-  // write this range's partial state (S back in value units) and its largest |v|
+  // write this range's partial state (S back in value units) and its largest
+  // |v|; masked features (at or past m) are written as an empty state
   const float sig = 1.0f / vinv;
   const size_t base = static_cast<size_t>(bh) * splits + split;
   {
     const float vm = block_max<NW>(sm, vmx, tid);
-    if (tid == 0) part_vmax[base] = vm;
+    if (tid == 0 && blockIdx.y == 0) part_vmax[base] = vm;
   }
-  float* zc = part_zc + base * 2 * M;
-  float* Sb = part_S + base * M * kD;
+  float* zc = part_zc + base * 2 * ma;
+  float* Sb = part_S + base * ma * kD;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
-    const int f0 = 32 * (FT * wave + ft);
-    if (half == 0) zc[M + f0 + col] = fs[ft].c;
+    const int f0 = fo + 32 * (FT * wave + ft);
+    if (half == 0) zc[ma + f0 + col] = f0 + col < m ? fs[ft].c : -kFInf;
     if (col == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) zc[f0 + 8 * (i >> 2) + 4 * half + (i & 3)] = fs[ft].zacc[i];
+      for (int i = 0; i < 16; ++i) {
+        const int fr = f0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        zc[fr] = fr < m ? fs[ft].zacc[i] : 0.f;
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int fr = f0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        Sb[static_cast<size_t>(fr) * kD + 32 * dt + col] = fs[ft].sacc[dt][i] * sig;
+        Sb[static_cast<size_t>(fr) * kD + 32 * dt + col] = fr < m ? fs[ft].sacc[dt][i] * sig : 0.f;
       }
   }
 }
@@ -500,14 +514,16 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_S,
   int ex = 0;   // smallest power of two strictly above vm (1 for all-zero values)
   if (vm > 0.f && vm <= 3.0e38f) frexpf(vm, &ex);
   const float sg = ldexpf(1.0f, ex);
-  const float inv = 1.0f / zt;
+  // a feature no key reaches (masked past the feature count) gets yhat = 0 and
+  // a beta so far below every other that its softmax weight is 0
+  const float inv = zt > 0.f ? 1.0f / zt : 0.f;
   const int pos = kblock_pos(f & 15);
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) {
     const _Float16 hv = static_cast<_Float16>((acc[cc] * inv) / sg);
     ys[4 * cq + cc][pos] = __builtin_bit_cast(uint16_t, hv);
   }
-  if (cq == 0) beta[static_cast<size_t>(bh) * m + f] = (cm + log2f(zt)) * kLn2;
+  if (cq == 0) beta[static_cast<size_t>(bh) * m + f] = zt > 0.f ? (cm + log2f(zt)) * kLn2 : kBetaNone;
   __syncthreads();
   {
     const int c = t >> 2, q = t & 3;   // 4 slots of one column per thread
@@ -560,25 +576,27 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-// k_output: 4 waves; each wave handles 32 queries at a time with all m
-// features.  LDS holds W' = [W | beta parts] (A operand of the projection)
-// and yhat^T (B operand of the output product) for the workgroup's (b, h).
+// k_output: 4 waves; each wave handles 32 queries at a time with all ma
+// features (MT = ma / 32 tiles).  LDS holds W' = [W |
+// beta parts] (A operand of the projection; rows past m zero, their beta far
+// below every other) and yhat^T (B operand of the output product) for the
+// workgroup's (b, h).
 //   proj: D[feature, query] = w_f.q + beta_f           (lane = query column)
 //   M_i  = max_f D;  u = exp2((D - M_i) log2e) -> fp16 (A operand, k = feature)
 //   [num | den] = u [yhat' | 1]                        (fp16 MFMA, fp32 acc)
-//   y = sigma * num / den
+//   y = sigma * num / den                              (the first d columns)
 // ---------------------------------------------------------------------------
-template <int MT>
+template <int MT, int D>
 __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ Q,
                                                    const uint16_t* __restrict__ W,
                                                    const uint16_t* __restrict__ yhat,
                                                    const float* __restrict__ beta,
                                                    const float* __restrict__ sigma,
                                                    float* __restrict__ out, int H, int n,
-                                                   int span) {
-  constexpr int M = 32 * MT;
-  constexpr int YS = M + 8;  // fp16 per staged yhat^T row
-  __shared__ __attribute__((aligned(16))) uint16_t wsh[M * kWStride];
+                                                   int m, int span) {
+  constexpr int mt = MT, ma = 32 * MT, d = D;
+  constexpr int YS = ma + 8;  // fp16 per staged yhat^T row
+  __shared__ __attribute__((aligned(16))) uint16_t wsh[ma * kWStride];
   __shared__ __attribute__((aligned(16))) uint16_t ysh[kD * YS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -591,21 +609,22 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   const int t1 = min(n, t0 + span);
 
   // stage W' and yhat^T
-  for (int c = tid; c < M * 8; c += 256) {
+  for (int c = tid; c < ma * 8; c += 256) {
     const int f = c >> 3, ch = c & 7;
     *reinterpret_cast<u32x4*>(&wsh[f * kWStride + ch * 8]) =
-        *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * M + f) * kD + ch * 8);
+        (f < m && 8 * ch < d) ? *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * m + f) * d + ch * 8)
+                              : u32x4{0u, 0u, 0u, 0u};
   }
-  for (int f = tid; f < M; f += 256) {
+  for (int f = tid; f < ma; f += 256) {
     uint32_t w01, w23;
-    split3_bf16(beta[static_cast<size_t>(bh) * M + f], w01, w23);
+    split3_bf16(beta[static_cast<size_t>(bh) * ma + f], w01, w23);
     *reinterpret_cast<u32x4*>(&wsh[f * kWStride + 64]) = u32x4{w01, w23, 0u, 0u};
     *reinterpret_cast<u32x4*>(&wsh[f * kWStride + 72]) = u32x4{0u, 0u, 0u, 0u};
   }
-  for (int c = tid; c < kD * (M / 8); c += 256) {
-    const int dv = c / (M / 8), ch = c - dv * (M / 8);
+  for (int c = tid; c < kD * (ma / 8); c += 256) {
+    const int dv = c / (ma / 8), ch = c - dv * (ma / 8);
     *reinterpret_cast<u32x4*>(&ysh[dv * YS + ch * 8]) =
-        *reinterpret_cast<const u32x4*>(yhat + (static_cast<size_t>(bh) * kD + dv) * M + ch * 8);
+        *reinterpret_cast<const u32x4*>(yhat + (static_cast<size_t>(bh) * kD + dv) * ma + ch * 8);
   }
   const float sg0 = sigma[static_cast<size_t>(bh) * kD + col];
   const float sg1 = sigma[static_cast<size_t>(bh) * kD + 32 + col];
@@ -614,16 +633,16 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   const u32x4 augB = half == 0 ? u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u}
                                : u32x4{0u, 0u, 0u, 0u};
   const u32x4 onesB = u32x4{kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
-  const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * kD;
-  float* Ob = out + static_cast<size_t>(bh) * n * kD;
+  const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * d;
+  float* Ob = out + static_cast<size_t>(bh) * n * d;
 
   auto load_q = [&](int tb, u32x4 (&qB)[4]) {
     const int qt = tb + col;  // this lane's query (B operand column)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      qB[kb] = (qt < t1) ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * kD +
-                                                            16 * kb + 8 * half)
-                         : u32x4{0u, 0u, 0u, 0u};
+      qB[kb] = (qt < t1 && 16 * kb + 8 * half < d)
+                   ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * d + 16 * kb + 8 * half)
+                   : u32x4{0u, 0u, 0u, 0u};
   };
   u32x4 qB[4], qN[4];
   int tb = t0 + 32 * wave;
@@ -644,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
     float tmax = -kFInf;
     out_accumulate(pa, off, 0, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
 #pragma unroll 1
-    for (int ft = 1; ft < MT; ++ft) {
+    for (int ft = 1; ft < mt; ++ft) {
       const f32x16 pn = out_proj(wsh, ft, col, half, qB, augB);
       out_accumulate(pn, off, ft, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
     }
@@ -652,7 +671,7 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
       // exact row maximum, then redo the tile
       mx = -kFInf;
 #pragma unroll 1
-      for (int ft = 0; ft < MT; ++ft) {
+      for (int ft = 0; ft < mt; ++ft) {
         const f32x16 pa = out_proj(wsh, ft, col, half, qB, augB);
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, pa[i]);
@@ -663,19 +682,20 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
       yacc1 = f32x16{};
       dacc = f32x16{};
 #pragma unroll 1
-      for (int ft = 0; ft < MT; ++ft) {
+      for (int ft = 0; ft < mt; ++ft) {
         const f32x16 pa = out_proj(wsh, ft, col, half, qB, augB);
         out_accumulate(pa, off, ft, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
       }
     }
-    float* orow = Ob + static_cast<size_t>(tb) * kD;
+    float* orow = Ob + static_cast<size_t>(tb) * d;
+    const bool c1 = 32 + col < d;   // the second 32 value columns exist (d = 64)
     if (tb + 32 <= t1) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i >> 2) + 4 * half + (i & 3);
         const float inv = fast_rcp(dacc[i]);
-        __builtin_nontemporal_store(yacc0[i] * sg0 * inv, orow + row * kD + col);
-        __builtin_nontemporal_store(yacc1[i] * sg1 * inv, orow + row * kD + 32 + col);
+        __builtin_nontemporal_store(yacc0[i] * sg0 * inv, orow + row * d + col);
+        if (c1) __builtin_nontemporal_store(yacc1[i] * sg1 * inv, orow + row * d + 32 + col);
       }
     } else {
 #pragma unroll
@@ -683,8 +703,8 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
         const int row = 8 * (i >> 2) + 4 * half + (i & 3);
         if (tb + row < t1) {
           const float inv = fast_rcp(dacc[i]);
-          orow[row * kD + col] = yacc0[i] * sg0 * inv;
-          orow[row * kD + 32 + col] = yacc1[i] * sg1 * inv;
+          orow[row * d + col] = yacc0[i] * sg0 * inv;
+          if (c1) orow[row * d + 32 + col] = yacc1[i] * sg1 * inv;
         }
       }
     }
@@ -693,69 +713,148 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   }
 }
 
-template <int NW, int FT>
-hipError_t launch_kv(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W,
-                     float* pS, float* pzc, float* pvm, hipStream_t s) {
-  // the causal path runs the same kernel over its segments; it is timed under its own name
-  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, FT>),
-               dim3(p.B * p.H * p.splits), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, p.H, p.n,
-               p.splits, p.span);
-  return hipGetLastError();
+// ---------------------------------------------------------------------------
+// k_slice_combine: the causal walk's feature slices, combined per query in
+// slice order: y = sum_s 2^(L_s - L) num_s / sum_s 2^(L_s - L) den_s, L = max_s
+// L_s (each slice's numerator is its share of phi(q)^T S_i over its features,
+// in value units, at the log2 scale L_s).  One thread per (query, 4 columns).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_slice_combine(const float* __restrict__ pnum,
+                                                       const float* __restrict__ pdl, float* __restrict__ out,
+                                                       long long rows, int d, int nslices) {
+  const long long g = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int cg = d >> 2;
+  const long long row = g / cg;
+  const int c4 = static_cast<int>(g - row * cg);
+  if (row >= rows) return;
+  float L = -kFInf;
+  for (int s = 0; s < nslices; ++s) L = fmaxf(L, pdl[(s * rows + row) * 2 + 1]);
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nslices; ++s) {
+    const long long r = s * rows + row;
+    const f32x2 dl = *reinterpret_cast<const f32x2*>(pdl + r * 2);
+    const float wt = dl[1] == -kFInf ? 0.f : exp2f(dl[1] - L);
+    den = fmaf(wt, dl[0], den);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(pnum + r * kD + 4 * c4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) num[j] = fmaf(wt, x[j], num[j]);
+  }
+  const float inv = 1.0f / den;
+  *reinterpret_cast<f32x4*>(out + row * d + 4 * c4) = num * inv;
 }
 
-template <int MT>
-hipError_t launch_out(const Bf16Plan& p, const uint16_t* q, const uint16_t* W, const uint16_t* yh,
-                      const float* beta, const float* sigma, float* out, int span,
-                      hipStream_t s) {
-  const int nblk = (p.n + span - 1) / span;
-  FAVOR_LAUNCH("k_output", k_output<MT>, dim3(p.B * p.H * nblk), dim3(256), 0, s, q, W, yh, beta, sigma,
-                     out, p.H, p.n, span);
+template <int NW>
+hipError_t launch_kv_piece(const Bf16Plan& p, int fo0, int pieces, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* W, float* pS, float* pzc, float* pvm, hipStream_t s) {
+  // the causal path runs the same kernel over its segments; it is timed under its own name
+  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, 1>),
+               dim3(p.B * p.H * p.splits, pieces), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, p.H, p.n, p.d,
+               p.m, p.ma, fo0, p.splits, p.span);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool bf16_supported(int d, int m) { return d == kD && (m == 64 || m == 128 || m == 256); }
+bool bf16_supported(int d, int m) {
+  return (d == 32 || d == kD) && m >= 16 && m <= kMaxFeatures && m % 16 == 0;
+}
 
-Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal) {
+bool chunk_supported(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128; }
+
+bool causal_chunks_shape(const Bf16Plan& p) {
+  return p.causal && p.d == kD && p.chunk == 64 && (p.m == 64 || p.m == 128 || p.m == 256);
+}
+
+Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal, int chunk) {
   Bf16Plan p{};
   p.B = B;
   p.H = H;
   p.n = n;
   p.d = d;
   p.m = m;
+  p.ma = (m + 31) / 32 * 32;
   p.causal = causal;
+  p.chunk = chunk;
   const long long BH = static_cast<long long>(B) * H;
+  const int tiles = p.ma / 32;
+  // causal: feature slices of at most 256 features (128 with chunks of 128),
+  // in at most two groups of equal width
+  p.nslices = 1;
+  p.ngroups = 1;
+  p.groups[0] = SliceGroup{0, 1, tiles, 0};
+  if (causal) {
+    const int maxw = (chunk == 128 ? 128 : 256) / 32;
+    const int ns = (tiles + maxw - 1) / maxw;
+    const int base = tiles / ns, extra = tiles % ns;
+    p.nslices = ns;
+    if (extra == 0) {
+      p.groups[0] = SliceGroup{0, ns, base, 0};
+    } else {
+      p.ngroups = 2;
+      p.groups[0] = SliceGroup{0, extra, base + 1, 0};
+      p.groups[1] = SliceGroup{extra, ns - extra, base, extra * (base + 1) * 32};
+    }
+  }
   const long long max_splits = (n + kKT - 1) / kKT;
   long long splits;
   if (causal) {
-    // one chunk-walking workgroup per CU: segments per (b, h)
-    splits = (256 + BH - 1) / BH;
+    // one chunk-walking workgroup per CU: segments per (b, h) and slice
+    splits = (256 + BH * p.nslices - 1) / (BH * p.nslices);
   } else {
-    // about 2048 state waves (8 per CU); a workgroup has m/32 waves
-    const long long wgs = 2048 / (m / 32);
+    // about 2048 state waves (8 per CU); a range has ma/32 waves over its pieces
+    const long long wgs = 2048 / tiles;
     splits = (wgs + BH - 1) / BH;
   }
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
-  const long long span = align_up((n + splits - 1) / splits, kKT);
+  const int al = causal && chunk > kKT ? chunk : kKT;
+  const long long span = align_up((n + splits - 1) / splits, al);
   p.span = static_cast<int>(span);
   p.splits = static_cast<int>((n + span - 1) / span);
+  const size_t ma = p.ma;
   size_t o = 0;
   p.off_part_S = o;
-  o = align_up(o + sizeof(float) * BH * p.splits * m * kD, 256);
+  o = align_up(o + sizeof(float) * BH * p.splits * ma * kD, 256);
   p.off_part_zc = o;
-  o = align_up(o + sizeof(float) * BH * p.splits * 2 * m, 256);
+  o = align_up(o + sizeof(float) * BH * p.splits * 2 * ma, 256);
   p.off_vmax = o;
   o = align_up(o + sizeof(float) * BH * p.splits, 256);
+  const size_t nc = causal ? 0 : 1;   // buffers of the non-causal merge and output
   p.off_yhat = o;
-  o = align_up(o + sizeof(uint16_t) * BH * kD * m, 256);
+  o = align_up(o + nc * sizeof(uint16_t) * BH * kD * ma, 256);
   p.off_beta = o;
-  o = align_up(o + sizeof(float) * BH * m, 256);
+  o = align_up(o + nc * sizeof(float) * BH * ma, 256);
   p.off_sigma = o;
-  o = align_up(o + sizeof(float) * BH * kD, 256);
+  o = align_up(o + nc * sizeof(float) * BH * kD, 256);
+  const size_t ms = (causal && p.nslices > 1) ? p.nslices : 0;   // slice partials of the causal walk
+  p.off_pnum = o;
+  o = align_up(o + ms * sizeof(float) * BH * n * kD, 256);
+  p.off_pdl = o;
+  o = align_up(o + ms * sizeof(float) * BH * n * 2, 256);
   p.off_end = o;
   return p;
+}
+
+hipError_t launch_kv_all(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W, float* pS,
+                         float* pzc, float* pvm, hipStream_t s) {
+  // the ma / 32 feature tiles as pieces of 8, 4, 2 and 1 tiles (one wave per tile)
+  int rem = p.ma / 32, fo = 0;
+  for (int nw = 8; nw >= 1; nw >>= 1) {
+    const int cnt = rem / nw;
+    if (cnt == 0) continue;
+    hipError_t e = hipSuccess;
+    switch (nw) {
+      case 8: e = launch_kv_piece<8>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 4: e = launch_kv_piece<4>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 2: e = launch_kv_piece<2>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 1: e = launch_kv_piece<1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+    }
+    if (e != hipSuccess) return e;
+    fo += cnt * nw * 32;
+    rem -= cnt * nw;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_state_bf16(const Bf16Plan& p, const uint16_t* k, const uint16_t* v,
@@ -764,18 +863,64 @@ hipError_t launch_state_bf16(const Bf16Plan& p, const uint16_t* k, const uint16_
   float* pS = reinterpret_cast<float*>(base + p.off_part_S);
   float* pzc = reinterpret_cast<float*>(base + p.off_part_zc);
   float* pvm = reinterpret_cast<float*>(base + p.off_vmax);
-  hipError_t e = hipSuccess;
-  switch (p.m) {
-    case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-    case 128: e = launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-    case 256: e = launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipError_t e = launch_kv_all(p, k, v, W, pS, pzc, pvm, s);
   if (e != hipSuccess) return e;
-  FAVOR_LAUNCH("k_state_merge", k_state_merge, dim3(p.B * p.H * (p.m / 16)), dim3(256), 0, s, pS, pzc,
-               state, p.B * p.H, p.m, p.splits);
+  FAVOR_LAUNCH("k_state_merge", k_state_merge, dim3(p.B * p.H * (p.ma / 16)), dim3(256), 0, s, pS, pzc,
+               state, p.B * p.H, p.ma, p.splits);
   return hipGetLastError();
 }
+
+namespace walk {
+
+hipError_t launch_causal(const Bf16Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* W, const float* part_S, const float* part_zc, const float* vmax,
+                         float* out, float* pnum, float* pdl, hipStream_t s) {
+  Args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.W = W;
+  a.part_S = part_S;
+  a.part_zc = part_zc;
+  a.seg_vmax = vmax;
+  a.out = out;
+  a.pnum = pnum;
+  a.pdl = pdl;
+  a.BH = p.B * p.H;
+  a.H = p.H;
+  a.n = p.n;
+  a.d = p.d;
+  a.m = p.m;
+  a.malloc_ = p.ma;
+  a.nseg = p.splits;
+  a.seglen = p.span;
+  a.has_carry = p.splits > 1 ? 1 : 0;
+  a.nslices = p.nslices;
+  for (int g = 0; g < p.ngroups; ++g) {
+    const SliceGroup& gr = p.groups[g];
+    a.fbase = gr.fbase;
+    a.slice0 = gr.first_slice;
+    a.ms = 32 * gr.nw;
+    hipError_t e = hipErrorInvalidValue;
+    switch (p.chunk) {
+      case 16: e = launch_walk_c16(a, gr.nw, gr.nslices, s); break;
+      case 32: e = launch_walk_c32(a, gr.nw, gr.nslices, s); break;
+      case 64: e = launch_walk_c64(a, gr.nw, gr.nslices, s); break;
+      case 128: e = launch_walk_c128(a, gr.nw, gr.nslices, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  if (p.nslices > 1) {
+    const long long rows = static_cast<long long>(p.B) * p.H * p.n;
+    const long long threads = rows * (p.d / 4);
+    FAVOR_LAUNCH("k_slice_combine", k_slice_combine, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
+                 0, s, pnum, pdl, out, rows, p.d, p.nslices);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace walk
 
 hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                                  const uint16_t* v, const uint16_t* W, float* out, void* ws,
@@ -789,31 +934,42 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   float* sigma = reinterpret_cast<float*>(base + p.off_sigma);
   hipError_t e = hipSuccess;
   if (!p.causal || p.splits > 1) {
-    switch (p.m) {
-      case 64: e = launch_kv<2, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-      case 128: e = launch_kv<4, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-      case 256: e = launch_kv<8, 1>(p, k, v, W, pS, pzc, pvm, s); break;
-      default: return hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) return e;
+    if ((e = launch_kv_all(p, k, v, W, pS, pzc, pvm, s)) != hipSuccess) return e;
   }
   if (p.causal) {
-    return launch_causal_chunks(p, q, k, v, W, pS, pzc, p.splits > 1 ? pvm : nullptr, out, s);
+    if (causal_chunks_shape(p))
+      return launch_causal_chunks(p, q, k, v, W, pS, pzc, p.splits > 1 ? pvm : nullptr, out, s);
+    return walk::launch_causal(p, q, k, v, W, pS, pzc, p.splits > 1 ? pvm : nullptr, out,
+                               reinterpret_cast<float*>(base + p.off_pnum),
+                               reinterpret_cast<float*>(base + p.off_pdl), s);
   }
-  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * (p.m / 16)), dim3(256), 0, s, pS, pzc, pvm, yh,
-               beta, sigma, p.m, p.splits);
+  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * (p.ma / 16)), dim3(256), 0, s, pS, pzc, pvm, yh,
+               beta, sigma, p.ma, p.splits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // output: about 512 workgroups, each a contiguous run of query tiles
   const long long BH = static_cast<long long>(p.B) * p.H;
   long long per = (512 + BH - 1) / BH;
   long long span = (p.n + per - 1) / per;
   span = align_up(span < 128 ? 128 : span, 128);
-  switch (p.m) {
-    case 64: return launch_out<2>(p, q, W, yh, beta, sigma, out, static_cast<int>(span), s);
-    case 128: return launch_out<4>(p, q, W, yh, beta, sigma, out, static_cast<int>(span), s);
-    case 256: return launch_out<8>(p, q, W, yh, beta, sigma, out, static_cast<int>(span), s);
+  const int nblk = static_cast<int>((p.n + span - 1) / span);
+#define FAVOR_OUT_CASE(MTV)                                                                                    \
+  case MTV:                                                                                                  \
+    if (p.d == 64)                                                                                           \
+      FAVOR_LAUNCH("k_output", (k_output<MTV, 64>), dim3(p.B * p.H * nblk), dim3(256), 0, s, q, W, yh, beta,  \
+                   sigma, out, p.H, p.n, p.m, static_cast<int>(span));                                       \
+    else                                                                                                     \
+      FAVOR_LAUNCH("k_output", (k_output<MTV, 32>), dim3(p.B * p.H * nblk), dim3(256), 0, s, q, W, yh, beta,  \
+                   sigma, out, p.H, p.n, p.m, static_cast<int>(span));                                       \
+    break;
+  switch (p.ma / 32) {
+    FAVOR_OUT_CASE(1) FAVOR_OUT_CASE(2) FAVOR_OUT_CASE(3) FAVOR_OUT_CASE(4)
+    FAVOR_OUT_CASE(5) FAVOR_OUT_CASE(6) FAVOR_OUT_CASE(7) FAVOR_OUT_CASE(8)
+    FAVOR_OUT_CASE(9) FAVOR_OUT_CASE(10) FAVOR_OUT_CASE(11) FAVOR_OUT_CASE(12)
+    FAVOR_OUT_CASE(13) FAVOR_OUT_CASE(14) FAVOR_OUT_CASE(15) FAVOR_OUT_CASE(16)
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+#undef FAVOR_OUT_CASE
+  return hipGetLastError();
 }
 
 }  // namespace favor

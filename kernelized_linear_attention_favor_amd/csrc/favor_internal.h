@@ -42,23 +42,55 @@ hipError_t launch_attention_causal_f32(const float* q, const float* k, const flo
                                        int m, hipStream_t s);
 
 // ---------------------------------------------------------------- bf16 path
+// Shapes: d in {32, 64}; m a multiple of 16 up to 512 (features are handled in
+// 32-feature tiles, m rounded up to ma = 32 ceil(m / 32), the tail masked);
+// causal chunk in {16, 32, 64, 128}.
+constexpr int kMaxFeatures = 512;
+constexpr int kDefaultChunk = 64;
+bool bf16_supported(int d, int m);
+bool chunk_supported(int chunk);
+
+// A group of feature slices of equal width launched together (the causal walk).
+struct SliceGroup {
+  int first_slice, nslices, nw, fbase;   // nw waves (32 features each) per slice
+};
+
 struct Bf16Plan {
-  int B, H, n, d, m;
-  int causal;
+  int B, H, n, d, m, ma;   // ma: m rounded up to a multiple of 32 (state rows per range)
+  int causal, chunk;
   int splits;     // key ranges per (b,h): state splits (non-causal) or segments (causal)
   int span;       // tokens per split / segment (multiple of 64)
+  int nslices;    // causal: feature slices (1 unless m exceeds one walk's width)
+  int ngroups;    // causal: launch groups of slices (1 or 2)
+  SliceGroup groups[2];
   // workspace carve-up (byte offsets)
-  size_t off_part_S, off_part_zc, off_vmax, off_yhat, off_beta, off_sigma, off_end;
+  size_t off_part_S, off_part_zc, off_vmax, off_yhat, off_beta, off_sigma, off_pnum, off_pdl, off_end;
 };
-bool bf16_supported(int d, int m);
-Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal);
+Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal, int chunk = kDefaultChunk);
+hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const uint16_t* W, float* out, void* ws,
+                                 hipStream_t s);
+// The causal chunk walk specialised for d = 64, m in {64, 128, 256} and chunks
+// of 64 (k_causal_chunks); other shapes take the general walk (walk::).
+bool causal_chunks_shape(const Bf16Plan& p);
 hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const uint16_t* W, const float* part_S,
                                 const float* part_zc, const float* vmax, float* out,
                                 hipStream_t s);
-hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
-                                 const uint16_t* v, const uint16_t* W, float* out, void* ws,
-                                 hipStream_t s);
+// The state pass (k_kv_state) over the plan's key ranges for every feature.
+hipError_t launch_kv_all(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W, float* pS,
+                         float* pzc, float* pvm, hipStream_t s);
+
+namespace walk {
+struct Args;
+hipError_t launch_walk_c16(const Args& a, int nw, int nsl, hipStream_t s);
+hipError_t launch_walk_c32(const Args& a, int nw, int nsl, hipStream_t s);
+hipError_t launch_walk_c64(const Args& a, int nw, int nsl, hipStream_t s);
+hipError_t launch_walk_c128(const Args& a, int nw, int nsl, hipStream_t s);
+hipError_t launch_causal(const Bf16Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* W, const float* part_S, const float* part_zc, const float* vmax,
+                         float* out, float* pnum, float* pdl, hipStream_t s);
+}  // namespace walk
 
 // ---------------------------------------------------------------- decode
 // State of the keys of a non-causal plan's ranges, merged (k_kv_state + k_state_merge).

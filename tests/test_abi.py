@@ -72,8 +72,16 @@ def test_workspace_bytes_host_only():
     L = _lib()
     assert L.favor_workspace_bytes(4, 8, 16384, 64, 256, 0) > 0
     assert L.favor_workspace_bytes(4, 8, 16384, 64, 256, 1) > 0
-    assert L.favor_workspace_bytes(4, 8, 16384, 32, 256, 0) == 0   # d unsupported
-    assert L.favor_workspace_bytes(4, 8, 16384, 64, 100, 0) == 0   # m unsupported
+    # the bf16 path: d in {32, 64}, every m in 16Z from 16 to 512
+    for d in (32, 64):
+        for m in range(16, 513, 16):
+            for causal in (0, 1):
+                assert L.favor_workspace_bytes(2, 3, 1000, d, m, causal) > 0, (d, m, causal)
+    assert L.favor_workspace_bytes(4, 8, 16384, 48, 256, 0) == 0   # d unsupported
+    assert L.favor_workspace_bytes(4, 8, 16384, 128, 256, 0) == 0  # d unsupported
+    assert L.favor_workspace_bytes(4, 8, 16384, 64, 100, 0) == 0   # m not a multiple of 16
+    assert L.favor_workspace_bytes(4, 8, 16384, 64, 8, 0) == 0     # m below 16
+    assert L.favor_workspace_bytes(4, 8, 16384, 64, 528, 0) == 0   # m above 512
     assert L.favor_workspace_bytes(0, 8, 16384, 64, 256, 0) == 0
     assert L.favor_workspace_bytes(1, 1, 16, 64, 64, 2) == 0
 
@@ -88,7 +96,9 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails v
     ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, -3, 64, 64, 0), 1),     # n < 0
     ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 64, 2), 1),     # causal flag
     ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 48, 64, 0), 2),     # d unsupported
-    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 96, 0), 2),     # m unsupported
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 16, 64, 0), 2),     # d unsupported
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 100, 0), 2),    # m not a multiple of 16
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 528, 0), 2),    # m above 512
     ((FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 64, 0), 2),  # misaligned
 ])
 def test_attention_rejects_bad_arguments(args, status):
@@ -101,8 +111,10 @@ def test_attention_rejects_bad_arguments(args, status):
 def test_causal_chunk_and_f32_limits():
     L = _lib()
     base = (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 64)
-    assert L.favor_attention_causal(*base, 32, None) == 2
+    for bad in (8, 24, 48, 96, 256):
+        assert L.favor_attention_causal(*base, bad, None) == 2, bad   # chunk not in {16, 32, 64, 128}
     assert L.favor_attention_causal(*base, -1, None) == 1
+    assert L.favor_attention_causal(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 100, 32, None) == 2
     assert L.favor_attention_f32(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 256, 64, 0, None) == 2
     assert L.favor_attention_f32(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 1024, 0, None) == 2
     assert L.favor_feature_map(0, FAKE, FAKE, 1, 1, 16, 64, 64, None) == 1
@@ -189,6 +201,7 @@ def test_backward_host_only():
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 256, 0) > 0
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 100, 0) == 0
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 32, 64, 0) == 0
+    assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 96, 0) == 0   # its own fixed shape set
     # the causal pass keeps both partial states (no merged tiles)
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 256, 1) > 0
     assert L.favor_backward_workspace_bytes(4, 8, 16384, 64, 256, 2) == 0
