@@ -134,6 +134,24 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * favor_attention_noalloc -- favor_attention (same arguments, same kernels,
+ * bitwise the same output) for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It calls no allocator.  Its scratch is one fixed array of 64 MiB
+ * (67108864 bytes) per GPU, a static device array of the library that each GPU
+ * it runs on holds until the process ends; a shape whose scratch
+ * (favor_workspace_bytes) exceeds it returns FAVOR_ERR_UNSUPPORTED and launches
+ * nothing.  No part of the array needs to start at zero (every call writes each
+ * scratch word before reading it).  All calls on one GPU share that GPU's array:
+ * calls that overlap in time on one GPU (different streams, or threads without
+ * ordering) race and give undefined results; calls ordered on one stream are
+ * safe.
+ */
+favor_status_t favor_attention_noalloc(const void* q, const void* k, const void* v, const void* W,
+                                       float* out, int B, int H, int n, int d, int m, int causal,
+                                       hipStream_t stream);
+
+/*
  * Deterministic feature maps on the same state / output / causal structure
  * (Performer for vision, What Is Performer? and Kernel Choices: ReLU features of
  * the random projections; quiz page on linear attention variants, comparison

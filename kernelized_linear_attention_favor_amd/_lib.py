@@ -43,6 +43,7 @@ SIGNATURES = {
     "favor_attention_causal_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "favor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "favor_attention_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "favor_attention_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "favor_workspace_bytes_phi": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "favor_attention_phi": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "favor_draw_features": (_i, [ctypes.c_ulonglong, ctypes.c_ulonglong, _vp, _i, _i, _i, _i, _vp]),
@@ -133,6 +134,10 @@ def favor_workspace_bytes(B, H, n, d, m, causal) -> int:
 
 def favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream) -> int:
     return lib().favor_attention_ws(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream)
+
+
+def favor_attention_noalloc(q, k, v, W, out, B, H, n, d, m, causal, stream) -> int:
+    return lib().favor_attention_noalloc(q, k, v, W, out, B, H, n, d, m, causal, stream)
 
 
 def favor_workspace_bytes_phi(B, H, n, d, m, causal, phi) -> int:

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "favor_internal.h"
@@ -201,6 +202,42 @@ favor_status_t check_phi(const void* q, const void* k, const void* v, const void
   return FAVOR_OK;
 }
 
+// Fixed scratch for favor_attention_noalloc: one array per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory; the device address of each GPU's copy comes from hipGetSymbolAddress
+// (taken once per device, with that device current) and only that address is
+// ever handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array (nullptr on failure, with
+// the HIP error in *err).
+void* scratch_for_current_device(hipError_t* err, int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  *dev_out = dev;
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&sl] {
+    void* p = nullptr;
+    sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (sl.err == hipSuccess) sl.ptr = p;
+  });
+  *err = sl.err;
+  return sl.err == hipSuccess ? sl.ptr : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -334,6 +371,29 @@ favor_status_t favor_attention_ws(const void* q, const void* k, const void* v, c
   if (st != FAVOR_OK) return st;
   if (!ws) return fail(FAVOR_ERR_INVALID_ARGUMENT, "ws is null");
   return run_bf16(q, k, v, W, out, B, H, n, d, m, causal, ws, ws_bytes, stream);
+}
+
+favor_status_t favor_attention_noalloc(const void* q, const void* k, const void* v, const void* W, float* out,
+                                       int B, int H, int n, int d, int m, int causal, hipStream_t stream) {
+  if (causal != 0 && causal != 1)
+    return fail(FAVOR_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  favor_status_t st = check_bf16(q, k, v, W, out, B, H, n, d, m);
+  if (st != FAVOR_OK) return st;
+  const favor::Bf16Plan plan = favor::bf16_plan(B, H, n, d, m, causal);
+  if (plan.off_end > kNoAllocScratchBytes)
+    return fail(FAVOR_ERR_UNSUPPORTED,
+                "favor_attention_noalloc: this shape needs %zu bytes of scratch, above the fixed %zu-byte "
+                "array (use favor_attention_ws with a caller-owned workspace)",
+                plan.off_end, kNoAllocScratchBytes);
+  hipError_t e = hipSuccess;
+  int dev = -1;
+  void* ws = scratch_for_current_device(&e, &dev);
+  if (!ws) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  e = favor::launch_attention_bf16(plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                   static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(W), out, ws,
+                                   stream);
+  if (e != hipSuccess) return hip_fail(e, "bf16 attention launch");
+  return ok();
 }
 
 size_t favor_state_bytes(int B, int H, int d, int m) {
