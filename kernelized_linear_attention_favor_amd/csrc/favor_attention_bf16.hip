@@ -21,12 +21,13 @@
 // the measured workloads, against a 2e-3 budget):
 //   * key features exp(e - c) are rounded to fp16 (11 significant bits) for
 //     the S = Phi(K)^T V MFMA, with V scaled by a power of two into fp16 range
-//     (exact for bf16 values); z sums the same rounded features, so each
-//     yhat_f = S_f / z_f is an exact weighted average of the values.
-//   * query softmax weights are in (0, 1] and go to fp16; yhat is scaled by
-//     one power of two per (b, h) into (-1, 1) and goes to fp16; the denominator is
-//     the same fp16 weights times 1.0, so rounding of a weight moves numerator
-//     and denominator together.
+//     (exact for bf16 values); z sums the same rounded features (fp32, v_dot2),
+//     so each yhat_f = S_f / z_f is an exact weighted average of the values.
+//   * query softmax weights (at most 2^16, the shift being the first feature
+//     tile's row maximum) go to fp16; yhat is scaled by one power of two per
+//     (b, h) into (-1, 1) and goes to fp16; the denominator sums the same fp16
+//     weights in fp32, so rounding of a weight moves numerator and
+//     denominator together.
 //   * projections w.x (+ the -|k|^2/2 or beta term, carried as three bf16
 //     parts in an extra k-block) accumulate in fp32.
 #include <math.h>
@@ -42,29 +43,38 @@ namespace {
 using namespace bf16k;
 
 // ---------------------------------------------------------------------------
-// k_kv_state: one workgroup = NW waves of FT 32-feature tiles (all m features)
-// of one (b, h) over one contiguous key range.
+// k_kv_state: one workgroup = NW waves, one 32-feature tile per wave, of one
+// (b, h) over one contiguous key range.
 //
-// Per 32-key tile and feature tile:
+// Per 32-key block and feature tile:
 //   proj (32x32 MFMA, k = 64 d + 1 aug block) -> D[key, feature] =
 //        w_f.k_j - |k_j|^2/2                    (lane = feature column)
 //   phi  = exp2(D log2e - c_f) -> fp16           (c_f: per feature, the first
 //                                                 tile's maximum + 8)
 //   S_f += phi^T (V / sigma_v)                   (fp16 MFMA; output registers
 //                                                 reused as the A operand)
-//   z_f += phi                                   (same rounded values)
+//   z_f += phi                                   (the same rounded values,
+//                                                 summed in fp32 by v_dot2)
+// A staged 64-key tile is two blocks, software-pipelined inside the wave: the
+// projection of block 1 has no dependence on block 0's exponentials, nor
+// block 0's S MFMAs on block 1's, so the matrix and vector pipes of one wave
+// can work side by side instead of in turn.
 // sigma_v is a power of two above the first tile's largest |v|.  If anything
 // overflowed (a later key or value far above the first tile's), the range is
 // recomputed with c_f and sigma_v from an exact max-only pass.
 // ---------------------------------------------------------------------------
 constexpr int kKBuf = 2;   // staged key/value tiles (double buffering)
 constexpr float kBetaNone = -1.0e30f;   // beta of a feature without keys (finite: it is split into bf16 parts)
+// Per staged tile: two words per key (bf16 parts of -|k|^2/2), then one sink
+// word per lane for the lanes that hold no key's norm, so that staging has no
+// branch.
+constexpr int kAugWords = 2 * kKT + 64;
 
 template <int NW>
 struct KvSmem {
   uint16_t k[kKBuf][kKT * kD];     // keys, bf16
   uint16_t v[kKBuf][kKT * kD];     // values / sigma_v, fp16
-  uint32_t aug[kKBuf][kKT * 2];   // per key: bf16 parts of -|k|^2/2, packed (p0 | p1 << 16, p2)
+  uint32_t aug[kKBuf][kAugWords];  // per key: (p0 | p1 << 16, p2), the bf16 parts of -|k|^2/2
   float vred[NW];
   int flag;
 };
@@ -78,8 +88,10 @@ struct KvRegs {
 
 // Global -> registers for one tile.  Keys past the end of the range are
 // clamped to the last key (finite data; their weights are masked later).
-// Rows are d bf16 wide (d = 32 or 64); the tile keeps 64 columns, the ones
-// past d zero.
+// Rows are d bf16 wide (d = 32 or 64); the tile keeps 64 columns.  The
+// chunks past d re-read the row's first chunk and are zeroed when staged:
+// no load is predicated and nothing reads the registers before the stage, so
+// the loads stay in flight for the whole step in between.
 template <int NW>
 __device__ __forceinline__ void load_kv(KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
                                         int tile0, int ntok, int d, int tid) {
@@ -87,9 +99,9 @@ __device__ __forceinline__ void load_kv(KvRegs<NW>& r, const uint16_t* Kb, const
   for (int i = 0; i < KvRegs<NW>::R; ++i) {
     const int c = tid + NW * 64 * i;
     const int tok = min(tile0 + (c >> 3), ntok - 1), ch = c & 7;
-    const bool live = 8 * ch < d;
-    r.k[i] = live ? *reinterpret_cast<const u32x4*>(Kb + static_cast<size_t>(tok) * d + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-    r.v[i] = live ? *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(tok) * d + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    const size_t o = static_cast<size_t>(tok) * d + (8 * ch < d ? ch * 8 : 0);
+    r.k[i] = *reinterpret_cast<const u32x4*>(Kb + o);
+    r.v[i] = *reinterpret_cast<const u32x4*>(Vb + o);
   }
 }
 
@@ -104,35 +116,38 @@ __device__ __forceinline__ float chunk_absmax(const u32x4& c) {
 
 // Registers -> swizzled LDS tile: keys as given (bf16), values times vinv (a
 // power of two) as fp16, plus -|k|^2/2 of each key as three bf16 parts (the 8
-// threads holding a key's 8 chunks are adjacent lanes).  vmx tracks the
-// largest |v| staged.
+// threads holding a key's 8 chunks are adjacent lanes; the first two store
+// the key's two words, the others their sink word).  vmx tracks the largest
+// |v| staged.
 template <int NW>
-__device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<NW>& r, int tid,
+__device__ __forceinline__ void stage_kv(KvSmem<NW>& sm, int buf, const KvRegs<NW>& r, int tid, int d,
                                          float vinv, float& vmx) {
 #pragma unroll
   for (int i = 0; i < KvRegs<NW>::R; ++i) {
     const int c = tid + NW * 64 * i;
     const int key = c >> 3, ch = c & 7;
-    *reinterpret_cast<u32x4*>(&sm.k[buf][swz(key, ch)]) = r.k[i];
+    const bool live = 8 * ch < d;   // columns past d are zero
+    const u32x4 kx = live ? r.k[i] : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 vx = live ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&sm.k[buf][swz(key, ch)]) = kx;
     u32x4 vh;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      vh[w] = pack_f16(bf16_lo_as_f32(r.v[i][w]) * vinv, bf16_hi_as_f32(r.v[i][w]) * vinv);
+      vh[w] = pack_f16(bf16_lo_as_f32(vx[w]) * vinv, bf16_hi_as_f32(vx[w]) * vinv);
     *reinterpret_cast<u32x4*>(&sm.v[buf][swz(key, ch)]) = vh;
-    vmx = fmaxf(vmx, chunk_absmax(r.v[i]));
+    vmx = fmaxf(vmx, chunk_absmax(vx));
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float a = bf16_lo_as_f32(r.k[i][w]), b = bf16_hi_as_f32(r.k[i][w]);
+      const float a = bf16_lo_as_f32(kx[w]), b = bf16_hi_as_f32(kx[w]);
       s = fmaf(a, a, s);
       s = fmaf(b, b, s);
     }
     s = sum8(s);
-    if (ch == 0) {
-      uint32_t w01, w23;
-      split3_bf16(-0.5f * s, w01, w23);
-      *reinterpret_cast<u32x2*>(&sm.aug[buf][2 * key]) = u32x2{w01, w23};
-    }
+    uint32_t w01, w23;
+    split3_bf16(-0.5f * s, w01, w23);
+    const int slot = ch < 2 ? 2 * key + ch : 2 * kKT + (tid & 63);
+    sm.aug[buf][slot] = ch == 0 ? w01 : w23;
   }
 }
 
@@ -157,53 +172,82 @@ __device__ __forceinline__ float inv_pow2_above(float m) {
 }
 
 // Per-wave state of one 32-feature tile: W operand (B, lane = feature), the
-// shift c_f, the running z_f and S_f (D layout, rows = features).
+// shift c_f, the running S_f (D layout, rows = features) and this lane's
+// share of z_f (the keys of its half of every block; the two lanes of a
+// feature column are added at the end).
 struct KvFeat {
   u32x4 wB[4];
   float c;
   f32x16 sacc[2];
-  f32x16 zacc;   // z_f in every column of D-layout row f
+  float z;
 };
 
-// Projection of 32 keys (rows row0 .. row0+31 of a staged tile) on one
-// 32-feature tile: D[key, feature] = w_f.k_j - |k_j|^2/2 (lane = feature column).
-template <int NW>
-__device__ __forceinline__ f32x16 kv_proj(const KvSmem<NW>& sm, int buf, int row0, int col, int half,
-                                          const u32x4 (&wB)[4], const u32x4 augB) {
-  const int row = row0 + col;
+// Lane offsets (bf16 elements from a staged tile's start) of the MFMA
+// operands for the first rows; rows 16 apart share the swizzle pattern, so
+// every other 16-row group is a constant offset away and the per-tile
+// addresses reduce to immediates.
+struct KvAddr {
+  int k[4];   // projection A operand: key row `col`, chunk 2 kb + half
+  int v[4];   // value B operand [2 dt + j]: key slots 8 j + 4 half + (0..3)
+};
+
+__device__ __forceinline__ KvAddr kv_addr(int lane) {
+  KvAddr a;
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) a.k[kb] = swz(col, 2 * kb + half);
+  // ds_read_tr16_b64 layout (as v_operand): lane 4v+q of each 16-lane group
+  // supplies 4 consecutive columns of key slot v
+  const int g = lane >> 4, v = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    const int chunk = 4 * dt + 2 * (g & 1) + (q >> 1);
+    a.v[2 * dt] = swz(4 * half + v, chunk) + 4 * (q & 1);
+    a.v[2 * dt + 1] = swz(4 * half + v + 8, chunk) + 4 * (q & 1);
+  }
+  return a;
+}
+
+// Projection of the 32 keys row0 .. row0 + 31 of a staged tile on the wave's
+// features: D[key, feature] = w_f.k_j - |k_j|^2/2 (lane = feature column).
+__device__ __forceinline__ f32x16 kv_proj(const uint16_t* kt, const uint32_t* at, int row0, const KvAddr& ad,
+                                          int col, int half, const u32x4 (&wB)[4], const u32x4 augB) {
   f32x16 acc = {};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
-    acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][swz(row, 2 * kb + half)])),
-                    as_bf16x8(wB[kb]), acc);
-  const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.aug[buf][2 * row]);
+    acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + row0 * 64 + ad.k[kb])), as_bf16x8(wB[kb]),
+                    acc);
+  const u32x2 a = *reinterpret_cast<const u32x2*>(at + 2 * (row0 + col));
   const u32x4 ka4 = half == 0 ? u32x4{a[0], a[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
   return mfma_bf16(as_bf16x8(ka4), as_bf16x8(augB), acc);
 }
 
-// phi = 2^(D log2e - c) for 32 keys, rounded to fp16; S += phi^T (V / sigma_v)
-// and z += phi^T 1 on fp16 MFMA from the same rounded values, so every
-// S_f / z_f is an exact average of the staged values with the rounded weights.
-template <int NW>
-__device__ __forceinline__ void kv_accumulate(const KvSmem<NW>& sm, int buf, int row0,
-                                              const f32x16& pacc, KvFeat& fs, int lane) {
-  const float nc = -fs.c;
-  const u32x4 ones = u32x4{kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
+// phi = 2^(D log2e - c) of the 16 keys in registers 8 kb2 .. 8 kb2 + 7 of a
+// projection, rounded to fp16 and packed as an A operand; z gets their sum.
+__device__ __forceinline__ u32x4 kv_phi(const f32x16& p, int kb2, float nc, float& z) {
+  const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  u32x4 a;
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    u32x4 a;
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t h = pack_f16(fast_exp2(fmaf(p[8 * kb2 + 2 * w], kLog2e, nc)),
+                                fast_exp2(fmaf(p[8 * kb2 + 2 * w + 1], kLog2e, nc)));
+    z = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones, z, false);
+    a[w] = h;
+  }
+  return a;
+}
+
+// S += phi^T (V / sigma_v) for the 16-key group starting at key0 (a multiple
+// of 16) of a staged tile; the value operand is read with the LDS transpose.
+__device__ __forceinline__ void kv_sv(const uint16_t* vt, int key0, const u32x4& a, const KvAddr& ad,
+                                      f32x16 (&sacc)[2]) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float p0 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w], kLog2e, nc));
-      const float p1 = fast_exp2(fmaf(pacc[8 * kb2 + 2 * w + 1], kLog2e, nc));
-      a[w] = pack_f16(p0, p1);
-    }
-    fs.zacc = mfma_f16(as_f16x8(a), as_f16x8(ones), fs.zacc);
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const u32x4 vb = v_operand(sm.v[buf], row0 + 16 * kb2, dt, lane);
-      fs.sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), fs.sacc[dt]);
-    }
+  for (int dt = 0; dt < 2; ++dt) {
+    const v4i16 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)as_lds(vt + key0 * 64 + ad.v[2 * dt]));
+    const v4i16 rb =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)as_lds(vt + key0 * 64 + ad.v[2 * dt + 1]));
+    const u32x2 x = __builtin_bit_cast(u32x2, ra), y = __builtin_bit_cast(u32x2, rb);
+    sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(u32x4{x[0], x[1], y[0], y[1]}), sacc[dt]);
   }
 }
 
@@ -220,118 +264,207 @@ __device__ __forceinline__ void kv_max(const f32x16& pacc, int tok_base, int nto
   c = fmaxf(c, mx * kLog2e);
 }
 
-// One 64-key tile for the wave's FT feature tiles.  MAX: only raise c.  ACC:
-// accumulate with c fixed.  PARTIAL: the tile runs past the end of the key
-// range; tail keys are masked.
-enum { kModeMax = 1, kModeAcc = 2 };
-template <int NW, int FT, int MODE, bool PARTIAL>
-__device__ __forceinline__ void kv_tile(KvSmem<NW>& sm, int buf, int tile0, int ntok,
-                                        const u32x4 augB, KvFeat (&fs)[FT], int col, int half,
-                                        int lane) {
+// Projections of the 32 keys row0 .. row0 + 31 on FT feature tiles, the key
+// operand read once for all of them.
+template <int FT>
+__device__ __forceinline__ void kv_proj_n(const uint16_t* kt, const uint32_t* at, int row0, const KvAddr& ad,
+                                          int col, int half, const KvFeat (&fs)[FT], const u32x4 augB,
+                                          f32x16 (&p)[FT]) {
+  u32x4 kop[4];
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int tok_base = tile0 + 32 * st;
-    if (PARTIAL && tok_base >= ntok) break;
+  for (int kb = 0; kb < 4; ++kb) kop[kb] = *reinterpret_cast<const u32x4*>(kt + row0 * 64 + ad.k[kb]);
+  const u32x2 a = *reinterpret_cast<const u32x2*>(at + 2 * (row0 + col));
+  const u32x4 ka4 = half == 0 ? u32x4{a[0], a[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      f32x16 pacc = kv_proj(sm, buf, 32 * st, col, half, fs[ft].wB, augB);
-      if (MODE == kModeMax) {
-        kv_max(pacc, tok_base, ntok, half, PARTIAL, fs[ft].c);
-        continue;
+  for (int ft = 0; ft < FT; ++ft) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16(as_bf16x8(kop[kb]), as_bf16x8(fs[ft].wB[kb]), acc);
+    p[ft] = mfma_bf16(as_bf16x8(ka4), as_bf16x8(augB), acc);
+  }
+}
+
+// S += phi^T (V / sigma_v) of FT feature tiles for the 16-key group at key0,
+// the value operand read once for all of them.
+template <int FT>
+__device__ __forceinline__ void kv_sv_n(const uint16_t* vt, int key0, const u32x4 (&a)[FT], const KvAddr& ad,
+                                        KvFeat (&fs)[FT]) {
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    const v4i16 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)as_lds(vt + key0 * 64 + ad.v[2 * dt]));
+    const v4i16 rb =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)as_lds(vt + key0 * 64 + ad.v[2 * dt + 1]));
+    const u32x2 x = __builtin_bit_cast(u32x2, ra), y = __builtin_bit_cast(u32x2, rb);
+    const u32x4 vop = u32x4{x[0], x[1], y[0], y[1]};
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) fs[ft].sacc[dt] = mfma_f16(as_f16x8(a[ft]), as_f16x8(vop), fs[ft].sacc[dt]);
+  }
+}
+
+// One full 64-key tile, accumulating with c fixed.  One feature tile: both
+// projections first, then each block's features and S update (the next
+// block's projection overlaps this block's exponentials).  Two feature
+// tiles: block by block, the two tiles' chains interleaving.
+template <int NW, int FT>
+__device__ __forceinline__ void kv_tile_acc(const KvSmem<NW>& sm, int buf, const KvAddr& ad, const u32x4 augB,
+                                            KvFeat (&fs)[FT], int col, int half) {
+  const uint16_t* kt = sm.k[buf];
+  const uint16_t* vt = sm.v[buf];
+  const uint32_t* at = sm.aug[buf];
+  if constexpr (FT == 1) {
+    const float nc = -fs[0].c;
+    const f32x16 p0 = kv_proj(kt, at, 0, ad, col, half, fs[0].wB, augB);
+    const f32x16 p1 = kv_proj(kt, at, 32, ad, col, half, fs[0].wB, augB);
+    const u32x4 a0 = kv_phi(p0, 0, nc, fs[0].z);
+    const u32x4 a1 = kv_phi(p0, 1, nc, fs[0].z);
+    kv_sv(vt, 0, a0, ad, fs[0].sacc);
+    kv_sv(vt, 16, a1, ad, fs[0].sacc);
+    const u32x4 a2 = kv_phi(p1, 0, nc, fs[0].z);
+    const u32x4 a3 = kv_phi(p1, 1, nc, fs[0].z);
+    kv_sv(vt, 32, a2, ad, fs[0].sacc);
+    kv_sv(vt, 48, a3, ad, fs[0].sacc);
+  } else {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x16 p[FT];
+      kv_proj_n<FT>(kt, at, 32 * st, ad, col, half, fs, augB, p);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        u32x4 a[FT];
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) a[ft] = kv_phi(p[ft], kb2, -fs[ft].c, fs[ft].z);
+        kv_sv_n<FT>(vt, 32 * st + 16 * kb2, a, ad, fs);
       }
-      if (PARTIAL) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + 4 * half + (i & 3);
-          if (tok_base + r >= ntok) pacc[i] = -kFInf;
-        }
-      }
-      kv_accumulate(sm, buf, 32 * st, pacc, fs[ft], lane);
     }
   }
 }
 
-// One pass over the key range.  Tiles are loaded into registers two tiles
-// ahead of use (one tile of compute does not cover the load latency), staged
-// into the LDS buffer the next tile reads, and computed from LDS.
-template <int NW, int FT, int MODE>
-__device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntiles, int ntok, int d,
-                                        KvRegs<NW>& r, const uint16_t* Kb, const uint16_t* Vb,
-                                        const u32x4 augB, KvFeat (&fs)[FT], float vinv, float& vmx,
-                                        int tid, int lane) {
-  // Lane-dependent LDS addresses are recomputed per tile rather than held in
-  // loop-invariant registers.
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  const int lcol = ln & 31, lhalf = ln >> 5;
-  kv_tile<NW, FT, MODE, false>(sm, t & 1, t * kKT, ntok, augB, fs, lcol, lhalf, ln);
-  // r holds tile t + 1: stage it, then reuse r for tile t + 3.  The load is
-  // issued on every path (past the end it re-reads the clamped last key), so
-  // the wait before the next stage can leave the other tile's load in flight.
-  if (t + 1 < ntiles) stage_kv<NW>(sm, (t + 1) & 1, r, tid, vinv, vmx);
-  load_kv<NW>(r, Kb, Vb, (t + 3) * kKT, ntok, d, tid);
+// One 64-key tile, block by block.  MAX: only raise c.  ACC: accumulate with
+// c fixed.  PARTIAL: the tile runs past the end of the key range; tail keys
+// are masked.
+enum { kModeMax = 1, kModeAcc = 2 };
+template <int NW, int FT, int MODE, bool PARTIAL>
+__device__ __forceinline__ void kv_tile(const KvSmem<NW>& sm, int buf, int tile0, int ntok, const KvAddr& ad,
+                                        const u32x4 augB, KvFeat (&fs)[FT], int col, int half) {
+  const uint16_t* kt = sm.k[buf];
+  const uint16_t* vt = sm.v[buf];
+  const uint32_t* at = sm.aug[buf];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int tok_base = tile0 + 32 * st;
+    if (PARTIAL && tok_base >= ntok) break;
+    f32x16 p[FT];
+    kv_proj_n<FT>(kt, at, 32 * st, ad, col, half, fs, augB, p);
+    if (MODE == kModeMax) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) kv_max(p[ft], tok_base, ntok, half, PARTIAL, fs[ft].c);
+      continue;
+    }
+    if (PARTIAL) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * half + (i & 3);
+          if (tok_base + r >= ntok) p[ft][i] = -kFInf;
+        }
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      u32x4 a[FT];
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) a[ft] = kv_phi(p[ft], kb2, -fs[ft].c, fs[ft].z);
+      kv_sv_n<FT>(vt, 32 * st + 16 * kb2, a, ad, fs);
+    }
+  }
+}
+
+// One step over a full tile t.  Tiles are loaded into a ring of P register
+// sets, P + 1 tiles ahead of use (the loads of several tiles are in flight
+// while one computes), staged into the LDS buffer the next tile reads, and
+// computed from LDS.  The step stages and loads unconditionally: past the last
+// tile r holds clamped copies of the last key, staged into the free buffer and
+// never read.
+template <int NW, int FT, int MODE, int P>
+__device__ __forceinline__ void kv_step(KvSmem<NW>& sm, int t, int ntok, int d, KvRegs<NW>& r,
+                                        const uint16_t* Kb, const uint16_t* Vb, const KvAddr& ad,
+                                        const u32x4 augB, KvFeat (&fs)[FT], float vinv, float& vmx, int tid,
+                                        int col, int half) {
+  if (MODE == kModeAcc)
+    kv_tile_acc<NW, FT>(sm, t & 1, ad, augB, fs, col, half);
+  else
+    kv_tile<NW, FT, MODE, false>(sm, t & 1, t * kKT, ntok, ad, augB, fs, col, half);
+  stage_kv<NW>(sm, (t + 1) & 1, r, tid, d, vinv, vmx);
+  load_kv<NW>(r, Kb, Vb, (t + P + 1) * kKT, ntok, d, tid);
   lds_barrier();
 }
+
+// Register sets in the prefetch ring (two: a deeper ring measured no faster,
+// the loads of two tiles in flight already cover the compute of one).
+constexpr int kKvRing = 2;
 
 // FIRST: c is first set from tile 0 alone (a max over its keys) and the value
 // scale from tile 0's largest |v|, then the range is accumulated with both
 // fixed; otherwise MODE applies to every tile with the given vinv.  vmx
 // returns the largest |v| of the range (MAX passes).
 template <int NW, int FT, int MODE, bool FIRST>
-__device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb,
-                                         int ntok, int d, const u32x4 augB, KvFeat (&fs)[FT], float& vinv,
-                                         float& vmx, int tid, int lane) {
+__device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, const uint16_t* Vb, int ntok,
+                                         int d, const KvAddr& ad, const u32x4 augB, KvFeat (&fs)[FT],
+                                         float& vinv, float& vmx, int tid, int lane) {
   const int ntiles = (ntok + kKT - 1) / kKT;
   if (ntiles == 0) return;   // uniform over the workgroup
-  KvRegs<NW> ra, rb;
-  load_kv<NW>(ra, Kb, Vb, 0, ntok, d, tid);
+  const int col = lane & 31, half = lane >> 5;
+  constexpr int P = kKvRing;
+  KvRegs<NW> r[P];
+  load_kv<NW>(r[0], Kb, Vb, 0, ntok, d, tid);
   if (FIRST) {
     // values are staged as fp16 after scaling by 1 / sigma_v, a power of two
     // above tile 0's largest |v| (a later tile over 2^15 larger overflows
     // and sends the range to the exact pass)
     float m0 = 0.f;
 #pragma unroll
-    for (int i = 0; i < KvRegs<NW>::R; ++i) m0 = fmaxf(m0, chunk_absmax(ra.v[i]));
+    for (int i = 0; i < KvRegs<NW>::R; ++i) m0 = fmaxf(m0, chunk_absmax(r[0].v[i]));
     vinv = inv_pow2_above(block_max<NW>(sm, m0, tid));
   }
-  stage_kv<NW>(sm, 0, ra, tid, vinv, vmx);
-  load_kv<NW>(ra, Kb, Vb, kKT, ntok, d, tid);
-  load_kv<NW>(rb, Kb, Vb, 2 * kKT, ntok, d, tid);
+  stage_kv<NW>(sm, 0, r[0], tid, d, vinv, vmx);
+#pragma unroll
+  for (int j = 0; j < P; ++j) load_kv<NW>(r[j], Kb, Vb, (j + 1) * kKT, ntok, d, tid);
   lds_barrier();
   if (FIRST) {
-    const int col = lane & 31, half = lane >> 5;
     if (kKT <= ntok)
-      kv_tile<NW, FT, kModeMax, false>(sm, 0, 0, ntok, augB, fs, col, half, lane);
+      kv_tile<NW, FT, kModeMax, false>(sm, 0, 0, ntok, ad, augB, fs, col, half);
     else
-      kv_tile<NW, FT, kModeMax, true>(sm, 0, 0, ntok, augB, fs, col, half, lane);
+      kv_tile<NW, FT, kModeMax, true>(sm, 0, 0, ntok, ad, augB, fs, col, half);
     // 2^8 of headroom: fp16 features of later keys overflow only 2^24 above
     // tile 0's largest
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) fs[ft].c += 8.0f;
   }
-  // full tiles in pairs (ra holds the odd tiles, rb the even ones), then at
-  // most one more full tile and the partial last tile
+  // full tiles P at a time (set j holds tile t + 1 + j), then the remaining
+  // full tiles and the partial last tile
   const int nfull = ntok / kKT;
   int t = 0;
-  for (; t + 2 <= nfull; t += 2) {
-    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, d, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
-    kv_step<NW, FT, MODE>(sm, t + 1, ntiles, ntok, d, rb, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
+  for (; t + P <= nfull; t += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+      kv_step<NW, FT, MODE, P>(sm, t + j, ntok, d, r[j], Kb, Vb, ad, augB, fs, vinv, vmx, tid, col, half);
   }
-  if (t < nfull) {
-    kv_step<NW, FT, MODE>(sm, t, ntiles, ntok, d, ra, Kb, Vb, augB, fs, vinv, vmx, tid, lane);
-    ++t;
+#pragma unroll
+  for (int j = 0; j + 1 < P; ++j) {
+    if (t < nfull) {
+      kv_step<NW, FT, MODE, P>(sm, t, ntok, d, r[j], Kb, Vb, ad, augB, fs, vinv, vmx, tid, col, half);
+      ++t;
+    }
   }
-  if (t < ntiles)
-    kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, augB, fs, lane & 31, lane >> 5, lane);
+  if (t < ntiles) kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, ad, augB, fs, col, half);
 }
 
-// NW waves of FT 32-feature tiles each cover the 32 NW FT features fo ..
-// of a piece (blockIdx.y selects the piece: fo = fo0 + blockIdx.y * 32 NW FT);
-// features at or past m are masked (their range state is written empty).  The
-// library launches FT = 1: with FT = 2 (half the waves, so that two workgroups
-// share a CU) the kernel does not fit its register budget without spills.
+// NW waves of FT 32-feature tiles each cover the 32 NW FT features fo .. of a
+// piece (blockIdx.y selects the piece: fo = fo0 + blockIdx.y * 32 NW FT);
+// features at or past m are masked (their range state is written empty).
+// The library launches FT = 1.
 template <int NW, int FT>
-__global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void k_kv_state(
+__global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
     float* __restrict__ part_S, float* __restrict__ part_zc, float* __restrict__ part_vmax, int H,
     int n, int d, int m, int ma, int fo0, int splits, int span) {
@@ -348,6 +481,7 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
   const int ntok = max(0, min(n, j0 + span) - j0);
   const uint16_t* Kb = K + (static_cast<size_t>(bh) * n + j0) * d;
   const uint16_t* Vb = V + (static_cast<size_t>(bh) * n + j0) * d;
+  const KvAddr ad = kv_addr(lane);
 
   KvFeat fs[FT];
 #pragma unroll
@@ -364,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
       asm volatile("" : "+v"(fs[ft].wB[kb]));
     }
     fs[ft].c = -kFInf;
-    fs[ft].zacc = f32x16{};
+    fs[ft].z = 0.f;
     fs[ft].sacc[0] = f32x16{};
     fs[ft].sacc[1] = f32x16{};
   }
@@ -376,12 +510,11 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
   // pass finds the exact maximum over the range and the range is accumulated
   // again with it.
   float vinv = 1.0f, vmx = 0.f;
-  kv_range<NW, FT, kModeAcc, true>(sm, Kb, Vb, ntok, d, augB, fs, vinv, vmx, tid, lane);
+  kv_range<NW, FT, kModeAcc, true>(sm, Kb, Vb, ntok, d, ad, augB, fs, vinv, vmx, tid, lane);
   bool bad = false;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bad |= !(fabsf(fs[ft].zacc[i]) <= 3.0e38f);
+    bad |= !(fabsf(fs[ft].z) <= 3.0e38f);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -395,14 +528,14 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       fs[ft].c = -kFInf;
-      fs[ft].zacc = f32x16{};
+      fs[ft].z = 0.f;
       fs[ft].sacc[0] = f32x16{};
       fs[ft].sacc[1] = f32x16{};
     }
     vmx = 0.f;
-    kv_range<NW, FT, kModeMax, false>(sm, Kb, Vb, ntok, d, augB, fs, vinv, vmx, tid, lane);
+    kv_range<NW, FT, kModeMax, false>(sm, Kb, Vb, ntok, d, ad, augB, fs, vinv, vmx, tid, lane);
     vinv = inv_pow2_above(block_max<NW>(sm, vmx, tid));
-    kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, d, augB, fs, vinv, vmx, tid, lane);
+    kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, d, ad, augB, fs, vinv, vmx, tid, lane);
   }
 
   // write this range's partial state (S back in value units) and its largest
@@ -418,13 +551,10 @@ __global__ __launch_bounds__(NW * 64, FT == 1 ? FAVOR_KV_WAVES_PER_EU : 2) void 
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
     const int f0 = fo + 32 * (FT * wave + ft);
-    if (half == 0) zc[ma + f0 + col] = f0 + col < m ? fs[ft].c : -kFInf;
-    if (col == 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int fr = f0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        zc[fr] = fr < m ? fs[ft].zacc[i] : 0.f;
-      }
+    const float zf = pair_sum(fs[ft].z);   // the column's two halves, in a fixed order
+    if (half == 0) {
+      zc[f0 + col] = f0 + col < m ? zf : 0.f;
+      zc[ma + f0 + col] = f0 + col < m ? fs[ft].c : -kFInf;
     }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -583,8 +713,11 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 // workgroup's (b, h).
 //   proj: D[feature, query] = w_f.q + beta_f           (lane = query column)
 //   M_i  = max_f D;  u = exp2((D - M_i) log2e) -> fp16 (A operand, k = feature)
-//   [num | den] = u [yhat' | 1]                        (fp16 MFMA, fp32 acc)
+//   num = u yhat'                                      (fp16 MFMA, fp32 acc)
+//   den = sum_f u                                      (same rounded u, v_dot2)
 //   y = sigma * num / den                              (the first d columns)
+// The feature tiles are software-pipelined: tile ft + 1's projection is
+// issued before tile ft's exponentials, which do not depend on it.
 // ---------------------------------------------------------------------------
 template <int MT, int D>
 __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ Q,
@@ -619,30 +752,32 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
     uint32_t w01, w23;
     split3_bf16(beta[static_cast<size_t>(bh) * ma + f], w01, w23);
     *reinterpret_cast<u32x4*>(&wsh[f * kWStride + 64]) = u32x4{w01, w23, 0u, 0u};
-    *reinterpret_cast<u32x4*>(&wsh[f * kWStride + 72]) = u32x4{0u, 0u, 0u, 0u};
   }
   for (int c = tid; c < kD * (ma / 8); c += 256) {
     const int dv = c / (ma / 8), ch = c - dv * (ma / 8);
     *reinterpret_cast<u32x4*>(&ysh[dv * YS + ch * 8]) =
         *reinterpret_cast<const u32x4*>(yhat + (static_cast<size_t>(bh) * kD + dv) * ma + ch * 8);
   }
-  const float sg0 = sigma[static_cast<size_t>(bh) * kD + col];
-  const float sg1 = sigma[static_cast<size_t>(bh) * kD + 32 + col];
+  const float sg = sigma[static_cast<size_t>(bh) * kD];   // one value scale per (b, h)
   __syncthreads();
 
   const u32x4 augB = half == 0 ? u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u}
                                : u32x4{0u, 0u, 0u, 0u};
-  const u32x4 onesB = u32x4{kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
   const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * d;
   float* Ob = out + static_cast<size_t>(bh) * n * d;
 
+  // This lane's query (B operand column), loaded without predication: rows
+  // past the end re-read the last row, and with d = 32 the upper k-blocks are
+  // zero at compile time.  Everything below is per query, so a row past the
+  // end computes exactly the last row's output and is stored there (the same
+  // value to the same address): loads and stores carry no branches, and the
+  // wait for a prefetched tile leaves the stores issued after it in flight.
   auto load_q = [&](int tb, u32x4 (&qB)[4]) {
-    const int qt = tb + col;  // this lane's query (B operand column)
+    const int qt = min(tb + col, t1 - 1);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      qB[kb] = (qt < t1 && 16 * kb + 8 * half < d)
-                   ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * d + 16 * kb + 8 * half)
-                   : u32x4{0u, 0u, 0u, 0u};
+      qB[kb] = 16 * kb < D ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * d + 16 * kb + 8 * half)
+                           : u32x4{0u, 0u, 0u, 0u};
   };
   u32x4 qB[4], qN[4];
   int tb = t0 + 32 * wave;
@@ -650,24 +785,39 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   for (; tb < t1; tb += 128) {
     // Shift: the first feature tile's row maximum (log2 units), so the largest
     // weights sit near 1 with the whole fp16 normal range below them.  A later
-    // feature more than 2^15 above it would overflow fp16; that case is
-    // detected and the tile is redone with the exact row maximum.
-    f32x16 pa = out_proj(wsh, 0, col, half, qB, augB);
-    if (tb + 128 < t1) load_q(tb + 128, qN);  // next tile's queries, in flight during this one
-    float mx = pa[0];
+    // feature more than 2^16 above it overflows fp16 and makes the
+    // denominator infinite; then the tile is redone with the exact row maximum.
+    f32x16 pc = out_proj(wsh, 0, col, half, qB, augB);
+    load_q(tb + 128, qN);  // next tile's queries, in flight during this one
+    float mx = pc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pa[i]);
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pc[i]);
     mx = pair_max(mx);
     float off = -mx * kLog2e;
-    f32x16 yacc0 = {}, yacc1 = {}, dacc = {};
-    float tmax = -kFInf;
-    out_accumulate(pa, off, 0, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
-#pragma unroll 1
-    for (int ft = 1; ft < mt; ++ft) {
-      const f32x16 pn = out_proj(wsh, ft, col, half, qB, augB);
-      out_accumulate(pn, off, ft, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
+    f32x16 yacc0 = {}, yacc1 = {};
+    float den = 0.f;
+    // two tiles per iteration (no copies between the projection registers);
+    // an opaque trip count keeps the loop rolled (fully unrolled, the
+    // compiler hoists every tile's operand reads and runs out of registers)
+    int nft = mt;
+    asm volatile("" : "+s"(nft));
+    int ft = 0;
+    for (; ft + 2 < nft; ft += 2) {
+      const f32x16 pn = out_proj(wsh, ft + 1, col, half, qB, augB);
+      out_accumulate<D>(pc, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
+      out_interleave();
+      pc = out_proj(wsh, ft + 2, col, half, qB, augB);
+      out_accumulate<D>(pn, off, ft + 1, ysh, YS, col, half, yacc0, yacc1, den);
+      out_interleave();
     }
-    if (__ballot(tmax > 15.0f) != 0) {
+    if (ft + 1 < nft) {
+      const f32x16 pn = out_proj(wsh, ft + 1, col, half, qB, augB);
+      out_accumulate<D>(pc, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
+      pc = pn;
+      ++ft;
+    }
+    out_accumulate<D>(pc, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
+    if (__ballot(!(den <= 3.0e38f)) != 0) {
       // exact row maximum, then redo the tile
       mx = -kFInf;
 #pragma unroll 1
@@ -680,35 +830,25 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
       off = -mx * kLog2e;
       yacc0 = f32x16{};
       yacc1 = f32x16{};
-      dacc = f32x16{};
+      den = 0.f;
 #pragma unroll 1
       for (int ft = 0; ft < mt; ++ft) {
         const f32x16 pa = out_proj(wsh, ft, col, half, qB, augB);
-        out_accumulate(pa, off, ft, ysh, YS, col, half, onesB, yacc0, yacc1, dacc, tmax);
+        out_accumulate<D>(pa, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
       }
     }
-    float* orow = Ob + static_cast<size_t>(tb) * d;
-    const bool c1 = 32 + col < d;   // the second 32 value columns exist (d = 64)
-    if (tb + 32 <= t1) {
+    // the query's denominator (both lanes of its column, in a fixed order),
+    // then moved to the rows of the output layout: query r sits in lane r.
+    // Each store writes 128 contiguous bytes per row from 32 lanes.
+    const float dq = pair_sum(den);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-        const float inv = fast_rcp(dacc[i]);
-        __builtin_nontemporal_store(yacc0[i] * sg0 * inv, orow + row * d + col);
-        if (c1) __builtin_nontemporal_store(yacc1[i] * sg1 * inv, orow + row * d + 32 + col);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-        if (tb + row < t1) {
-          const float inv = fast_rcp(dacc[i]);
-          orow[row * d + col] = yacc0[i] * sg0 * inv;
-          if (c1) orow[row * d + 32 + col] = yacc1[i] * sg1 * inv;
-        }
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      const float sc = sg * fast_rcp(__shfl(dq, row));
+      float* orow = Ob + static_cast<size_t>(min(tb + row, t1 - 1)) * d;
+      __builtin_nontemporal_store(yacc0[i] * sc, orow + col);
+      if (D > 32) __builtin_nontemporal_store(yacc1[i] * sc, orow + 32 + col);
     }
-#pragma unroll
     for (int kb = 0; kb < 4; ++kb) qB[kb] = qN[kb];
   }
 }
@@ -744,11 +884,11 @@ __global__ __launch_bounds__(256) void k_slice_combine(const float* __restrict__
   *reinterpret_cast<f32x4*>(out + row * d + 4 * c4) = num * inv;
 }
 
-template <int NW>
+template <int NW, int FT>
 hipError_t launch_kv_piece(const Bf16Plan& p, int fo0, int pieces, const uint16_t* k, const uint16_t* v,
                            const uint16_t* W, float* pS, float* pzc, float* pvm, hipStream_t s) {
   // the causal path runs the same kernel over its segments; it is timed under its own name
-  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, 1>),
+  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, FT>),
                dim3(p.B * p.H * p.splits, pieces), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, p.H, p.n, p.d,
                p.m, p.ma, fo0, p.splits, p.span);
   return hipGetLastError();
@@ -838,17 +978,19 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal, int chunk) {
 
 hipError_t launch_kv_all(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W, float* pS,
                          float* pzc, float* pvm, hipStream_t s) {
-  // the ma / 32 feature tiles as pieces of 8, 4, 2 and 1 tiles (one wave per tile)
+  // the ma / 32 feature tiles as pieces of 8, 4, 2 and 1 tiles (one wave per
+  // tile: two tiles per wave, sharing the operand reads, measured slower and
+  // needed twice the key ranges for the same occupancy)
   int rem = p.ma / 32, fo = 0;
   for (int nw = 8; nw >= 1; nw >>= 1) {
     const int cnt = rem / nw;
     if (cnt == 0) continue;
     hipError_t e = hipSuccess;
     switch (nw) {
-      case 8: e = launch_kv_piece<8>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
-      case 4: e = launch_kv_piece<4>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
-      case 2: e = launch_kv_piece<2>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
-      case 1: e = launch_kv_piece<1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 8: e = launch_kv_piece<8, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 4: e = launch_kv_piece<4, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 2: e = launch_kv_piece<2, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 1: e = launch_kv_piece<1, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
     }
     if (e != hipSuccess) return e;
     fo += cnt * nw * 32;

@@ -464,13 +464,15 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
     if (kt <= qt && rmx[kt] > 0.f) fac[kt] = fast_exp2(amax + s[kt] - Ls);
   const float cfac = mc == -kFInf ? 0.f : fast_exp2(mc - Ls);
 
-  // Both terms accumulate into one numerator (and one denominator, against a
-  // ones operand) from fp16 weights already at the row's scale L: the carry
-  // weights times cfac (packed fp16; a weight under fp16 range is under 2^-24
-  // of the row's largest and drops out), the chunk weights times fac.  The
-  // denominator sums exactly the rounded weights the numerator uses.
-  f32x16 np0 = {}, np1 = {}, den = {};
-  const u32x4 ones = {kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
+  // Both terms accumulate into one numerator from fp16 weights already at the
+  // row's scale L: the carry weights times cfac (packed fp16; a weight under
+  // fp16 range is under 2^-24 of the row's largest and drops out), the chunk
+  // weights times fac.  The denominator sums exactly the rounded weights the
+  // numerator uses, in fp32 (v_dot2 over this lane's weights of its query,
+  // then the two lanes of the query column).
+  f32x16 np0 = {}, np1 = {};
+  float dl = 0.f;
+  const f16x2 ones2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
   const f16x2 cf2 = {static_cast<_Float16>(cfac), static_cast<_Float16>(cfac)};
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
@@ -481,11 +483,13 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       const u32x4 b1 = *reinterpret_cast<const u32x4*>(&sm.ysh[(32 + col) * YS + kpos]);
       u32x4 a;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        a[w] = mul_f16x2(ua[ft][kb2][w], cf2);
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t h = mul_f16x2(ua[ft][kb2][w], cf2);
+        dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, dl, false);
+        a[w] = h;
+      }
       np0 = mfma_f16(as_f16x8(a), as_f16x8(b0), np0);
       np1 = mfma_f16(as_f16x8(a), as_f16x8(b1), np1);
-      den = mfma_f16(as_f16x8(a), as_f16x8(ones), den);
     }
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -494,13 +498,15 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       u32x4 a;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        a[w] = pack_f16(pt[kt][8 * kb2 + 2 * w] * fac[kt], pt[kt][8 * kb2 + 2 * w + 1] * fac[kt]);
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t h = pack_f16(pt[kt][8 * kb2 + 2 * w] * fac[kt], pt[kt][8 * kb2 + 2 * w + 1] * fac[kt]);
+        dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, dl, false);
+        a[w] = h;
+      }
       const u32x4 v0 = v_operand(sm.v, 32 * kt + 16 * kb2, 0, lane);
       const u32x4 v1 = v_operand(sm.v, 32 * kt + 16 * kb2, 1, lane);
       np0 = mfma_f16(as_f16x8(a), as_f16x8(v0), np0);
       np1 = mfma_f16(as_f16x8(a), as_f16x8(v1), np1);
-      den = mfma_f16(as_f16x8(a), as_f16x8(ones), den);
     }
   }
 
@@ -513,14 +519,11 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
     scr[r * kD + (col ^ sw)] = np0[i];
     scr[r * kD + ((32 + col) ^ sw)] = np1[i];
   }
-  // every column of den holds the row sums (D layout: register i = row drow(i, half))
-  if (col == 0) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-      *reinterpret_cast<f32x4*>(&sm.dp[wave][8 * g4 + 4 * half]) =
-          f32x4{den[4 * g4], den[4 * g4 + 1], den[4 * g4 + 2], den[4 * g4 + 3]};
+  const float dq = pair_sum(dl);   // the denominator of query col
+  if (half == 0) {
+    sm.dp[wave][col] = dq;
+    sm.lp[wave][col] = L;
   }
-  if (half == 0) sm.lp[wave][col] = L;
 }
 
 // Power of two >= x (x >= 0); 1 for x = 0.
@@ -777,34 +780,30 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
       }
     }
     // S += Phi(K_t)^T V_t / sigma_v with fp16 key features (at most 2^8); z
-    // sums the same rounded features on the same MFMA (times a ones operand)
+    // sums the same rounded features in fp32 (v_dot2: this lane's keys, then
+    // the two lanes of the feature column)
     const float cs = c == -kFInf ? 0.f : c;
-    f32x16 zacc = {};
-    const u32x4 ones = {kF16OnePair, kF16OnePair, kF16OnePair, kF16OnePair};
+    const f16x2 ones2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    float zp = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         u32x4 a;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          a[w] = pack_f16(fast_exp2(pk[st][8 * kb2 + 2 * w] - cs), fast_exp2(pk[st][8 * kb2 + 2 * w + 1] - cs));
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t h = pack_f16(fast_exp2(pk[st][8 * kb2 + 2 * w] - cs),
+                                      fast_exp2(pk[st][8 * kb2 + 2 * w + 1] - cs));
+          zp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, zp, false);
+          a[w] = h;
+        }
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
           const u32x4 vb = v_operand(sm.v, 32 * st + 16 * kb2, dt, ln);
           sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), sacc[dt]);
         }
-        zacc = mfma_f16(as_f16x8(a), as_f16x8(ones), zacc);
       }
-    // every column of zacc holds the chunk's z of the feature in that row:
-    // rows to lanes through the wave's scalar slots
-    if (col == 0) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]) =
-            f32x4{zacc[4 * g4], zacc[4 * g4 + 1], zacc[4 * g4 + 2], zacc[4 * g4 + 3]};
-    }
-    z += sm.xs[wave][col];
+    z += pair_sum(zp);
     const bool more = t + 1 < nchunks;
     if (more) summarize(col, half);
     if (tile0) {
