@@ -706,8 +706,9 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-// k_output: 4 waves; each wave handles 32 queries at a time with all ma
-// features (MT = ma / 32 tiles).  LDS holds W' = [W |
+// k_output: NWO = 4 waves; each wave handles two 32-query tiles at a time
+// with all ma features (MT = ma / 32 tiles), the W' and yhat operands read from
+// LDS once for both tiles.  LDS holds W' = [W |
 // beta parts] (A operand of the projection; rows past m zero, their beta far
 // below every other) and yhat^T (B operand of the output product) for the
 // workgroup's (b, h).
@@ -719,8 +720,8 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 // The feature tiles are software-pipelined: tile ft + 1's projection is
 // issued before tile ft's exponentials, which do not depend on it.
 // ---------------------------------------------------------------------------
-template <int MT, int D>
-__global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ Q,
+template <int MT, int D, int NWO>
+__global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restrict__ Q,
                                                    const uint16_t* __restrict__ W,
                                                    const uint16_t* __restrict__ yhat,
                                                    const float* __restrict__ beta,
@@ -728,6 +729,7 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
                                                    float* __restrict__ out, int H, int n,
                                                    int m, int span) {
   constexpr int mt = MT, ma = 32 * MT, d = D;
+  constexpr int QT = 2;       // 32-query tiles per wave, sharing every W' and yhat operand read
   constexpr int YS = ma + 8;  // fp16 per staged yhat^T row
   __shared__ __attribute__((aligned(16))) uint16_t wsh[ma * kWStride];
   __shared__ __attribute__((aligned(16))) uint16_t ysh[kD * YS];
@@ -742,18 +744,18 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   const int t1 = min(n, t0 + span);
 
   // stage W' and yhat^T
-  for (int c = tid; c < ma * 8; c += 256) {
+  for (int c = tid; c < ma * 8; c += NWO * 64) {
     const int f = c >> 3, ch = c & 7;
     *reinterpret_cast<u32x4*>(&wsh[f * kWStride + ch * 8]) =
         (f < m && 8 * ch < d) ? *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(hh) * m + f) * d + ch * 8)
                               : u32x4{0u, 0u, 0u, 0u};
   }
-  for (int f = tid; f < ma; f += 256) {
+  for (int f = tid; f < ma; f += NWO * 64) {
     uint32_t w01, w23;
     split3_bf16(beta[static_cast<size_t>(bh) * ma + f], w01, w23);
     *reinterpret_cast<u32x4*>(&wsh[f * kWStride + 64]) = u32x4{w01, w23, 0u, 0u};
   }
-  for (int c = tid; c < kD * (ma / 8); c += 256) {
+  for (int c = tid; c < kD * (ma / 8); c += NWO * 64) {
     const int dv = c / (ma / 8), ch = c - dv * (ma / 8);
     *reinterpret_cast<u32x4*>(&ysh[dv * YS + ch * 8]) =
         *reinterpret_cast<const u32x4*>(yhat + (static_cast<size_t>(bh) * kD + dv) * ma + ch * 8);
@@ -766,90 +768,149 @@ __global__ __launch_bounds__(256, 2) void k_output(const uint16_t* __restrict__ 
   const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * d;
   float* Ob = out + static_cast<size_t>(bh) * n * d;
 
-  // This lane's query (B operand column), loaded without predication: rows
-  // past the end re-read the last row, and with d = 32 the upper k-blocks are
-  // zero at compile time.  Everything below is per query, so a row past the
-  // end computes exactly the last row's output and is stored there (the same
-  // value to the same address): loads and stores carry no branches, and the
-  // wait for a prefetched tile leaves the stores issued after it in flight.
-  auto load_q = [&](int tb, u32x4 (&qB)[4]) {
-    const int qt = min(tb + col, t1 - 1);
+  // This lane's queries (B operand column of each tile), loaded without
+  // predication: rows past the end re-read the last row, and with d = 32 the
+  // upper k-blocks are zero at compile time.  Everything below is per query,
+  // so a row past the end computes exactly the last row's output and is
+  // stored there (the same value to the same address): loads and stores carry
+  // no branches, and the wait for a prefetched tile leaves the stores issued
+  // after it in flight.
+  auto load_q = [&](int tb, u32x4 (&qB)[QT][4]) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      qB[kb] = 16 * kb < D ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * d + 16 * kb + 8 * half)
-                           : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < QT; ++q) {
+      const int qt = min(tb + 32 * q + col, t1 - 1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        qB[q][kb] = 16 * kb < D
+                        ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * d + 16 * kb + 8 * half)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
   };
-  u32x4 qB[4], qN[4];
-  int tb = t0 + 32 * wave;
+  // projections of feature tile ft for the wave's query tiles: the W' operand
+  // (4 k-blocks and the beta block) is read once for all of them
+  auto proj = [&](int ft, const u32x4 (&qB)[QT][4], f32x16 (&pr)[QT]) {
+    const uint16_t* wr = &wsh[(32 * ft + col) * kWStride + 8 * half];
+    u32x4 wa[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) wa[kb] = *reinterpret_cast<const u32x4*>(wr + 16 * kb);
+    const u32x4 aug = half == 0 ? *reinterpret_cast<const u32x4*>(wr + 64) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16(as_bf16x8(wa[kb]), as_bf16x8(qB[q][kb]), acc);
+      pr[q] = mfma_bf16(as_bf16x8(aug), as_bf16x8(augB), acc);
+    }
+  };
+  // weights of feature tile ft -> numerators (the yhat operand read once for
+  // all query tiles) and the denominators (v_dot2 over the same fp16 weights)
+  const f16x2 ones2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  auto accumulate = [&](int ft, const f32x16 (&pr)[QT], const float (&off)[QT], f32x16 (&y0)[QT],
+                        f32x16 (&y1)[QT], float (&den)[QT]) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      u32x4 a[QT];
+#pragma unroll
+      for (int q = 0; q < QT; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t h = pack_f16(fast_exp2(fmaf(pr[q][8 * kb2 + 2 * w], kLog2e, off[q])),
+                                      fast_exp2(fmaf(pr[q][8 * kb2 + 2 * w + 1], kLog2e, off[q])));
+          den[q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, den[q], false);
+          a[q][w] = h;
+        }
+      const int kpos = 32 * ft + 16 * kb2 + 8 * half;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(&ysh[col * YS + kpos]);
+#pragma unroll
+      for (int q = 0; q < QT; ++q) y0[q] = mfma_f16(as_f16x8(a[q]), as_f16x8(b0), y0[q]);
+      if (D > 32) {
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(&ysh[(32 + col) * YS + kpos]);
+#pragma unroll
+        for (int q = 0; q < QT; ++q) y1[q] = mfma_f16(as_f16x8(a[q]), as_f16x8(b1), y1[q]);
+      }
+    }
+  };
+
+  u32x4 qB[QT][4], qN[QT][4];
+  int tb = t0 + 32 * QT * wave;
   if (tb < t1) load_q(tb, qB);
-  for (; tb < t1; tb += 128) {
+  for (; tb < t1; tb += 32 * QT * NWO) {
     // Shift: the first feature tile's row maximum (log2 units), so the largest
     // weights sit near 1 with the whole fp16 normal range below them.  A later
     // feature more than 2^16 above it overflows fp16 and makes the
-    // denominator infinite; then the tile is redone with the exact row maximum.
-    f32x16 pc = out_proj(wsh, 0, col, half, qB, augB);
-    load_q(tb + 128, qN);  // next tile's queries, in flight during this one
-    float mx = pc[0];
+    // denominator infinite; then the tiles are redone with the exact row maxima.
+    f32x16 pr[QT];
+    proj(0, qB, pr);
+    load_q(tb + 32 * QT * NWO, qN);  // next tiles' queries, in flight during these
+    float off[QT], den[QT];
+    f32x16 y0[QT], y1[QT];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pc[i]);
-    mx = pair_max(mx);
-    float off = -mx * kLog2e;
-    f32x16 yacc0 = {}, yacc1 = {};
-    float den = 0.f;
-    // two tiles per iteration (no copies between the projection registers);
+    for (int q = 0; q < QT; ++q) {
+      float mx = pr[q][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, pr[q][i]);
+      off[q] = -pair_max(mx) * kLog2e;
+      den[q] = 0.f;
+      y0[q] = f32x16{};
+      y1[q] = f32x16{};
+    }
+    accumulate(0, pr, off, y0, y1, den);
     // an opaque trip count keeps the loop rolled (fully unrolled, the
     // compiler hoists every tile's operand reads and runs out of registers)
     int nft = mt;
     asm volatile("" : "+s"(nft));
-    int ft = 0;
-    for (; ft + 2 < nft; ft += 2) {
-      const f32x16 pn = out_proj(wsh, ft + 1, col, half, qB, augB);
-      out_accumulate<D>(pc, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
-      out_interleave();
-      pc = out_proj(wsh, ft + 2, col, half, qB, augB);
-      out_accumulate<D>(pn, off, ft + 1, ysh, YS, col, half, yacc0, yacc1, den);
-      out_interleave();
+    for (int ft = 1; ft < nft; ++ft) {
+      proj(ft, qB, pr);
+      accumulate(ft, pr, off, y0, y1, den);
     }
-    if (ft + 1 < nft) {
-      const f32x16 pn = out_proj(wsh, ft + 1, col, half, qB, augB);
-      out_accumulate<D>(pc, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
-      pc = pn;
-      ++ft;
-    }
-    out_accumulate<D>(pc, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
-    if (__ballot(!(den <= 3.0e38f)) != 0) {
-      // exact row maximum, then redo the tile
-      mx = -kFInf;
-#pragma unroll 1
-      for (int ft = 0; ft < mt; ++ft) {
-        const f32x16 pa = out_proj(wsh, ft, col, half, qB, augB);
+    bool over = false;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, pa[i]);
-      }
-      mx = pair_max(mx);
-      off = -mx * kLog2e;
-      yacc0 = f32x16{};
-      yacc1 = f32x16{};
-      den = 0.f;
+    for (int q = 0; q < QT; ++q) over |= !(den[q] <= 3.0e38f);
+    if (__ballot(over) != 0) {
+      // exact row maxima, then redo the tiles
+      float mx[QT];
+#pragma unroll
+      for (int q = 0; q < QT; ++q) mx[q] = -kFInf;
 #pragma unroll 1
       for (int ft = 0; ft < mt; ++ft) {
-        const f32x16 pa = out_proj(wsh, ft, col, half, qB, augB);
-        out_accumulate<D>(pa, off, ft, ysh, YS, col, half, yacc0, yacc1, den);
+        proj(ft, qB, pr);
+#pragma unroll
+        for (int q = 0; q < QT; ++q)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx[q] = fmaxf(mx[q], pr[q][i]);
+      }
+#pragma unroll
+      for (int q = 0; q < QT; ++q) {
+        off[q] = -pair_max(mx[q]) * kLog2e;
+        den[q] = 0.f;
+        y0[q] = f32x16{};
+        y1[q] = f32x16{};
+      }
+#pragma unroll 1
+      for (int ft = 0; ft < mt; ++ft) {
+        proj(ft, qB, pr);
+        accumulate(ft, pr, off, y0, y1, den);
       }
     }
-    // the query's denominator (both lanes of its column, in a fixed order),
+    // each query's denominator (both lanes of its column, in a fixed order),
     // then moved to the rows of the output layout: query r sits in lane r.
     // Each store writes 128 contiguous bytes per row from 32 lanes.
-    const float dq = pair_sum(den);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-      const float sc = sg * fast_rcp(__shfl(dq, row));
-      float* orow = Ob + static_cast<size_t>(min(tb + row, t1 - 1)) * d;
-      __builtin_nontemporal_store(yacc0[i] * sc, orow + col);
-      if (D > 32) __builtin_nontemporal_store(yacc1[i] * sc, orow + 32 + col);
+    for (int q = 0; q < QT; ++q) {
+      const float dq = pair_sum(den[q]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+        const float sc = sg * fast_rcp(__shfl(dq, row));
+        float* orow = Ob + static_cast<size_t>(min(tb + 32 * q + row, t1 - 1)) * d;
+        __builtin_nontemporal_store(y0[q][i] * sc, orow + col);
+        if (D > 32) __builtin_nontemporal_store(y1[q][i] * sc, orow + 32 + col);
+      }
     }
-    for (int kb = 0; kb < 4; ++kb) qB[kb] = qN[kb];
+#pragma unroll
+    for (int q = 0; q < QT; ++q)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) qB[q][kb] = qN[q][kb];
   }
 }
 
@@ -891,6 +952,21 @@ hipError_t launch_kv_piece(const Bf16Plan& p, int fo0, int pieces, const uint16_
   FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, FT>),
                dim3(p.B * p.H * p.splits, pieces), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, p.H, p.n, p.d,
                p.m, p.ma, fo0, p.splits, p.span);
+  return hipGetLastError();
+}
+
+// Output kernel launch for MT feature tiles (four waves per workgroup; six,
+// for three waves per SIMD, measured slower).
+template <int MT>
+hipError_t launch_output(const Bf16Plan& p, const uint16_t* q, const uint16_t* W, const uint16_t* yh,
+                         const float* beta, const float* sigma, float* out, int nblk, int span, hipStream_t s) {
+  constexpr int NV = 4;
+  if (p.d == 64)
+    FAVOR_LAUNCH("k_output", (k_output<MT, 64, NV>), dim3(p.B * p.H * nblk), dim3(NV * 64), 0, s, q, W, yh, beta,
+                 sigma, out, p.H, p.n, p.m, span);
+  else
+    FAVOR_LAUNCH("k_output", (k_output<MT, 32, NV>), dim3(p.B * p.H * nblk), dim3(NV * 64), 0, s, q, W, yh, beta,
+                 sigma, out, p.H, p.n, p.m, span);
   return hipGetLastError();
 }
 
@@ -1090,19 +1166,13 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // output: about 512 workgroups, each a contiguous run of query tiles
   const long long BH = static_cast<long long>(p.B) * p.H;
+  const int nwo = 4;   // waves per workgroup; each iteration covers 64 queries per wave
   long long per = (512 + BH - 1) / BH;
   long long span = (p.n + per - 1) / per;
-  span = align_up(span < 128 ? 128 : span, 128);
+  span = align_up(span < 64 * nwo ? 64 * nwo : span, 64 * nwo);
   const int nblk = static_cast<int>((p.n + span - 1) / span);
-#define FAVOR_OUT_CASE(MTV)                                                                                    \
-  case MTV:                                                                                                  \
-    if (p.d == 64)                                                                                           \
-      FAVOR_LAUNCH("k_output", (k_output<MTV, 64>), dim3(p.B * p.H * nblk), dim3(256), 0, s, q, W, yh, beta,  \
-                   sigma, out, p.H, p.n, p.m, static_cast<int>(span));                                       \
-    else                                                                                                     \
-      FAVOR_LAUNCH("k_output", (k_output<MTV, 32>), dim3(p.B * p.H * nblk), dim3(256), 0, s, q, W, yh, beta,  \
-                   sigma, out, p.H, p.n, p.m, static_cast<int>(span));                                       \
-    break;
+#define FAVOR_OUT_CASE(MTV) \
+  case MTV: return launch_output<MTV>(p, q, W, yh, beta, sigma, out, nblk, static_cast<int>(span), s);
   switch (p.ma / 32) {
     FAVOR_OUT_CASE(1) FAVOR_OUT_CASE(2) FAVOR_OUT_CASE(3) FAVOR_OUT_CASE(4)
     FAVOR_OUT_CASE(5) FAVOR_OUT_CASE(6) FAVOR_OUT_CASE(7) FAVOR_OUT_CASE(8)

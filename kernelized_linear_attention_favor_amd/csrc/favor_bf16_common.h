@@ -72,63 +72,5 @@ __device__ __forceinline__ u32x4 v_operand(const uint16_t* vt, int key0, int dt,
 
 constexpr int kWStride = 72;   // bf16 per staged W' row: 64 d + 8 beta parts (36 banks: 16 rows conflict-free)
 
-// Projection of one 32-feature tile: D[feature, query] = w_f.q + beta_f.
-__device__ __forceinline__ f32x16 out_proj(const uint16_t* wsh, int ft, int col, int half,
-                                           const u32x4 (&qB)[4], const u32x4 augB) {
-  f32x16 acc = {};
-  const uint16_t* wr = &wsh[(32 * ft + col) * kWStride + 8 * half];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(wr + 16 * kb)), as_bf16x8(qB[kb]),
-                    acc);
-  const u32x4 aug = half == 0 ? *reinterpret_cast<const u32x4*>(wr + 64) : u32x4{0u, 0u, 0u, 0u};
-  return mfma_bf16(as_bf16x8(aug), as_bf16x8(augB), acc);
-}
-
-// Softmax weights of one feature tile -> fp16 A operand -> numerator MFMAs
-// (yacc[query, value column]).  den, this lane's share of its query's
-// denominator, sums the same rounded weights in fp32 (v_dot2): a weight that
-// overflows fp16 makes it infinite.
-template <int D>
-__device__ __forceinline__ void out_accumulate(const f32x16& pa, float off, int ft, const uint16_t* ysh, int YS,
-                                               int col, int half, f32x16& yacc0, f32x16& yacc1, float& den) {
-  const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    u32x4 a;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t h = pack_f16(fast_exp2(fmaf(pa[8 * kb2 + 2 * w], kLog2e, off)),
-                                  fast_exp2(fmaf(pa[8 * kb2 + 2 * w + 1], kLog2e, off)));
-      den = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones, den, false);
-      a[w] = h;
-    }
-    const int kpos = 32 * ft + 16 * kb2 + 8 * half;
-    const u32x4 b0 = *reinterpret_cast<const u32x4*>(&ysh[col * YS + kpos]);
-    yacc0 = mfma_f16(as_f16x8(a), as_f16x8(b0), yacc0);
-    if (D > 32) {
-      const u32x4 b1 = *reinterpret_cast<const u32x4*>(&ysh[(32 + col) * YS + kpos]);
-      yacc1 = mfma_f16(as_f16x8(a), as_f16x8(b1), yacc1);
-    }
-  }
-}
-
-// Instruction order for one pipelined output step (the next tile's
-// projection, this tile's weights and numerator): the operand reads first,
-// then each projection MFMA followed by a share of the weights' vector work,
-// then the numerator MFMAs between the two 16-feature groups.  A scheduling
-// hint only; the data dependences are unchanged.
-__device__ __forceinline__ void out_interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);    // LDS reads: W' rows, yhat columns
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one projection MFMA
-    __builtin_amdgcn_sched_group_barrier(0x406, 5, 0);  // vector / transcendental work
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // numerator, first group
-  __builtin_amdgcn_sched_group_barrier(0x406, 24, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // numerator, second group
-}
-
 }  // namespace bf16k
 }  // namespace favor
