@@ -277,6 +277,19 @@ favor_status_t favor_profile_enable(void);
 favor_status_t favor_profile_enable_only(const char* name);
 int favor_profile_collect(const char** names, int* counts, double* total_ms, int capacity);
 
+/*
+ * Test hook for the causal kernel at d = 64, chunk 64, m in {64, 128, 256}
+ * (Performer for vision, How It Works, Step 2: the chunked prefix sums).  In
+ * each chunk the waves of the second query tile receive the first key tile's
+ * features from the waves of the first, guarded by a per-chunk flag; a
+ * waiting wave polls the flag at most `limit` times, then (if the tile has
+ * not been claimed) abandons the hand-over and computes the tile itself.
+ * Both ways give the same output.  Default 4096; 0 abandons every chunk
+ * whose tile is not already claimed, which is how tests reach that path.
+ * Process-wide, read at each launch.  limit < 0: FAVOR_ERR_INVALID_ARGUMENT.
+ */
+favor_status_t favor_set_handover_spin_limit(int limit);
+
 #ifdef __cplusplus
 }
 #endif

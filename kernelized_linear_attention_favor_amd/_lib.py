@@ -56,6 +56,7 @@ SIGNATURES = {
     "favor_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "favor_profile_enable": (_i, []),
     "favor_profile_enable_only": (_i, [ctypes.c_char_p]),
+    "favor_set_handover_spin_limit": (_i, [_i]),
     "favor_profile_collect": (_i, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_i),
                                    ctypes.POINTER(ctypes.c_double), _i]),
 }
@@ -183,6 +184,10 @@ def favor_profile_enable() -> int:
 
 def favor_profile_enable_only(name) -> int:
     return lib().favor_profile_enable_only(None if name is None else name.encode())
+
+
+def favor_set_handover_spin_limit(limit) -> int:
+    return lib().favor_set_handover_spin_limit(limit)
 
 
 def favor_profile_collect(capacity: int = 32) -> dict:

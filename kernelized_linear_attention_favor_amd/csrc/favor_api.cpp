@@ -246,6 +246,12 @@ int favor_version(void) { return 10000; }
 
 favor_status_t favor_profile_enable(void) { return favor_profile_enable_only(nullptr); }
 
+favor_status_t favor_set_handover_spin_limit(int limit) {
+  if (limit < 0) return fail(FAVOR_ERR_INVALID_ARGUMENT, "spin limit %d is negative", limit);
+  favor::g_handover_spin.store(limit, std::memory_order_relaxed);
+  return ok();
+}
+
 favor_status_t favor_profile_enable_only(const char* name) {
   auto& P = favor::g_prof;
   if (name && strlen(name) >= sizeof(P.only))

@@ -1015,12 +1015,16 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal, int chunk) {
   const long long max_splits = (n + kKT - 1) / kKT;
   long long splits;
   if (causal) {
-    // one chunk-walking workgroup per CU: segments per (b, h) and slice
-    splits = (256 + BH * p.nslices - 1) / (BH * p.nslices);
+    // one chunk-walking workgroup per CU (their LDS allows no second): as many
+    // segments per (b, h) and slice as fill the 256 CUs in one round.  Rounded
+    // down: one segment more would leave a second round of a few workgroups
+    // that walks as long as the first.
+    splits = 256 / (BH * p.nslices);
   } else {
-    // about 2048 state waves (8 per CU); a range has ma/32 waves over its pieces
+    // about 2048 state waves (8 per CU) in one round; a range has ma/32 waves
+    // over its pieces (rounded down, as above)
     const long long wgs = 2048 / tiles;
-    splits = (wgs + BH - 1) / BH;
+    splits = wgs / BH;
   }
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -1164,10 +1168,12 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * (p.ma / 16)), dim3(256), 0, s, pS, pzc, pvm, yh,
                beta, sigma, p.ma, p.splits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // output: about 512 workgroups, each a contiguous run of query tiles
+  // output: at most 512 workgroups (two per CU, one round), each a contiguous
+  // run of query tiles
   const long long BH = static_cast<long long>(p.B) * p.H;
   const int nwo = 4;   // waves per workgroup; each iteration covers 64 queries per wave
-  long long per = (512 + BH - 1) / BH;
+  long long per = 512 / BH;
+  if (per < 1) per = 1;
   long long span = (p.n + per - 1) / per;
   span = align_up(span < 64 * nwo ? 64 * nwo : span, 64 * nwo);
   const int nblk = static_cast<int>((p.n + span - 1) / span);

@@ -24,11 +24,18 @@
 //   after them.  Factors common to a row (exp(-|q|^2/2), 1/sqrt(m)) cancel.
 #include <math.h>
 
+#include <atomic>
+
 #include "favor_bf16_common.h"
 #include "favor_internal.h"
 #include "favor_mfma.h"
 
 namespace favor {
+
+// Polls of the key-tile hand-over wait before the query tile 1 wave gives up
+// (see cs_query_phase); set through favor_set_handover_spin_limit.
+std::atomic<int> g_handover_spin{kHandoverSpinDefault};
+
 namespace {
 
 using namespace bf16k;
@@ -188,7 +195,7 @@ __device__ __attribute__((noinline)) CarryW carry_weights_exact(const CsSmem<NW>
 // exp(-|q_i|^2/2) / sqrt(m) common to every term of a row is left out.
 template <int NW, int QT>
 __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lane, float Gm,
-                                               int chunk) {
+                                               int chunk, int spin) {
   constexpr int YS = CsSmem<NW>::YS;
   const float* gexp = sm.gexp();
   constexpr int qt = QT;
@@ -313,7 +320,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       for (int it = 0;;) {
         f = __hip_atomic_load(&sm.hflag[grp], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (f == cgive || f == cnogive) break;
-        if (f != cclaim && ++it >= 4096) {
+        if (f != cclaim && ++it >= spin) {
           // tile 0 has not claimed the slot: abandon the hand-over, unless the
           // flag moved meanwhile (then look again)
           int ok = 0;
@@ -538,7 +545,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ W, const float* __restrict__ part_S,
     const float* __restrict__ part_zc, const float* __restrict__ seg_vmax,
-    float* __restrict__ out, int H, int n, int nseg, int seglen, int has_carry) {
+    float* __restrict__ out, int H, int n, int nseg, int seglen, int has_carry, int spin) {
   constexpr int M = NW * 32;
   constexpr int YS = CsSmem<NW>::YS;
   constexpr int NQ = NW / 2;  // feature groups per query tile
@@ -725,9 +732,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     const int fk = 32 * wave + col;
     const bool tile0 = wave < NW / 2;   // wave-uniform
     if (tile0)
-      cs_query_phase<NW, 0>(sm, wave, ln, Gm, t);
+      cs_query_phase<NW, 0>(sm, wave, ln, Gm, t, spin);
     else
-      cs_query_phase<NW, 1>(sm, wave, ln, Gm, t);
+      cs_query_phase<NW, 1>(sm, wave, ln, Gm, t, spin);
     // Query tile 1 carries twice tile 0's chunk term.  Its waves therefore
     // update their key state after the first barrier, while the tile 0 waves
     // combine the partials; a second barrier then lets the tiles be restaged.
@@ -854,7 +861,8 @@ hipError_t launch_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k
                          const uint16_t* v, const uint16_t* W, const float* pS, const float* pzc,
                          const float* vmax, float* out, hipStream_t s) {
   FAVOR_LAUNCH("k_causal_output", k_causal_chunks<NW>, dim3(p.B * p.H * p.splits), dim3(NW * 64), 0,
-               s, q, k, v, W, pS, pzc, vmax, out, p.H, p.n, p.splits, p.span, p.splits > 1 ? 1 : 0);
+               s, q, k, v, W, pS, pzc, vmax, out, p.H, p.n, p.splits, p.span, p.splits > 1 ? 1 : 0,
+               g_handover_spin.load(std::memory_order_relaxed));
   return hipGetLastError();
 }
 

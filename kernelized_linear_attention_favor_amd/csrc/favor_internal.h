@@ -2,6 +2,8 @@
 // Nothing here is part of the public ABI (include/favor.h).
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -73,6 +75,11 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
 // The causal chunk walk specialised for d = 64, m in {64, 128, 256} and chunks
 // of 64 (k_causal_chunks); other shapes take the general walk (walk::).
 bool causal_chunks_shape(const Bf16Plan& p);
+// Bounded wait of the causal chunk kernel's key-tile hand-over (polls before
+// the waiting wave computes the tile itself).
+constexpr int kHandoverSpinDefault = 4096;
+extern std::atomic<int> g_handover_spin;
+
 hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const uint16_t* W, const float* part_S,
                                 const float* part_zc, const float* vmax, float* out,

@@ -142,6 +142,14 @@ def test_profile_filter_host_only():
     assert L.favor_profile_collect() == {}
 
 
+def test_handover_spin_limit_host_only():
+    # the causal kernel's hand-over wait limit: a setting only, no launch
+    L = _lib()
+    assert L.favor_set_handover_spin_limit(-1) == 1   # invalid argument
+    assert L.favor_set_handover_spin_limit(0) == 0
+    assert L.favor_set_handover_spin_limit(4096) == 0
+
+
 def test_decode_entries_host_only():
     L = _lib()
     assert L.favor_state_bytes(2, 3, 64, 256) == 4 * 2 * 3 * (256 * (64 + 2) + 1)

@@ -278,6 +278,31 @@ def test_bf16_causal_growing_keys():
     assert oracle.max_rel_err(y, oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
 
 
+@pytest.mark.parametrize("limit", [0, 1])
+def test_bf16_causal_handover_fallback(limit):
+    """The key-tile hand-over's bounded wait, forced short from the host: with
+    limit 0 the query tile 1 waves abandon every chunk whose first key tile
+    the tile 0 waves have not yet claimed, and compute that tile themselves.
+    Every launch completes; each output equals the normal run's bit for bit
+    (both ways form the same operands) and meets the oracle's bar."""
+    cfg = fi.config("C2", H=4, n=2048, causal=True)
+    x = fi.make_inputs(cfg)
+    t = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    _lib = favor._lib
+    y0 = favor.attention(t["q"], t["k"], t["v"], t["W"], causal=True)
+    torch.cuda.synchronize()
+    try:
+        _lib.check(_lib.favor_set_handover_spin_limit(limit))
+        ys = [favor.attention(t["q"], t["k"], t["v"], t["W"], causal=True) for _ in range(3)]
+        torch.cuda.synchronize()
+    finally:
+        _lib.check(_lib.favor_set_handover_spin_limit(4096))
+    for y in ys:
+        assert torch.equal(y, y0)
+    ref = oracle.attention_causal(x["q"], x["k"], x["v"], x["W"])
+    assert oracle.max_rel_err(y0.cpu().numpy(), ref) < TOL_BF16
+
+
 def test_profile_filter_records_one_kernel():
     x = fi.make_inputs(fi.config("C2", H=2, n=512))
     t = {k: dev(v, torch.bfloat16) for k, v in x.items()}
