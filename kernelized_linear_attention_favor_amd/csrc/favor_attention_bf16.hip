@@ -731,7 +731,7 @@ __global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restri
   constexpr int mt = MT, ma = 32 * MT, d = D;
   constexpr int QT = 2;       // 32-query tiles per wave, sharing every W' and yhat operand read
   constexpr int YS = ma + 8;  // fp16 per staged yhat^T row
-  __shared__ __attribute__((aligned(16))) uint16_t wsh[ma * kWStride];
+  __shared__ __attribute__((aligned(16))) uint16_t wsh[ma * kWStride + 8];   // + padding read by the last row
   __shared__ __attribute__((aligned(16))) uint16_t ysh[kD * YS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -793,7 +793,11 @@ __global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restri
     u32x4 wa[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) wa[kb] = *reinterpret_cast<const u32x4*>(wr + 16 * kb);
-    const u32x4 aug = half == 0 ? *reinterpret_cast<const u32x4*>(wr + 64) : u32x4{0u, 0u, 0u, 0u};
+    // read by every lane and zeroed for the upper half (a predicated read
+    // would split the loop into branches); the last row's upper half reads
+    // the padding past the table
+    const u32x4 aug_all = *reinterpret_cast<const u32x4*>(wr + 64);
+    const u32x4 aug = half == 0 ? aug_all : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
       f32x16 acc = {};
