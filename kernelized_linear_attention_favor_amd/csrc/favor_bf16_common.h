@@ -70,6 +70,31 @@ __device__ __forceinline__ u32x4 v_operand(const uint16_t* vt, int key0, int dt,
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Lane offsets of v_operand's two reads for the key rows of a 16-key group
+// starting at a multiple of 16 (rows 16 apart share the swizzle pattern, so
+// the group start is an immediate offset): [dt][0] keys 0..7, [dt][1] keys 8..15.
+struct VOpAddr {
+  int a[2][2];
+};
+__device__ __forceinline__ VOpAddr vop_addr(int lane) {
+  const int g = lane >> 4, v = (lane >> 2) & 3, q = lane & 3, h = lane >> 5;
+  VOpAddr r;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    const int chunk = 4 * dt + 2 * (g & 1) + (q >> 1);
+    r.a[dt][0] = swz(4 * h + v, chunk) + 4 * (q & 1);
+    r.a[dt][1] = swz(4 * h + v + 8, chunk) + 4 * (q & 1);
+  }
+  return r;
+}
+// v_operand with precomputed lane offsets; key0 a multiple of 16.
+__device__ __forceinline__ u32x4 v_operand_at(const uint16_t* vt, int key0, int dt, const VOpAddr& va) {
+  const v4i16 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)as_lds(vt + key0 * 64 + va.a[dt][0]));
+  const v4i16 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)as_lds(vt + key0 * 64 + va.a[dt][1]));
+  const u32x2 a = __builtin_bit_cast(u32x2, ra), b = __builtin_bit_cast(u32x2, rb);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 constexpr int kWStride = 72;   // bf16 per staged W' row: 64 d + 8 beta parts (36 banks: 16 rows conflict-free)
 
 }  // namespace bf16k

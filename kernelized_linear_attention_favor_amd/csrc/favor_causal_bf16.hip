@@ -133,6 +133,31 @@ __device__ __forceinline__ void tile_rows(const uint16_t* t, int row, int half, 
   for (int kb = 0; kb < 4; ++kb) xB[kb] = *reinterpret_cast<const u32x4*>(&t[swz(row, 2 * kb + half)]);
 }
 
+// Lane offsets of a row operand (16 bytes of row `col`, chunk 2 kb + half) in
+// a swizzled tile; rows 16 apart share the swizzle, so a row base that is a
+// multiple of 16 is an immediate offset.
+struct RowAddr {
+  int c[4];
+};
+__device__ __forceinline__ RowAddr row_addr(int lane) {
+  RowAddr r;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) r.c[kb] = swz(lane & 31, 2 * kb + (lane >> 5));
+  return r;
+}
+// w_proj / tile_rows for row base + col, base a multiple of 16.
+__device__ __forceinline__ f32x16 w_proj_at(const uint16_t* w, int base, const RowAddr& ra, const u32x4 (&xB)[4]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(w + base * 64 + ra.c[kb])), as_bf16x8(xB[kb]), acc);
+  return acc;
+}
+__device__ __forceinline__ void tile_rows_at(const uint16_t* t, int base, const RowAddr& ra, u32x4 (&xB)[4]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) xB[kb] = *reinterpret_cast<const u32x4*>(t + base * 64 + ra.c[kb]);
+}
+
 // Row of D-layout register i inside a 32 x 32 tile, for lane half `half`.
 __device__ __forceinline__ int drow(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
@@ -202,11 +227,12 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
   const int col = lane & 31, half = lane >> 5;
   const int f0 = 64 * (wave % (NW / 2));
 
+  const RowAddr ra = row_addr(lane);
   u32x4 xB[4];
-  tile_rows(sm.q, 32 * qt + col, half, xB);
+  tile_rows_at(sm.q, 32 * qt, ra, xB);
   f32x16 pa[2];
-  pa[0] = w_proj(sm.w, f0 + col, half, xB);
-  pa[1] = w_proj(sm.w, f0 + 32 + col, half, xB);
+  pa[0] = w_proj_at(sm.w, f0, ra, xB);
+  pa[1] = w_proj_at(sm.w, f0 + 32, ra, xB);
   // query features 2^(a_if - alpha_i), alpha_i = max_f a_if (the maximum of
   // the raw projections, scaled afterwards: rounding is monotone), in place
   float amax = -kFInf;
@@ -353,12 +379,12 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         continue;
       }
     }
-    tile_rows(sm.k, 32 * kt + col, half, xB);
+    tile_rows_at(sm.k, 32 * kt, ra, xB);
     float sh = 0.f;
     bool give = false;   // wave-uniform
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft) {
-      const f32x16 pk = w_proj(sm.w, f0 + 32 * ft + col, half, xB);
+      const f32x16 pk = w_proj_at(sm.w, f0 + 32 * ft, ra, xB);
       if (ft == 0) {
         float bm = -kFInf;
 #pragma unroll
@@ -498,6 +524,7 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       np0 = mfma_f16(as_f16x8(a), as_f16x8(b0), np0);
       np1 = mfma_f16(as_f16x8(a), as_f16x8(b1), np1);
     }
+  const VOpAddr va = vop_addr(lane);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     if (kt > qt) break;
@@ -510,21 +537,27 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, dl, false);
         a[w] = h;
       }
-      const u32x4 v0 = v_operand(sm.v, 32 * kt + 16 * kb2, 0, lane);
-      const u32x4 v1 = v_operand(sm.v, 32 * kt + 16 * kb2, 1, lane);
+      const u32x4 v0 = v_operand_at(sm.v, 32 * kt + 16 * kb2, 0, va);
+      const u32x4 v1 = v_operand_at(sm.v, 32 * kt + 16 * kb2, 1, va);
       np0 = mfma_f16(as_f16x8(a), as_f16x8(v0), np0);
       np1 = mfma_f16(as_f16x8(a), as_f16x8(v1), np1);
     }
   }
 
+  // row r's 64 values with their 8-float blocks XOR-swizzled by r & 7, so
+  // that the combine step's reads of 8 rows hit different banks.  Register
+  // 4 g + j holds row r = 8 g + 4 half + j, and r & 7 = 4 half + j does not
+  // depend on g: four lane addresses per value tile, g an immediate offset.
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = drow(i, half);
-    // row r's 64 values with their 8-float blocks XOR-swizzled by r & 7, so
-    // that the combine step's reads of 8 rows hit different banks
-    const int sw = (r & 7) << 3;
-    scr[r * kD + (col ^ sw)] = np0[i];
-    scr[r * kD + ((32 + col) ^ sw)] = np1[i];
+  for (int j = 0; j < 4; ++j) {
+    const int rj = 4 * half + j;
+    float* b0 = scr + rj * kD + (col ^ (rj << 3));
+    float* b1 = scr + rj * kD + ((32 + col) ^ (rj << 3));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      b0[g * 8 * kD] = np0[4 * g + j];
+      b1[g * 8 * kD] = np1[4 * g + j];
+    }
   }
   const float dq = pair_sum(dl);   // the denominator of query col
   if (half == 0) {
@@ -744,14 +777,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     // ---- key side: this chunk's keys into the wave's features
     f32x16 pk[2];
     {
+      const RowAddr ra = row_addr(ln);
       u32x4 wB[4];
-      tile_rows(sm.w, fk, half, wB);
+      tile_rows_at(sm.w, 32 * wave, ra, wB);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         f32x16 acc = {};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[swz(32 * st + col, 2 * kb + half)])),
+          acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[32 * st * 64 + ra.c[kb]])),
                           as_bf16x8(wB[kb]), acc);
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -791,6 +825,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     // the two lanes of the feature column)
     const float cs = c == -kFInf ? 0.f : c;
     const f16x2 ones2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    const VOpAddr va = vop_addr(ln);
     float zp = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -806,7 +841,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
         }
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          const u32x4 vb = v_operand(sm.v, 32 * st + 16 * kb2, dt, ln);
+          const u32x4 vb = v_operand_at(sm.v, 32 * st + 16 * kb2, dt, va);
           sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), sacc[dt]);
         }
       }
