@@ -743,6 +743,31 @@ __global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restri
   const int t0 = blk * span;
   const int t1 = min(n, t0 + span);
 
+  const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * d;
+  float* Ob = out + static_cast<size_t>(bh) * n * d;
+
+  // This lane's queries (B operand column of each tile), loaded without
+  // predication: rows past the end re-read the last row, and with d = 32 the
+  // upper k-blocks are zero at compile time.  Everything below is per query,
+  // so a row past the end computes exactly the last row's output and is
+  // stored there (the same value to the same address): loads and stores carry
+  // no branches, and the wait for a prefetched tile leaves the stores issued
+  // after it in flight.
+  auto load_q = [&](int tb, u32x4 (&qB)[QT][4]) {
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      const int qt = min(tb + 32 * q + col, t1 - 1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        qB[q][kb] = 16 * kb < D
+                        ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * d + 16 * kb + 8 * half)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 qB[QT][4], qN[QT][4];
+  int tb = t0 + 32 * QT * wave;
+  if (tb < t1) load_q(tb, qB);   // the first queries, in flight during the staging below
+
   // stage W' and yhat^T
   for (int c = tid; c < ma * 8; c += NWO * 64) {
     const int f = c >> 3, ch = c & 7;
@@ -765,27 +790,6 @@ __global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restri
 
   const u32x4 augB = half == 0 ? u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u}
                                : u32x4{0u, 0u, 0u, 0u};
-  const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * d;
-  float* Ob = out + static_cast<size_t>(bh) * n * d;
-
-  // This lane's queries (B operand column of each tile), loaded without
-  // predication: rows past the end re-read the last row, and with d = 32 the
-  // upper k-blocks are zero at compile time.  Everything below is per query,
-  // so a row past the end computes exactly the last row's output and is
-  // stored there (the same value to the same address): loads and stores carry
-  // no branches, and the wait for a prefetched tile leaves the stores issued
-  // after it in flight.
-  auto load_q = [&](int tb, u32x4 (&qB)[QT][4]) {
-#pragma unroll
-    for (int q = 0; q < QT; ++q) {
-      const int qt = min(tb + 32 * q + col, t1 - 1);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        qB[q][kb] = 16 * kb < D
-                        ? *reinterpret_cast<const u32x4*>(Qb + static_cast<size_t>(qt) * d + 16 * kb + 8 * half)
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
   // projections of feature tile ft for the wave's query tiles: the W' operand
   // (4 k-blocks and the beta block) is read once for all of them
   auto proj = [&](int ft, const u32x4 (&qB)[QT][4], f32x16 (&pr)[QT]) {
@@ -835,9 +839,6 @@ __global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restri
     }
   };
 
-  u32x4 qB[QT][4], qN[QT][4];
-  int tb = t0 + 32 * QT * wave;
-  if (tb < t1) load_q(tb, qB);
   for (; tb < t1; tb += 32 * QT * NWO) {
     // Shift: the first feature tile's row maximum (log2 units), so the largest
     // weights sit near 1 with the whole fp16 normal range below them.  A later

@@ -774,79 +774,82 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
     // (Every wave passes three barriers per chunk, at wave-uniform points.)
     if (!tile0) lds_barrier();
 
-    // ---- key side: this chunk's keys into the wave's features
-    f32x16 pk[2];
-    {
-      const RowAddr ra = row_addr(ln);
-      u32x4 wB[4];
-      tile_rows_at(sm.w, 32 * wave, ra, wB);
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[32 * st * 64 + ra.c[kb]])),
-                          as_bf16x8(wB[kb]), acc);
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 kn = *reinterpret_cast<const f32x4*>(&sm.knorm[32 * st + 8 * g4 + 4 * half]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[4 * g4 + j] = fmaf(acc[4 * g4 + j], kLog2e, kn[j]);
-        }
-        pk[st] = acc;
-      }
-    }
-    float mx = -kFInf;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, pk[st][i]);
-    mx = pair_max(mx);
-    // raise the shift when this chunk's keys exceed it by more than 2^8
-    const bool need = mx > c + 8.0f;
-    if (__ballot(need) != 0) {
-      const float cn = need ? mx : c;
-      const float sc = need ? ((c == -kFInf) ? 0.f : exp2f(c - cn)) : 1.0f;
-      z *= sc;
-      c = cn;
-      if (half == 0) sm.xs[wave][col] = sc;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sacc[0][4 * g4 + j] *= s4[j];
-          sacc[1][4 * g4 + j] *= s4[j];
-        }
-      }
-    }
-    // S += Phi(K_t)^T V_t / sigma_v with fp16 key features (at most 2^8); z
-    // sums the same rounded features in fp32 (v_dot2: this lane's keys, then
-    // the two lanes of the feature column)
-    const float cs = c == -kFInf ? 0.f : c;
-    const f16x2 ones2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    const VOpAddr va = vop_addr(ln);
-    float zp = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        u32x4 a;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t h = pack_f16(fast_exp2(pk[st][8 * kb2 + 2 * w] - cs),
-                                      fast_exp2(pk[st][8 * kb2 + 2 * w + 1] - cs));
-          zp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, zp, false);
-          a[w] = h;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const u32x4 vb = v_operand_at(sm.v, 32 * st + 16 * kb2, dt, va);
-          sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), sacc[dt]);
-        }
-      }
-    z += pair_sum(zp);
+    // ---- key side: this chunk's keys into the wave's features (not after
+    // the segment's last chunk, whose state nothing reads)
     const bool more = t + 1 < nchunks;
+    if (more) {
+      f32x16 pk[2];
+      {
+        const RowAddr ra = row_addr(ln);
+        u32x4 wB[4];
+        tile_rows_at(sm.w, 32 * wave, ra, wB);
+  #pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          f32x16 acc = {};
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[32 * st * 64 + ra.c[kb]])),
+                            as_bf16x8(wB[kb]), acc);
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 kn = *reinterpret_cast<const f32x4*>(&sm.knorm[32 * st + 8 * g4 + 4 * half]);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * g4 + j] = fmaf(acc[4 * g4 + j], kLog2e, kn[j]);
+          }
+          pk[st] = acc;
+        }
+      }
+      float mx = -kFInf;
+  #pragma unroll
+      for (int st = 0; st < 2; ++st)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, pk[st][i]);
+      mx = pair_max(mx);
+      // raise the shift when this chunk's keys exceed it by more than 2^8
+      const bool need = mx > c + 8.0f;
+      if (__ballot(need) != 0) {
+        const float cn = need ? mx : c;
+        const float sc = need ? ((c == -kFInf) ? 0.f : exp2f(c - cn)) : 1.0f;
+        z *= sc;
+        c = cn;
+        if (half == 0) sm.xs[wave][col] = sc;
+  #pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sm.xs[wave][8 * g4 + 4 * half]);
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sacc[0][4 * g4 + j] *= s4[j];
+            sacc[1][4 * g4 + j] *= s4[j];
+          }
+        }
+      }
+      // S += Phi(K_t)^T V_t / sigma_v with fp16 key features (at most 2^8); z
+      // sums the same rounded features in fp32 (v_dot2: this lane's keys, then
+      // the two lanes of the feature column)
+      const float cs = c == -kFInf ? 0.f : c;
+      const f16x2 ones2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+      const VOpAddr va = vop_addr(ln);
+      float zp = 0.f;
+  #pragma unroll
+      for (int st = 0; st < 2; ++st)
+  #pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          u32x4 a;
+  #pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t h = pack_f16(fast_exp2(pk[st][8 * kb2 + 2 * w] - cs),
+                                        fast_exp2(pk[st][8 * kb2 + 2 * w + 1] - cs));
+            zp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, zp, false);
+            a[w] = h;
+          }
+  #pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const u32x4 vb = v_operand_at(sm.v, 32 * st + 16 * kb2, dt, va);
+            sacc[dt] = mfma_f16(as_f16x8(a), as_f16x8(vb), sacc[dt]);
+          }
+        }
+      z += pair_sum(zp);
+    }
     if (more) summarize(col, half);
     if (tile0) {
       lds_barrier();
