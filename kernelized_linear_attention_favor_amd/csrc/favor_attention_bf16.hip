@@ -706,9 +706,11 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-// k_output: NWO = 4 waves; each wave handles two 32-query tiles at a time
-// with all ma features (MT = ma / 32 tiles), the W' and yhat operands read from
-// LDS once for both tiles.  LDS holds W' = [W |
+// k_output: NWO waves; each wave handles 32 queries at a time (two tiles of
+// 32 with four-wave workgroups, the W' and yhat operands then read once for
+// both) with all ma features (MT = ma / 32 tiles).  While two workgroups' LDS
+// fit a CU (ma <= 256), eight-wave workgroups at 128 VGPRs give four waves
+// per SIMD; larger tables take four waves and two tiles each.  LDS holds W' = [W |
 // beta parts] (A operand of the projection; rows past m zero, their beta far
 // below every other) and yhat^T (B operand of the output product) for the
 // workgroup's (b, h).
@@ -721,7 +723,7 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 // issued before tile ft's exponentials, which do not depend on it.
 // ---------------------------------------------------------------------------
 template <int MT, int D, int NWO>
-__global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(NWO * 64, NWO == 8 ? 4 : 2) void k_output(const uint16_t* __restrict__ Q,
                                                    const uint16_t* __restrict__ W,
                                                    const uint16_t* __restrict__ yhat,
                                                    const float* __restrict__ beta,
@@ -729,7 +731,7 @@ __global__ __launch_bounds__(NWO * 64, 2) void k_output(const uint16_t* __restri
                                                    float* __restrict__ out, int H, int n,
                                                    int m, int span) {
   constexpr int mt = MT, ma = 32 * MT, d = D;
-  constexpr int QT = 2;       // 32-query tiles per wave, sharing every W' and yhat operand read
+  constexpr int QT = NWO == 8 ? 1 : 2;   // 32-query tiles per wave
   constexpr int YS = ma + 8;  // fp16 per staged yhat^T row
   __shared__ __attribute__((aligned(16))) uint16_t wsh[ma * kWStride + 8];   // + padding read by the last row
   __shared__ __attribute__((aligned(16))) uint16_t ysh[kD * YS];
@@ -960,12 +962,12 @@ hipError_t launch_kv_piece(const Bf16Plan& p, int fo0, int pieces, const uint16_
   return hipGetLastError();
 }
 
-// Output kernel launch for MT feature tiles (four waves per workgroup; six,
-// for three waves per SIMD, measured slower).
+// Output kernel launch for MT feature tiles: eight waves per workgroup (four
+// per SIMD) while two workgroups' LDS fit a CU, else four.
 template <int MT>
 hipError_t launch_output(const Bf16Plan& p, const uint16_t* q, const uint16_t* W, const uint16_t* yh,
                          const float* beta, const float* sigma, float* out, int nblk, int span, hipStream_t s) {
-  constexpr int NV = 4;
+  constexpr int NV = MT <= 8 ? 8 : 4;
   if (p.d == 64)
     FAVOR_LAUNCH("k_output", (k_output<MT, 64, NV>), dim3(p.B * p.H * nblk), dim3(NV * 64), 0, s, q, W, yh, beta,
                  sigma, out, p.H, p.n, p.m, span);
@@ -1176,7 +1178,7 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   // output: at most 512 workgroups (two per CU, one round), each a contiguous
   // run of query tiles
   const long long BH = static_cast<long long>(p.B) * p.H;
-  const int nwo = 4;   // waves per workgroup; each iteration covers 64 queries per wave
+  const int nwo = 4;   // a workgroup iteration covers 256 queries (8 waves x 32 or 4 waves x 64)
   long long per = 512 / BH;
   if (per < 1) per = 1;
   long long span = (p.n + per - 1) / per;
