@@ -706,11 +706,11 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-// k_output: NWO waves; each wave handles 32 queries at a time (two tiles of
-// 32 with four-wave workgroups, the W' and yhat operands then read once for
-// both) with all ma features (MT = ma / 32 tiles).  While two workgroups' LDS
-// fit a CU (ma <= 256), eight-wave workgroups at 128 VGPRs give four waves
-// per SIMD; larger tables take four waves and two tiles each.  LDS holds W' = [W |
+// k_output: 8 waves; each wave handles 32 queries at a time with all ma
+// features (MT = ma / 32 tiles).  While two workgroups' LDS fit a CU (ma <=
+// 288) the kernel runs at 128 VGPRs, four waves per SIMD; beyond, one
+// workgroup per CU, two waves per SIMD, and each wave takes two 32-query tiles
+// at a time (the W' and yhat operands read once for both).  LDS holds W' = [W |
 // beta parts] (A operand of the projection; rows past m zero, their beta far
 // below every other) and yhat^T (B operand of the output product) for the
 // workgroup's (b, h).
@@ -722,8 +722,14 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 // The feature tiles are software-pipelined: tile ft + 1's projection is
 // issued before tile ft's exponentials, which do not depend on it.
 // ---------------------------------------------------------------------------
-template <int MT, int D, int NWO>
-__global__ __launch_bounds__(NWO * 64, NWO == 8 ? 4 : 2) void k_output(const uint16_t* __restrict__ Q,
+// LDS of the output kernel for MT feature tiles (W' table with its padding,
+// yhat^T), and whether two workgroups fit a CU's 160 KB.
+constexpr int out_lds_bytes(int mt) { return (32 * mt * kWStride + 8) * 2 + kD * (32 * mt + 8) * 2; }
+constexpr bool out_two_per_cu(int mt) { return 2 * out_lds_bytes(mt) <= 160 * 1024; }
+constexpr int kOutWaves = 8;
+
+template <int MT, int D>
+__global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_output(const uint16_t* __restrict__ Q,
                                                    const uint16_t* __restrict__ W,
                                                    const uint16_t* __restrict__ yhat,
                                                    const float* __restrict__ beta,
@@ -731,7 +737,8 @@ __global__ __launch_bounds__(NWO * 64, NWO == 8 ? 4 : 2) void k_output(const uin
                                                    float* __restrict__ out, int H, int n,
                                                    int m, int span) {
   constexpr int mt = MT, ma = 32 * MT, d = D;
-  constexpr int QT = NWO == 8 ? 1 : 2;   // 32-query tiles per wave
+  constexpr int NWO = kOutWaves;
+  constexpr int QT = out_two_per_cu(MT) ? 1 : 2;   // 32-query tiles per wave
   constexpr int YS = ma + 8;  // fp16 per staged yhat^T row
   __shared__ __attribute__((aligned(16))) uint16_t wsh[ma * kWStride + 8];   // + padding read by the last row
   __shared__ __attribute__((aligned(16))) uint16_t ysh[kD * YS];
@@ -962,18 +969,26 @@ hipError_t launch_kv_piece(const Bf16Plan& p, int fo0, int pieces, const uint16_
   return hipGetLastError();
 }
 
-// Output kernel launch for MT feature tiles: eight waves per workgroup (four
-// per SIMD) while two workgroups' LDS fit a CU, else four.
+// Output kernel launch for MT feature tiles: as many workgroups as fit the
+// CUs in one round (two or one per CU by LDS), each a contiguous run of query
+// tiles.
 template <int MT>
 hipError_t launch_output(const Bf16Plan& p, const uint16_t* q, const uint16_t* W, const uint16_t* yh,
-                         const float* beta, const float* sigma, float* out, int nblk, int span, hipStream_t s) {
-  constexpr int NV = MT <= 8 ? 8 : 4;
+                         const float* beta, const float* sigma, float* out, hipStream_t s) {
+  constexpr bool two = out_two_per_cu(MT);
+  constexpr int step = 32 * (two ? 1 : 2) * kOutWaves;   // queries per workgroup iteration
+  const long long BH = static_cast<long long>(p.B) * p.H;
+  long long per = (two ? 512 : 256) / BH;
+  if (per < 1) per = 1;
+  long long span = (p.n + per - 1) / per;
+  span = align_up(span < step ? step : span, step);
+  const int nblk = static_cast<int>((p.n + span - 1) / span);
   if (p.d == 64)
-    FAVOR_LAUNCH("k_output", (k_output<MT, 64, NV>), dim3(p.B * p.H * nblk), dim3(NV * 64), 0, s, q, W, yh, beta,
-                 sigma, out, p.H, p.n, p.m, span);
+    FAVOR_LAUNCH("k_output", (k_output<MT, 64>), dim3(p.B * p.H * nblk), dim3(kOutWaves * 64), 0, s, q, W, yh,
+                 beta, sigma, out, p.H, p.n, p.m, static_cast<int>(span));
   else
-    FAVOR_LAUNCH("k_output", (k_output<MT, 32, NV>), dim3(p.B * p.H * nblk), dim3(NV * 64), 0, s, q, W, yh, beta,
-                 sigma, out, p.H, p.n, p.m, span);
+    FAVOR_LAUNCH("k_output", (k_output<MT, 32>), dim3(p.B * p.H * nblk), dim3(kOutWaves * 64), 0, s, q, W, yh,
+                 beta, sigma, out, p.H, p.n, p.m, static_cast<int>(span));
   return hipGetLastError();
 }
 
@@ -1175,17 +1190,8 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * (p.ma / 16)), dim3(256), 0, s, pS, pzc, pvm, yh,
                beta, sigma, p.ma, p.splits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // output: at most 512 workgroups (two per CU, one round), each a contiguous
-  // run of query tiles
-  const long long BH = static_cast<long long>(p.B) * p.H;
-  const int nwo = 4;   // a workgroup iteration covers 256 queries (8 waves x 32 or 4 waves x 64)
-  long long per = 512 / BH;
-  if (per < 1) per = 1;
-  long long span = (p.n + per - 1) / per;
-  span = align_up(span < 64 * nwo ? 64 * nwo : span, 64 * nwo);
-  const int nblk = static_cast<int>((p.n + span - 1) / span);
 #define FAVOR_OUT_CASE(MTV) \
-  case MTV: return launch_output<MTV>(p, q, W, yh, beta, sigma, out, nblk, static_cast<int>(span), s);
+  case MTV: return launch_output<MTV>(p, q, W, yh, beta, sigma, out, s);
   switch (p.ma / 32) {
     FAVOR_OUT_CASE(1) FAVOR_OUT_CASE(2) FAVOR_OUT_CASE(3) FAVOR_OUT_CASE(4)
     FAVOR_OUT_CASE(5) FAVOR_OUT_CASE(6) FAVOR_OUT_CASE(7) FAVOR_OUT_CASE(8)

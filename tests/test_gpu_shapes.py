@@ -59,11 +59,12 @@ def check(x, y, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("m", [16, 48, 96, 192, 320, 512])
+@pytest.mark.parametrize("m", [16, 48, 96, 192, 288, 320, 512])
 @pytest.mark.parametrize("n", NS)
 def test_feature_counts(n, m, causal):
     """m in 16Z beyond {64, 128, 256}: a masked half tile (16, 48), odd tile counts
-    (96, 192: 3 and 6 waves), and feature slices in the causal walk (320, 512)."""
+    (96, 192: 3 and 6 waves), the largest table two output workgroups share a CU
+    with (288), and feature slices in the causal walk (288, 320, 512)."""
     x = inputs(1, 2, n, 64, m, 1000 + m + n)
     check(x, gpu(x, causal), causal)
 
