@@ -122,9 +122,30 @@ def dist(us_list) -> dict:
             "calls": len(us_list)}
 
 
+def dpm_clocks(props):
+    """Current shader and memory clock levels of the device, read from the
+    driver's sysfs DPM tables (the level marked '*').  Read in-process: a tool
+    started as a child would inherit a profiler's preload.  None if the tables
+    are not visible."""
+    import glob
+    want = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}"
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            if not os.path.basename(os.path.realpath(dev)).startswith(want):
+                continue
+            out = []
+            for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+                with open(os.path.join(dev, name)) as fh:
+                    cur = [ln.strip() for ln in fh if ln.rstrip().endswith("*")]
+                out.append(f"{name[7:]} {cur[0].rstrip(' *')}" if cur else f"{name[7:]} ?")
+            return out
+        except OSError:
+            continue
+    return None
+
+
 def environment(torch) -> dict:
     """GPU, clocks, software versions and the library that was timed."""
-    import subprocess
     props = torch.cuda.get_device_properties(0)
     env = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
            "compute_units": props.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__}
@@ -133,13 +154,7 @@ def environment(torch) -> dict:
             env["rocm"] = fh.read().strip()
     except OSError:
         env["rocm"] = None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        clocks = [ln.split(":", 1)[1].strip() if ":" in ln else ln.strip()
-                  for ln in r.stdout.splitlines() if "sclk" in ln.lower() or "mclk" in ln.lower()]
-        env["clocks"] = clocks[:4] or None
-    except Exception as e:  # the tool may be absent; the line still prints
-        env["clocks"] = f"unavailable ({type(e).__name__})"
+    env["clocks"] = dpm_clocks(props)
     from kernelized_linear_attention_favor_amd import _lib as L
     h = hashlib.sha256()
     with open(L.LIB_PATH, "rb") as fh:
