@@ -78,6 +78,7 @@ struct KvSmem {
   uint16_t v[kKBuf][kKT * kD];     // values / sigma_v, fp16
   uint32_t aug[kKBuf][kAugWords];  // per key: (p0 | p1 << 16, p2), the bf16 parts of -|k|^2/2
   float vred[NW];
+  float zinv[NW][32];              // per wave: 1 / z_f of its features (single-range epilogue)
   int flag;
 };
 
@@ -461,6 +462,65 @@ __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, con
   if (t < ntiles) kv_tile<NW, FT, MODE, true>(sm, t & 1, t * kKT, ntok, ad, augB, fs, col, half);
 }
 
+// Where the state pass writes when a (b, h) has a single key range: the
+// merge's outputs (yhat, beta, sigma), which need no merge then.  yhat null:
+// the pass writes partial states for k_merge.
+struct KvFinal {
+  uint16_t* yhat;
+  float* beta;
+  float* sigma;
+};
+
+// Single-range epilogue: what k_merge computes from one partial, with the same
+// operations in the same order (so the two routes agree bit for bit):
+// sigma = the power of two above the range's largest |v|, yhat_f = S_f / z_f /
+// sigma (fp16, k-block slot order), beta_f = (c_f + log2 z_f) ln 2; a masked
+// feature gets yhat = 0 and the empty beta.
+template <int NW, int FT>
+__device__ __forceinline__ void kv_final(KvSmem<NW>& sm, const KvFeat (&fs)[FT], const KvFinal& fin, float vm,
+                                         float sig, int bh, int fo, int fo0, int m, int ma, int wave, int lane,
+                                         int tid) {
+  const int col = lane & 31, half = lane >> 5;
+  int ex = 0;
+  if (vm > 0.f && vm <= 3.0e38f) frexpf(vm, &ex);
+  const float sg = ldexpf(1.0f, ex);
+  if (fo0 == 0 && blockIdx.y == 0 && tid < kD) fin.sigma[static_cast<size_t>(bh) * kD + tid] = sg;
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const int f0 = fo + 32 * (FT * wave + ft);
+    const float zf = pair_sum(fs[ft].z);
+    const bool live = f0 + col < m && fs[ft].c != -kFInf;
+    const float zt = live ? zf : 0.f;
+    if (half == 0) {
+      fin.beta[static_cast<size_t>(bh) * ma + f0 + col] = zt > 0.f ? (fs[ft].c + log2f(zt)) * kLn2 : kBetaNone;
+      sm.zinv[wave][col] = zt > 0.f ? 1.0f / zt : 0.f;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes (lgkmcnt(0))
+    __builtin_amdgcn_wave_barrier();
+    // register 4 g + j holds feature f0 + 8 g + 4 half + j; its yhat slot in
+    // the 16-feature block is 8 half + 4 (g & 1) + j, so the four registers
+    // of a group are four adjacent slots
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      uint16_t* yrow = fin.yhat + (static_cast<size_t>(bh) * kD + 32 * dt + col) * ma + f0 + 8 * half;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 iz = *reinterpret_cast<const f32x4*>(&sm.zinv[wave][8 * g + 4 * half]);
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int fr = f0 + 8 * g + 4 * half + j;
+          // (a feature with z = 0 contributes exactly 0, as in the merge)
+          const float acc = fr < m && iz[j] != 0.f ? fs[ft].sacc[dt][4 * g + j] * sig : 0.f;
+          y[j] = (acc * iz[j]) / sg;
+        }
+        *reinterpret_cast<u32x2*>(yrow + 16 * (g >> 1) + 4 * (g & 1)) =
+            u32x2{pack_f16(y[0], y[1]), pack_f16(y[2], y[3])};
+      }
+    }
+  }
+}
+
 // NW waves of FT 32-feature tiles each cover the 32 NW FT features fo .. of a
 // piece (blockIdx.y selects the piece: fo = fo0 + blockIdx.y * 32 NW FT);
 // features at or past m are masked (their range state is written empty).
@@ -468,8 +528,8 @@ __device__ __forceinline__ void kv_range(KvSmem<NW>& sm, const uint16_t* Kb, con
 template <int NW, int FT>
 __global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
-    float* __restrict__ part_S, float* __restrict__ part_zc, float* __restrict__ part_vmax, int H,
-    int n, int d, int m, int ma, int fo0, int splits, int span) {
+    float* __restrict__ part_S, float* __restrict__ part_zc, float* __restrict__ part_vmax, KvFinal fin,
+    int H, int n, int d, int m, int ma, int fo0, int splits, int span) {
   constexpr int MP = NW * 32 * FT;   // features of the piece
   __shared__ __attribute__((aligned(16))) KvSmem<NW> sm;
   const int tid = threadIdx.x;
@@ -540,14 +600,16 @@ __global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
     kv_range<NW, FT, kModeAcc, false>(sm, Kb, Vb, ntok, d, ad, augB, fs, vinv, vmx, tid, lane);
   }
 
+  const float sig = 1.0f / vinv;
+  const float vm = block_max<NW>(sm, vmx, tid);
+  if (fin.yhat != nullptr) {
+    kv_final<NW, FT>(sm, fs, fin, vm, sig, bh, fo, fo0, m, ma, wave, lane, tid);
+    return;
+  }
   // write this range's partial state (S back in value units) and its largest
   // |v|; masked features (at or past m) are written as an empty state
-  const float sig = 1.0f / vinv;
   const size_t base = static_cast<size_t>(bh) * splits + split;
-  {
-    const float vm = block_max<NW>(sm, vmx, tid);
-    if (tid == 0 && blockIdx.y == 0) part_vmax[base] = vm;
-  }
+  if (tid == 0 && blockIdx.y == 0) part_vmax[base] = vm;
   float* zc = part_zc + base * 2 * ma;
   float* Sb = part_S + base * ma * kD;
 #pragma unroll
@@ -982,11 +1044,12 @@ long long balanced_pieces(long long BH, long long items, long long slots) {
 
 template <int NW, int FT>
 hipError_t launch_kv_piece(const Bf16Plan& p, int fo0, int pieces, const uint16_t* k, const uint16_t* v,
-                           const uint16_t* W, float* pS, float* pzc, float* pvm, hipStream_t s) {
+                           const uint16_t* W, float* pS, float* pzc, float* pvm, const KvFinal& fin,
+                           hipStream_t s) {
   // the causal path runs the same kernel over its segments; it is timed under its own name
   FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, FT>),
-               dim3(p.B * p.H * p.splits, pieces), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, p.H, p.n, p.d,
-               p.m, p.ma, fo0, p.splits, p.span);
+               dim3(p.B * p.H * p.splits, pieces), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, fin, p.H, p.n,
+               p.d, p.m, p.ma, fo0, p.splits, p.span);
   return hipGetLastError();
 }
 
@@ -1103,7 +1166,8 @@ Bf16Plan bf16_plan(int B, int H, int n, int d, int m, int causal, int chunk) {
 }
 
 hipError_t launch_kv_all(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W, float* pS,
-                         float* pzc, float* pvm, hipStream_t s) {
+                         float* pzc, float* pvm, hipStream_t s, uint16_t* yhat, float* beta, float* sigma) {
+  const KvFinal fin{yhat, beta, sigma};
   // the ma / 32 feature tiles as pieces of 8, 4, 2 and 1 tiles (one wave per
   // tile: two tiles per wave, sharing the operand reads, measured slower and
   // needed twice the key ranges for the same occupancy)
@@ -1113,10 +1177,10 @@ hipError_t launch_kv_all(const Bf16Plan& p, const uint16_t* k, const uint16_t* v
     if (cnt == 0) continue;
     hipError_t e = hipSuccess;
     switch (nw) {
-      case 8: e = launch_kv_piece<8, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
-      case 4: e = launch_kv_piece<4, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
-      case 2: e = launch_kv_piece<2, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
-      case 1: e = launch_kv_piece<1, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, s); break;
+      case 8: e = launch_kv_piece<8, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, fin, s); break;
+      case 4: e = launch_kv_piece<4, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, fin, s); break;
+      case 2: e = launch_kv_piece<2, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, fin, s); break;
+      case 1: e = launch_kv_piece<1, 1>(p, fo, cnt, k, v, W, pS, pzc, pvm, fin, s); break;
     }
     if (e != hipSuccess) return e;
     fo += cnt * nw * 32;
@@ -1201,8 +1265,12 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
   float* beta = reinterpret_cast<float*>(base + p.off_beta);
   float* sigma = reinterpret_cast<float*>(base + p.off_sigma);
   hipError_t e = hipSuccess;
+  // one key range per (b, h) (non-causal): the state pass writes the merge's
+  // outputs itself
+  const bool single = !p.causal && p.splits == 1;
   if (!p.causal || p.splits > 1) {
-    if ((e = launch_kv_all(p, k, v, W, pS, pzc, pvm, s)) != hipSuccess) return e;
+    if ((e = launch_kv_all(p, k, v, W, pS, pzc, pvm, s, single ? yh : nullptr, beta, sigma)) != hipSuccess)
+      return e;
   }
   if (p.causal) {
     if (causal_chunks_shape(p))
@@ -1211,9 +1279,11 @@ hipError_t launch_attention_bf16(const Bf16Plan& p, const uint16_t* q, const uin
                                reinterpret_cast<float*>(base + p.off_pnum),
                                reinterpret_cast<float*>(base + p.off_pdl), s);
   }
-  FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * (p.ma / 16)), dim3(256), 0, s, pS, pzc, pvm, yh,
-               beta, sigma, p.ma, p.splits);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!single) {
+    FAVOR_LAUNCH("k_merge", k_merge, dim3(p.B * p.H * (p.ma / 16)), dim3(256), 0, s, pS, pzc, pvm, yh,
+                 beta, sigma, p.ma, p.splits);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
 #define FAVOR_OUT_CASE(MTV) \
   case MTV: return launch_output<MTV>(p, q, W, yh, beta, sigma, out, s);
   switch (p.ma / 32) {

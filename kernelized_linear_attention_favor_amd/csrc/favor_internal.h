@@ -84,9 +84,12 @@ hipError_t launch_causal_chunks(const Bf16Plan& p, const uint16_t* q, const uint
                                 const uint16_t* v, const uint16_t* W, const float* part_S,
                                 const float* part_zc, const float* vmax, float* out,
                                 hipStream_t s);
-// The state pass (k_kv_state) over the plan's key ranges for every feature.
+// The state pass (k_kv_state) over the plan's key ranges for every feature:
+// partial states for the merge, or, with yhat non-null (one key range per
+// (b, h)), the merge's outputs yhat, beta and sigma directly.
 hipError_t launch_kv_all(const Bf16Plan& p, const uint16_t* k, const uint16_t* v, const uint16_t* W, float* pS,
-                         float* pzc, float* pvm, hipStream_t s);
+                         float* pzc, float* pvm, hipStream_t s, uint16_t* yhat = nullptr, float* beta = nullptr,
+                         float* sigma = nullptr);
 
 namespace walk {
 struct Args;
