@@ -521,8 +521,8 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
         dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones2, dl, false);
         a[w] = h;
       }
-      np0 = mfma_f16(as_f16x8(a), as_f16x8(b0), np0);
-      np1 = mfma_f16(as_f16x8(a), as_f16x8(b1), np1);
+      np0 = mfma_f16(as_f16x8(b0), as_f16x8(a), np0);
+      np1 = mfma_f16(as_f16x8(b1), as_f16x8(a), np1);
     }
   const VOpAddr va = vop_addr(lane);
 #pragma unroll
@@ -539,24 +539,25 @@ __device__ __forceinline__ void cs_query_phase(CsSmem<NW>& sm, int wave, int lan
       }
       const u32x4 v0 = v_operand_at(sm.v, 32 * kt + 16 * kb2, 0, va);
       const u32x4 v1 = v_operand_at(sm.v, 32 * kt + 16 * kb2, 1, va);
-      np0 = mfma_f16(as_f16x8(a), as_f16x8(v0), np0);
-      np1 = mfma_f16(as_f16x8(a), as_f16x8(v1), np1);
+      np0 = mfma_f16(as_f16x8(v0), as_f16x8(a), np0);
+      np1 = mfma_f16(as_f16x8(v1), as_f16x8(a), np1);
     }
   }
 
-  // row r's 64 values with their 8-float blocks XOR-swizzled by r & 7, so
-  // that the combine step's reads of 8 rows hit different banks.  Register
-  // 4 g + j holds row r = 8 g + 4 half + j, and r & 7 = 4 half + j does not
-  // depend on g: four lane addresses per value tile, g an immediate offset.
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rj = 4 * half + j;
-    float* b0 = scr + rj * kD + (col ^ (rj << 3));
-    float* b1 = scr + rj * kD + ((32 + col) ^ (rj << 3));
+  // The products are formed transposed (value operand first): register
+  // 4 g + j holds value column 8 g + 4 half + j (np1: 32 + that) of query
+  // col, so each lane writes its query row's values four at a time.  The
+  // row's 8-float blocks are XOR-swizzled by row & 7, so that the combine
+  // step's reads of 8 rows hit different banks.
+  {
+    float* row = scr + col * kD + 4 * half;
+    const int sw = (col & 7) << 3;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      b0[g * 8 * kD] = np0[4 * g + j];
-      b1[g * 8 * kD] = np1[4 * g + j];
+      *reinterpret_cast<f32x4*>(row + ((8 * g) ^ sw)) =
+          f32x4{np0[4 * g], np0[4 * g + 1], np0[4 * g + 2], np0[4 * g + 3]};
+      *reinterpret_cast<f32x4*>(row + ((32 + 8 * g) ^ sw)) =
+          f32x4{np1[4 * g], np1[4 * g + 1], np1[4 * g + 2], np1[4 * g + 3]};
     }
   }
   const float dq = pair_sum(dl);   // the denominator of query col
