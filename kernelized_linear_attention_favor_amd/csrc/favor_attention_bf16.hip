@@ -970,16 +970,17 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
         accumulate(ft, pr, off, y0, y1, den);
       }
     }
-    // each query's denominator (both lanes of its column, in a fixed order),
-    // then moved to the rows of the output layout: query r sits in lane r.
+    // each query's denominator (both lanes of its column, in a fixed order)
+    // and output scale, then moved to the rows of the output layout: query r
+    // sits in lane r.
     // Each store writes 128 contiguous bytes per row from 32 lanes.
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
-      const float dq = pair_sum(den[q]);
+      const float rq = sg * fast_rcp(pair_sum(den[q]));   // query col's output scale
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-        const float sc = sg * fast_rcp(__shfl(dq, row));
+        const float sc = __shfl(rq, row);
         float* orow = Ob + static_cast<size_t>(min(tb + 32 * q + row, t1 - 1)) * d;
         __builtin_nontemporal_store(y0[q][i] * sc, orow + col);
         if (D > 32) __builtin_nontemporal_store(y1[q][i] * sc, orow + 32 + col);
