@@ -788,7 +788,7 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 // ---------------------------------------------------------------------------
 // LDS of the output kernel for MT feature tiles (W' table with its padding,
 // yhat^T), and whether two workgroups fit a CU's 160 KB.
-constexpr int out_lds_bytes(int mt) { return (32 * mt * kWStride + 8) * 2 + kD * (32 * mt + 8) * 2; }
+constexpr int out_lds_bytes(int mt) { return (32 * mt * kWStride + 8) * 2 + kD * (32 * mt + 8) * 2 + 8 * 64 * 4; }
 constexpr bool out_two_per_cu(int mt) { return 2 * out_lds_bytes(mt) <= 160 * 1024; }
 constexpr int kOutWaves = 8;
 
@@ -806,6 +806,7 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
   constexpr int YS = ma + 8;  // fp16 per staged yhat^T row
   __shared__ __attribute__((aligned(16))) uint16_t wsh[ma * kWStride + 8];   // + padding read by the last row
   __shared__ __attribute__((aligned(16))) uint16_t ysh[kD * YS];
+  __shared__ __attribute__((aligned(16))) float rsh[NWO][64];   // per wave: its queries' output scales
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -977,15 +978,23 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
       const float rq = sg * fast_rcp(pair_sum(den[q]));   // query col's output scale
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-        const float sc = __shfl(rq, row);
-        float* orow = Ob + static_cast<size_t>(min(tb + 32 * q + row, t1 - 1)) * d;
-        __builtin_nontemporal_store(y0[q][i] * sc, orow + col);
-        if (D > 32) __builtin_nontemporal_store(y1[q][i] * sc, orow + 32 + col);
-      }
+      if (half == 0) rsh[wave][32 * q + col] = rq;
     }
+    // (the wave's own LDS write, read back by its other lanes: in order)
+#pragma unroll
+    for (int q = 0; q < QT; ++q)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 sc4 = *reinterpret_cast<const f32x4*>(&rsh[wave][32 * q + 8 * g + 4 * half]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * g + j, row = 8 * g + 4 * half + j;
+          // a 32-bit element offset inside the (b, h) slice (n d < 2^31)
+          const uint32_t o = static_cast<uint32_t>(min(tb + 32 * q + row, t1 - 1) * d + col);
+          __builtin_nontemporal_store(y0[q][i] * sc4[j], Ob + o);
+          if (D > 32) __builtin_nontemporal_store(y1[q][i] * sc4[j], Ob + o + 32);
+        }
+      }
 #pragma unroll
     for (int q = 0; q < QT; ++q)
 #pragma unroll
