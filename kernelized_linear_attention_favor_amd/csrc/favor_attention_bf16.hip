@@ -220,9 +220,10 @@ __device__ __forceinline__ f32x16 kv_proj(const uint16_t* kt, const uint32_t* at
   for (int kb = 0; kb < 4; ++kb)
     acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + row0 * 64 + ad.k[kb])), as_bf16x8(wB[kb]),
                     acc);
+  // the upper lane half's copy meets the zero half of augB (finite values
+  // times zero add nothing), so it needs no zeroing
   const u32x2 a = *reinterpret_cast<const u32x2*>(at + 2 * (row0 + col));
-  const u32x4 ka4 = half == 0 ? u32x4{a[0], a[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
-  return mfma_bf16(as_bf16x8(ka4), as_bf16x8(augB), acc);
+  return mfma_bf16(as_bf16x8(u32x4{a[0], a[1], 0u, 0u}), as_bf16x8(augB), acc);
 }
 
 // phi = 2^(D log2e - c) of the 16 keys in registers 8 kb2 .. 8 kb2 + 7 of a
@@ -277,7 +278,7 @@ __device__ __forceinline__ void kv_proj_n(const uint16_t* kt, const uint32_t* at
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) kop[kb] = *reinterpret_cast<const u32x4*>(kt + row0 * 64 + ad.k[kb]);
   const u32x2 a = *reinterpret_cast<const u32x2*>(at + 2 * (row0 + col));
-  const u32x4 ka4 = half == 0 ? u32x4{a[0], a[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 ka4 = u32x4{a[0], a[1], 0u, 0u};   // (upper half: times augB's zeros)
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
     f32x16 acc = {};
@@ -524,12 +525,14 @@ __device__ __forceinline__ void kv_final(KvSmem<NW>& sm, const KvFeat (&fs)[FT],
 // NW waves of FT 32-feature tiles each cover the 32 NW FT features fo .. of a
 // piece (blockIdx.y selects the piece: fo = fo0 + blockIdx.y * 32 NW FT);
 // features at or past m are masked (their range state is written empty).
-// The library launches FT = 1.
-template <int NW, int FT>
+// The library launches FT = 1.  D is the head dimension (32 or 64): with it
+// known, the staging needs no selects for dead 16-byte chunks at D = 64.
+template <int NW, int FT, int D>
 __global__ __launch_bounds__(NW * 64, FAVOR_KV_WAVES_PER_EU) void k_kv_state(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ W,
     float* __restrict__ part_S, float* __restrict__ part_zc, float* __restrict__ part_vmax, KvFinal fin,
-    int H, int n, int d, int m, int ma, int fo0, int splits, int span) {
+    int H, int n, int m, int ma, int fo0, int splits, int span) {
+  constexpr int d = D;
   constexpr int MP = NW * 32 * FT;   // features of the piece
   __shared__ __attribute__((aligned(16))) KvSmem<NW> sm;
   const int tid = threadIdx.x;
@@ -854,6 +857,7 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
     split3_bf16(beta[static_cast<size_t>(bh) * ma + f], w01, w23);
     *reinterpret_cast<u32x4*>(&wsh[f * kWStride + 64]) = u32x4{w01, w23, 0u, 0u};
   }
+  if (tid == 0) *reinterpret_cast<u32x4*>(&wsh[ma * kWStride]) = u32x4{0u, 0u, 0u, 0u};   // the padding
   for (int c = tid; c < kD * (ma / 8); c += NWO * 64) {
     const int dv = c / (ma / 8), ch = c - dv * (ma / 8);
     *reinterpret_cast<u32x4*>(&ysh[dv * YS + ch * 8]) =
@@ -871,11 +875,10 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
     u32x4 wa[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) wa[kb] = *reinterpret_cast<const u32x4*>(wr + 16 * kb);
-    // read by every lane and zeroed for the upper half (a predicated read
-    // would split the loop into branches); the last row's upper half reads
-    // the padding past the table
-    const u32x4 aug_all = *reinterpret_cast<const u32x4*>(wr + 64);
-    const u32x4 aug = half == 0 ? aug_all : u32x4{0u, 0u, 0u, 0u};
+    // read by every lane: the upper half reads the next row's first W
+    // values (the last row's, the zeroed padding past the table), finite
+    // values that meet the zero half of augB and add nothing
+    const u32x4 aug = *reinterpret_cast<const u32x4*>(wr + 64);
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
       f32x16 acc = {};
@@ -1057,9 +1060,14 @@ hipError_t launch_kv_piece(const Bf16Plan& p, int fo0, int pieces, const uint16_
                            const uint16_t* W, float* pS, float* pzc, float* pvm, const KvFinal& fin,
                            hipStream_t s) {
   // the causal path runs the same kernel over its segments; it is timed under its own name
-  FAVOR_LAUNCH(p.causal ? "k_causal_state" : "k_kv_state", (k_kv_state<NW, FT>),
-               dim3(p.B * p.H * p.splits, pieces), dim3(NW * 64), 0, s, k, v, W, pS, pzc, pvm, fin, p.H, p.n,
-               p.d, p.m, p.ma, fo0, p.splits, p.span);
+  const char* name = p.causal ? "k_causal_state" : "k_kv_state";
+  const dim3 grid(p.B * p.H * p.splits, pieces), block(NW * 64);
+  if (p.d == kD)
+    FAVOR_LAUNCH(name, (k_kv_state<NW, FT, kD>), grid, block, 0, s, k, v, W, pS, pzc, pvm, fin, p.H, p.n, p.m,
+                 p.ma, fo0, p.splits, p.span);
+  else
+    FAVOR_LAUNCH(name, (k_kv_state<NW, FT, 32>), grid, block, 0, s, k, v, W, pS, pzc, pvm, fin, p.H, p.n, p.m,
+                 p.ma, fo0, p.splits, p.span);
   return hipGetLastError();
 }
 
