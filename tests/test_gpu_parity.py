@@ -105,6 +105,20 @@ def _full_noncausal(cfg_name):
     return worst
 
 
+@pytest.mark.parametrize("B,H,n,d,m", [(10, 13, 1000, 64, 256), (3, 100, 300, 64, 128), (20, 55, 70, 64, 48),
+                                       (6, 100, 100, 32, 64)])
+def test_bf16_single_key_range(B, H, n, d, m):
+    """Many (b, h) pairs: each has one key range, so the state pass writes the
+    output kernel's inputs itself (no merge), including masked features (m = 48
+    in 64-feature tiles) and d = 32; the output grid cuts each sequence into the
+    query runs that fill whole rounds of workgroups.  Ragged n."""
+    cfg = fi.Config("single", B, H, n, d, m, "bf16", False, 64, "iid", 7 + n + m)
+    x = fi.make_inputs(cfg)
+    y = run(x, torch.bfloat16)
+    assert np.all(np.isfinite(y))
+    assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
+
+
 def test_bf16_C3_full():
     assert _full_noncausal("C3") < TOL_BF16
 
