@@ -791,6 +791,16 @@ __global__ __launch_bounds__(256) void k_state_merge(const float* __restrict__ p
 // ---------------------------------------------------------------------------
 // LDS of the output kernel for MT feature tiles (W' table with its padding,
 // yhat^T), and whether two workgroups fit a CU's 160 KB.
+// A raw buffer over `bytes` bytes at p (stride 0: byte offsets, a store whose
+// lane offset lies at or past the size is not performed; the gfx9 word-3
+// format bits), and a nontemporal 4-byte store through it at a lane offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows_rsrc(float* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_store_nt(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, 0, 2 /* nt */);
+}
+
 constexpr int out_lds_bytes(int mt) { return (32 * mt * kWStride + 8) * 2 + kD * (32 * mt + 8) * 2 + 8 * 64 * 4; }
 constexpr bool out_two_per_cu(int mt) { return 2 * out_lds_bytes(mt) <= 160 * 1024; }
 constexpr int kOutWaves = 8;
@@ -822,6 +832,7 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
 
   const uint16_t* Qb = Q + static_cast<size_t>(bh) * n * d;
   float* Ob = out + static_cast<size_t>(bh) * n * d;
+  const __amdgpu_buffer_rsrc_t orsrc = out_rows_rsrc(Ob + static_cast<size_t>(t0) * d, (t1 - t0) * d * 4);
 
   // This lane's queries (B operand column of each tile), loaded without
   // predication: rows past the end re-read the last row, and with d = 32 the
@@ -984,6 +995,12 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
       if (half == 0) rsh[wave][32 * q + col] = rq;
     }
     // (the wave's own LDS write, read back by its other lanes: in order)
+    // The run's rows t0 .. t1-1 as a raw buffer: the lane's byte offset (row
+    // and column) goes in the checked offset, so the stores of a partial last
+    // tile's rows at or past t1 fall outside the buffer and are dropped by the
+    // hardware.  The lane part is formed once per tile; a register's row
+    // offset is a constant added to it.
+    const uint32_t vo = static_cast<uint32_t>((tb - t0 + 4 * half) * d + col) * 4u;
 #pragma unroll
     for (int q = 0; q < QT; ++q)
 #pragma unroll
@@ -991,11 +1008,10 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
         const f32x4 sc4 = *reinterpret_cast<const f32x4*>(&rsh[wave][32 * q + 8 * g + 4 * half]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int i = 4 * g + j, row = 8 * g + 4 * half + j;
-          // a 32-bit element offset inside the (b, h) slice (n d < 2^31)
-          const uint32_t o = static_cast<uint32_t>(min(tb + 32 * q + row, t1 - 1) * d + col);
-          __builtin_nontemporal_store(y0[q][i] * sc4[j], Ob + o);
-          if (D > 32) __builtin_nontemporal_store(y1[q][i] * sc4[j], Ob + o + 32);
+          const int i = 4 * g + j;
+          const uint32_t o = vo + static_cast<uint32_t>((32 * q + 8 * g + j) * d * 4);
+          buffer_store_nt(y0[q][i] * sc4[j], orsrc, o);
+          if (D > 32) buffer_store_nt(y1[q][i] * sc4[j], orsrc, o + 128);
         }
       }
 #pragma unroll

@@ -119,6 +119,25 @@ def test_bf16_single_key_range(B, H, n, d, m):
     assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
 
 
+@pytest.mark.parametrize("m", [256, 512])
+@pytest.mark.parametrize("n", [1, 31, 65, 300, 4097])
+def test_bf16_output_stays_in_bounds(n, m):
+    """The output kernel's last tile runs past the sequence end; nothing may
+    land there: the rows after `out` in a larger buffer keep their sentinel.
+    (m = 512 takes the two-query-tile form.)"""
+    cfg = fi.Config("bounds", 1, 1, n, 64, m, "bf16", False, 64, "iid", 900 + n + m)
+    x = fi.make_inputs(cfg)
+    t = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    pad = 512 * 64
+    big = torch.full((n * 64 + pad,), 12345.0, dtype=torch.float32, device=DEV)
+    out = big[: n * 64].view(1, 1, n, 64)
+    favor.attention(t["q"], t["k"], t["v"], t["W"], causal=False, out=out)
+    torch.cuda.synchronize()
+    assert bool((big[n * 64:] == 12345.0).all())
+    y = out.cpu().numpy()
+    assert oracle.max_rel_err(y, oracle.attention(x["q"], x["k"], x["v"], x["W"])) < TOL_BF16
+
+
 def test_bf16_C3_full():
     assert _full_noncausal("C3") < TOL_BF16
 
