@@ -824,8 +824,9 @@ __global__ __launch_bounds__(kOutWaves * 64, out_two_per_cu(MT) ? 4 : 2) void k_
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int nblk = (n + span - 1) / span;
-  const int bh = blockIdx.x / nblk;
-  const int blk = blockIdx.x - bh * nblk;
+  const int wg = xcd_contiguous(blockIdx.x, gridDim.x);   // the runs of one (b, h) share an L2
+  const int bh = wg / nblk;
+  const int blk = wg - bh * nblk;
   const int hh = bh % H;
   const int t0 = blk * span;
   const int t1 = min(n, t0 + span);

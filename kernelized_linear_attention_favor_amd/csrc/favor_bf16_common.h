@@ -97,5 +97,19 @@ __device__ __forceinline__ u32x4 v_operand_at(const uint16_t* vt, int key0, int 
 
 constexpr int kWStride = 72;   // bf16 per staged W' row: 64 d + 8 beta parts (36 banks: 16 rows conflict-free)
 
+// The chip deals a launch's workgroups to its 8 XCDs round-robin by index, and
+// each XCD has its own L2.  This maps launch index b of a G-workgroup grid to a
+// logical index such that every XCD gets one contiguous run of logical indices
+// (the first G % 8 XCDs one more than the rest); a bijection on [0, G).  With
+// the (b, h) pair as the slow part of the logical index, the workgroups of one
+// sequence share an L2, and what they all read (its earlier segments' states,
+// its W rows, its normalised state table) is fetched from HBM once per XCD
+// instead of once per XCD that holds any of them.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous(int b, int G) {
+  const int x = b % kXcds, q = G / kXcds, r = G - q * kXcds;
+  return x * q + min(x, r) + b / kXcds;
+}
+
 }  // namespace bf16k
 }  // namespace favor

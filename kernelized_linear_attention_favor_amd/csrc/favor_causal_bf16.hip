@@ -587,8 +587,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_chunks(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int bh = blockIdx.x / nseg;
-  const int seg = blockIdx.x - bh * nseg;
+  // the segments of one (b, h) share an XCD: their prologues read the same
+  // earlier segment states, which then pass through one L2
+  const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int bh = wg / nseg;
+  const int seg = wg - bh * nseg;
   const int hh = bh % H;
   const int s0 = seg * seglen;
   const int ntok = min(n, s0 + seglen) - s0;

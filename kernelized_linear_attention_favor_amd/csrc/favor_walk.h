@@ -313,8 +313,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_causal_walk(Args a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int seg = blockIdx.x % a.nseg;
-  const int rest = blockIdx.x / a.nseg;
+  const int wg = xcd_contiguous(blockIdx.x, gridDim.x);   // segments of one (b, h) share an L2
+  const int seg = wg % a.nseg;
+  const int rest = wg / a.nseg;
   const int bh = rest % a.BH;
   const int sl = rest / a.BH;
   const int slice = a.slice0 + sl;
